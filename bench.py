@@ -1,0 +1,237 @@
+"""Benchmark: one MLA decode step over the dual-path low-bit cache, per layer.
+
+A step is what one decode step of a model does to every layer's cache: the
+fused writer appends the incoming token of each sequence (its latent and
+positional key are quantized and packed; this token completes a cache page,
+so the page's k_R is quantized too) and the decode attends over the N cached
+tokens.  The step is repeated over `--layers` distinct caches so that the
+256 MB Infinity Cache cannot hold them (the packed bytes of all layers exceed
+1 GB), and the metric is microseconds per layer.
+
+Workload: C4R4 decode, 16 heads, latent 512 + rope 64, batch 32 x 4096 cached
+tokens, page 128, sink 4 + local 128 in BF16 (synthetic, seeded inputs).
+
+Prints one JSON line.  Run on one GPU: python bench.py [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_decode_bytes(w, L: int) -> dict:
+    """Bytes the decode must move for one sequence of L tokens (layout sizes:
+    C4R4 304 B / C2R4 176 B per packed token, 256 B k_R metadata per page read,
+    1152 B per BF16 token, 1152 B of queries and 2052 B of output per head)."""
+    lat_row = 512 * w.latent_bits // 8
+    per_packed = lat_row + 16 + 32
+    lo_p = min(w.sink, L)
+    full = (L // w.page_size) * w.page_size
+    hi_p = max(lo_p, min(L - w.local, full))
+    n_packed = hi_p - lo_p
+    pages = 0 if n_packed == 0 else (hi_p - 1) // w.page_size - lo_p // w.page_size + 1
+    n_bf16 = L - n_packed
+    cache = n_packed * per_packed + pages * 256 + n_bf16 * 1152
+    return {"cache": cache, "q": w.heads * 1152, "out": w.heads * 2052,
+            "total": cache + w.heads * 1152 + w.heads * 2052, "packed_tokens": n_packed}
+
+
+def cpu_baseline(w, n_seq_sample: int, budget_s: float = 12.0) -> dict:
+    """The CPU oracle (single thread) doing the same step -- append one token,
+    decode over the cached tokens -- for a sample of sequences, scaled to the
+    whole batch (microseconds per layer)."""
+    import oracle
+    from bit_kv_cache_writer_amd import workloads as wl
+
+    olay = oracle.Layout(w.page_size, w.latent_bits, w.clip_q, w.sink, w.local)
+    max_pages = w.pages_per_seq()
+    pb = oracle.page_bytes(olay)
+    ql, qr = wl.queries(w)
+    t_total, done = 0.0, 0
+    for b in range(n_seq_sample):
+        c, k = wl.seq_tokens(w, b)
+        bt = np.arange(max_pages, dtype=np.int32).reshape(1, max_pages)
+        pool = np.zeros(max_pages * pb, np.uint8)
+        sink = np.zeros((1, max(w.sink, 1), 576), np.uint16)
+        ring = np.zeros((1, max(w.local, 1), 576), np.uint16)
+        tail = np.zeros((1, w.page_size, 64), np.uint16)
+        n = w.seqlen
+        oracle.write(olay, c[: n - 1], k[: n - 1], np.array([0, n - 1], np.int32),
+                     np.zeros(1, np.int32), bt, pool, sink, ring, tail)
+        t0 = time.perf_counter()
+        oracle.write(olay, np.ascontiguousarray(c[n - 1:]), np.ascontiguousarray(k[n - 1:]),
+                     np.array([0, 1], np.int32), np.array([n - 1], np.int32), bt, pool, sink, ring, tail)
+        oracle.decode(olay, np.ascontiguousarray(ql[b:b + 1]), np.ascontiguousarray(qr[b:b + 1]),
+                      w.softmax_scale, pool, bt, np.array([n], np.int32), sink, ring, tail)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total > budget_s:
+            break
+    us_layer = t_total / done * w.batch * 1e6
+    return {"value": us_layer, "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences (append 1 token + decode over {w.seqlen}), "
+                      f"single-threaded C oracle, scaled x{w.batch / done:.1f}",
+            "sample_seconds": round(t_total, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4r4_h16_b32")
+    ap.add_argument("--layers", type=int, default=0, help="0: enough layers for >= 1 GB of packed cache")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from bit_kv_cache_writer_amd import mla
+    from bit_kv_cache_writer_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    mla.lib()
+    w = wl.WORKLOADS[args.workload]
+    lay = mla.Layout(w.page_size, w.latent_bits, w.clip_q, w.sink, w.local)
+    n = w.seqlen
+    max_pages = w.pages_per_seq()
+    bt, n_pool = wl.block_table(w, max_pages)
+    page_bytes = mla.mla_lowbit_layout_query(lay)["page_bytes"]
+    packed_layer = w.batch * max_pages * page_bytes
+    layers = args.layers or max(2, math.ceil(1.0e9 / packed_layer))
+    print(f"[bench] {w.name}: {layers} layers x {packed_layer / 1e6:.1f} MB packed", file=sys.stderr,
+          flush=True)
+
+    # inputs: N-1 cached tokens per sequence + the incoming token
+    ckv = torch.empty((w.batch * (n - 1), 512), dtype=torch.int16, device="cuda")
+    kr = torch.empty((w.batch * (n - 1), 64), dtype=torch.int16, device="cuda")
+    new_ckv = torch.empty((w.batch, 512), dtype=torch.int16, device="cuda")
+    new_kr = torch.empty((w.batch, 64), dtype=torch.int16, device="cuda")
+    for b in range(w.batch):
+        c, k = wl.seq_tokens(w, b)
+        ckv[b * (n - 1):(b + 1) * (n - 1)] = torch.from_numpy(c[: n - 1].view(np.int16))
+        kr[b * (n - 1):(b + 1) * (n - 1)] = torch.from_numpy(k[: n - 1].view(np.int16))
+        new_ckv[b] = torch.from_numpy(c[n - 1].view(np.int16))
+        new_kr[b] = torch.from_numpy(k[n - 1].view(np.int16))
+    ql, qr = wl.queries(w)
+    q_lat = torch.from_numpy(ql.view(np.int16)).cuda()
+    q_rope = torch.from_numpy(qr.view(np.int16)).cuda()
+
+    caches = []
+    fill_ms = []
+    for _ in range(layers):
+        cache = mla.DeviceCache(lay, w.batch, max_pages, bt, n_pool)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cache.append(ckv, kr, [n - 1] * w.batch)
+        e1.record()
+        caches.append(cache)
+        torch.cuda.synchronize()
+        fill_ms.append(e0.elapsed_time(e1))
+    del ckv, kr
+    fill_bytes = w.batch * (n - 1) * 1152 + w.batch * (n - 1) * (512 * w.latent_bits // 8 + 16 + 32)
+    stream = torch.cuda.current_stream()
+    cu_new = torch.arange(w.batch + 1, dtype=torch.int32, device="cuda")
+    before = torch.full((w.batch,), n - 1, dtype=torch.int32, device="cuda")
+    seqlens = torch.full((w.batch,), n, dtype=torch.int32, device="cuda")
+    ws_bytes = mla.mla_lowbit_decode_workspace(lay, w.batch, w.heads, n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
+
+    def layer_step(c, ev=None):
+        mla.mla_lowbit_write(lay, new_ckv, new_kr, cu_new, before, w.batch, w.batch, 1, c.block_table,
+                             max_pages, n_pool, c.pool, c.sink, c.ring, c.tail, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_lowbit_decode(lay, q_lat, q_rope, w.batch, w.heads, w.softmax_scale, c.pool, n_pool,
+                              c.block_table, max_pages, seqlens, n, c.sink, c.ring, c.tail, out, lse,
+                              ws, ws_bytes, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        for c in caches:
+            layer_step(c)
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in caches] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for li, c in enumerate(caches):
+            layer_step(c, evs[s][li])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    dec_ms = np.array([a.elapsed_time(b) for row in evs for a, b in row])
+    ms_per_step = total_ms / args.steps
+    us_layer = ms_per_step * 1000.0 / layers
+    dec_us = float(dec_ms.mean() * 1000.0)
+
+    alg = algorithmic_decode_bytes(w, n)
+    dec_bytes = alg["total"] * w.batch
+    achieved = dec_bytes / (dec_us * 1e-6) / 1e9
+    packed_gbs = alg["cache"] * w.batch / (dec_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, w.batch)
+
+    line = {
+        "metric": "MLA low-bit decode us/layer and packed-cache HBM GB/s (% of roofline)",
+        "value": round(us_layer, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "batch": w.batch, "heads": w.heads,
+                   "cached_tokens": n, "page": w.page_size, "paths": w.paths, "sink": w.sink,
+                   "local": w.local, "layers_per_step": layers,
+                   "step": "per layer: append 1 token per sequence (completes a page) + decode over N"},
+        "decode_us": round(dec_us, 3),
+        "write_us": round(us_layer - dec_us, 3),
+        "packed_cache_gbs": round(packed_gbs, 1),
+        "writer_bulk_fill_gbs": round(fill_bytes / (np.median(fill_ms) * 1e-3) / 1e9, 1),
+        "wall_s": round(wall, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_lowbit_decode (split kernel + combine kernel, timed together)",
+                     "bytes_per_launch": dec_bytes},
+        "cpu_baseline": cpu,
+        "context_h20": {"raq_mla_us_per_layer": 12.6, "flashmla_us_per_layer": 17.4,
+                        "tpot_ms": [5.97, 6.56]},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

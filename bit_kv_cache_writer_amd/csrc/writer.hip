@@ -1,0 +1,373 @@
+// Fused cache writer for gfx950 (QuantMLA Figure 8 caption: a packed copy of
+// every incoming token plus BF16 retention of sink/recent tokens; RAQ-MLA
+// appendix Table 5: per-token 128-channel latent groups with FP16 scale/min,
+// 0.94-quantile |x| clipping for the 2-bit latent, per-(channel, page) 4-bit
+// k_R with FP16 scale/min).
+//
+// One workgroup (4 waves) per (sequence, cache page touched by the call):
+//   * each wave quantizes whole latent tokens: lane l owns channels 8l..8l+7,
+//     so a 128-channel group is 16 lanes and its min/max is a 16-lane
+//     butterfly; codes are packed in registers and stored as one dword
+//     (4-bit) or one half-word (2-bit) per lane;
+//   * if the page becomes full in this call the workgroup quantizes its k_R
+//     per channel over the P tokens (tail buffer for tokens written by earlier
+//     calls, input rows for the new ones);
+//   * only the workgroup of the sequence's first touched page reads the tail
+//     buffer, and it alone then writes the tail rows of a page left
+//     incomplete, after a barrier -- so no workgroup reads tail rows another
+//     one overwrites.
+// The quantizer's arithmetic is IEEE fp32 with each operation rounded on its
+// own (contraction off), so codes and metadata are reproducible bit for bit.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "geometry.h"
+
+#pragma clang fp contract(off)
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+struct WriterParams {
+  const uint16_t* c_kv;
+  const uint16_t* k_r;
+  const int32_t* cu_new;
+  const int32_t* seqlens_before;
+  const int32_t* block_table;
+  uint8_t* pool;
+  uint16_t* sink;
+  uint16_t* ring;
+  uint16_t* tail;
+  int32_t batch, total_new, max_pages, num_pool_pages, pages_per_seq_grid;
+  int32_t P, bits, sink_n, local;
+  int32_t clip, clip_lo, clip_hi;
+  float clip_frac;
+  int64_t latent_row, latent_meta_off, rope_codes_off, rope_meta_off, page_bytes;
+};
+
+__device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ inline float canon_zero(float x) { return x == 0.0f ? 0.0f : x; }
+
+__device__ inline uint16_t f16_bits_rn(float x) {
+  _Float16 h = static_cast<_Float16>(x);  // v_cvt_f16_f32, round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ inline float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Largest fp16 <= x: round to nearest, then step one ulp down if it went up.
+__device__ inline uint16_t f16_round_down(float x) {
+  uint16_t h = f16_bits_rn(x);
+  if (f16_to_f32(h) > x) {
+    if ((h & 0x7FFFu) == 0) h = 0x8001u;  // zero -> smallest negative subnormal
+    else h = (h & 0x8000u) ? h + 1 : h - 1;
+  }
+  return h;
+}
+
+// Smallest fp16 >= x (x >= 0 here; a zero result is +0).
+__device__ inline uint16_t f16_round_up(float x) {
+  uint16_t h = f16_bits_rn(x);
+  if (f16_to_f32(h) < x) {
+    if ((h & 0x7FFFu) == 0) h = 0x0001u;
+    else h = (h & 0x8000u) ? h - 1 : h + 1;
+    if (h == 0x8000u) h = 0;
+  }
+  return h;
+}
+
+__device__ inline float wave_min16(float v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) v = fminf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ inline float wave_max16(float v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, 64)));
+  return v;
+}
+
+// k-th smallest (0-based) of the 512 |x| bit patterns held 8 per lane,
+// built bit by bit from the most significant one.
+__device__ inline uint32_t wave_kth_smallest(const uint32_t (&a)[8], int k) {
+  uint32_t prefix = 0;
+  for (int b = 14; b >= 0; --b) {
+    const uint32_t t = prefix | ((1u << b) - 1u);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c += a[i] <= t ? 1 : 0;
+    c = wave_sum(c);
+    if (c < k + 1) prefix |= 1u << b;
+  }
+  return prefix;
+}
+
+// Quantizes one latent token (one wave; lane l holds channels 8l..8l+7).
+__device__ void write_latent_token(const WriterParams& p, const uint16_t* src, uint8_t* page,
+                                   int slot, int lane) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * lane);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = canon_zero(bf16_to_f32(w[i] & 0xFFFFu));
+    x[2 * i + 1] = canon_zero(bf16_to_f32(w[i] >> 16));
+  }
+  if (p.clip) {
+    uint32_t a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (__float_as_uint(x[i]) >> 16) & 0x7FFFu;
+    const uint32_t lo = wave_kth_smallest(a, p.clip_lo);
+    int c_le = 0;
+    uint32_t above = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c_le += a[i] <= lo ? 1 : 0;
+      if (a[i] > lo) above = min(above, a[i]);
+    }
+    c_le = wave_sum(c_le);
+    above = wave_min_u32(above);
+    const uint32_t hi = (c_le >= p.clip_hi + 1) ? lo : above;
+    const float flo = bf16_to_f32(lo), fhi = bf16_to_f32(hi);
+    const float d = fhi - flo;
+    const float prod = p.clip_frac * d;
+    const float c = flo + prod;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v = x[i];
+      v = v < -c ? -c : v;
+      v = v > c ? c : v;
+      x[i] = canon_zero(v);
+    }
+  }
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  mn = wave_min16(mn);
+  mx = wave_max16(mx);
+  const int levels = (1 << p.bits) - 1;
+  const uint16_t mh = f16_round_down(mn);
+  const float minf = f16_to_f32(mh);
+  const float span = mx - minf;
+  const float s = span / static_cast<float>(levels);
+  const uint16_t sh = f16_round_up(s);
+  const float sf = f16_to_f32(sh);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t code = 0;
+    if (sf > 0.0f) {
+      const float t = (x[i] - minf) / sf;
+      float r = rintf(t);
+      r = fminf(fmaxf(r, 0.0f), static_cast<float>(levels));
+      code = static_cast<uint32_t>(r);
+    }
+    packed |= code << (p.bits * i);
+  }
+  uint8_t* row = page + static_cast<int64_t>(slot) * p.latent_row;
+  if (p.bits == 4) {
+    reinterpret_cast<uint32_t*>(row)[lane] = packed;
+  } else {
+    reinterpret_cast<uint16_t*>(row)[lane] = static_cast<uint16_t>(packed);
+  }
+  if ((lane & 15) == 0) {
+    const uint32_t meta = static_cast<uint32_t>(sh) | (static_cast<uint32_t>(mh) << 16);
+    uint8_t* m = page + p.latent_meta_off + static_cast<int64_t>(slot) * (kGroups * 4);
+    reinterpret_cast<uint32_t*>(m)[lane >> 4] = meta;
+  }
+}
+
+// Copies one token's BF16 row [c_KV 512 | k_R 64] (1152 B) with one wave.
+__device__ inline void copy_row(uint16_t* dst, const uint16_t* ckv, const uint16_t* kr, int lane) {
+  reinterpret_cast<uint4*>(dst)[lane] = reinterpret_cast<const uint4*>(ckv)[lane];
+  if (lane < 8) reinterpret_cast<uint4*>(dst + kLatentDim)[lane] = reinterpret_cast<const uint4*>(kr)[lane];
+}
+
+__global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
+  const int b = blockIdx.x / p.pages_per_seq_grid;
+  const int pi = blockIdx.x % p.pages_per_seq_grid;
+  if (b >= p.batch) return;
+  const int r0 = p.cu_new[b], r1 = p.cu_new[b + 1];
+  const int sb = p.seqlens_before[b];
+  if (r0 < 0 || r1 < r0 || r1 > p.total_new || sb < 0) return;
+  const int n_new = r1 - r0;
+  if (n_new == 0) return;
+  const int P = p.P;
+  const int end = sb + n_new;
+  const int p0 = sb / P;
+  const int pg = p0 + pi;
+  if (static_cast<int64_t>(pg) * P >= end) return;
+  const int last_page = (end - 1) / P;
+  if (last_page >= p.max_pages) return;  // positions beyond the block table
+  const int page_id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pg];
+  if (page_id < 0 || page_id >= p.num_pool_pages) return;
+  uint8_t* page = p.pool + static_cast<int64_t>(page_id) * p.page_bytes;
+  const int tb = max(sb, pg * P), te = min(end, (pg + 1) * P);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint16_t* tail = p.tail + static_cast<int64_t>(b) * P * kRopeDim;
+
+  // Latent codes + metadata, BF16 sink / ring copies.
+  for (int t = tb + wave; t < te; t += kWaves) {
+    const int64_t row = r0 + (t - sb);
+    const uint16_t* xl = p.c_kv + row * kLatentDim;
+    const uint16_t* xr = p.k_r + row * kRopeDim;
+    write_latent_token(p, xl, page, t - pg * P, lane);
+    if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, xl, xr, lane);
+    if (p.local > 0 && t >= end - p.local)
+      copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, xl, xr, lane);
+  }
+
+  // k_R of a page that becomes full: per channel over its P tokens.
+  __shared__ float s_min[kWaves][kRopeDim], s_max[kWaves][kRopeDim];
+  __shared__ float s_minf[kRopeDim], s_sf[kRopeDim];
+  __shared__ uint8_t s_code[256 * kRopeDim];
+  const bool completes = (pg + 1) * P <= end;
+  if (completes) {
+    const int c = threadIdx.x & 63, part = threadIdx.x >> 6;
+    auto value = [&](int slot) -> float {
+      const int t = pg * P + slot;
+      const uint16_t h = t < sb ? tail[static_cast<int64_t>(slot) * kRopeDim + c]
+                                : p.k_r[(r0 + (t - sb)) * static_cast<int64_t>(kRopeDim) + c];
+      return canon_zero(bf16_to_f32(h));
+    };
+    float mn = 3.0e38f, mx = -3.0e38f;
+    for (int s = part; s < P; s += kWaves) {
+      const float v = value(s);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    s_min[part][c] = mn;
+    s_max[part][c] = mx;
+    __syncthreads();
+    if (part == 0) {
+#pragma unroll
+      for (int q = 1; q < kWaves; ++q) {
+        mn = fminf(mn, s_min[q][c]);
+        mx = fmaxf(mx, s_max[q][c]);
+      }
+      const uint16_t mh = f16_round_down(mn);
+      const float minf = f16_to_f32(mh);
+      const float span = mx - minf;
+      const float s = span / 15.0f;
+      const uint16_t sh = f16_round_up(s);
+      s_minf[c] = minf;
+      s_sf[c] = f16_to_f32(sh);
+      uint16_t* meta = reinterpret_cast<uint16_t*>(page + p.rope_meta_off);
+      meta[c] = sh;
+      meta[kRopeDim + c] = mh;
+    }
+    __syncthreads();
+    const float minf = s_minf[c], sf = s_sf[c];
+    for (int s = part; s < P; s += kWaves) {
+      uint32_t code = 0;
+      if (sf > 0.0f) {
+        const float t = (value(s) - minf) / sf;
+        float r = rintf(t);
+        r = fminf(fmaxf(r, 0.0f), 15.0f);
+        code = static_cast<uint32_t>(r);
+      }
+      s_code[s * kRopeDim + c] = static_cast<uint8_t>(code);
+    }
+    __syncthreads();
+    // pack: 8 channels per dword, P rows x 8 dwords
+    uint32_t* rc = reinterpret_cast<uint32_t*>(page + p.rope_codes_off);
+    for (int i = threadIdx.x; i < P * 8; i += kThreads) {
+      const uint8_t* cs = s_code + (i >> 3) * kRopeDim + (i & 7) * 8;
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w |= static_cast<uint32_t>(cs[k]) << (4 * k);
+      rc[i] = w;
+    }
+  }
+
+  // Tail rows of the page left incomplete, written by the first page's
+  // workgroup after every read of the old tail rows above.
+  if (pi == 0 && end % P != 0) {
+    __syncthreads();
+    const int t0 = max(sb, (end / P) * P);
+    for (int i = threadIdx.x; i < (end - t0) * (kRopeDim / 8); i += kThreads) {
+      const int t = t0 + i / (kRopeDim / 8), q = i % (kRopeDim / 8);
+      const uint4* src = reinterpret_cast<const uint4*>(p.k_r + (r0 + (t - sb)) * static_cast<int64_t>(kRopeDim)) + q;
+      reinterpret_cast<uint4*>(tail + static_cast<int64_t>(t % P) * kRopeDim)[q] = *src;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace mla
+
+extern "C" int mla_lowbit_write(const mla_lowbit_layout* layout, const void* c_kv, const void* k_r,
+                                const int32_t* cu_new, const int32_t* seqlens_before, int32_t batch,
+                                int32_t total_new, int32_t max_new_per_seq,
+                                const int32_t* block_table, int32_t max_pages,
+                                int32_t num_pool_pages, void* page_pool, void* sink_buf,
+                                void* ring_buf, void* rope_tail, hipStream_t stream) {
+  using namespace mla;
+  Geometry g;
+  int rc = make_geometry(layout, &g);
+  if (rc) return rc;
+  if (batch < 0 || total_new < 0 || max_new_per_seq < 0 || max_pages < 0 || num_pool_pages < 0)
+    return MLA_LOWBIT_ERR_ARG;
+  if (batch == 0 || total_new == 0 || max_new_per_seq == 0) return MLA_LOWBIT_OK;
+  if (!c_kv || !k_r || !cu_new || !seqlens_before || !block_table || !page_pool || !rope_tail)
+    return MLA_LOWBIT_ERR_ARG;
+  if (g.sink > 0 && !sink_buf) return MLA_LOWBIT_ERR_ARG;
+  if (g.local > 0 && !ring_buf) return MLA_LOWBIT_ERR_ARG;
+  if (!aligned16(c_kv) || !aligned16(k_r) || !aligned16(page_pool) || !aligned16(rope_tail) ||
+      (sink_buf && !aligned16(sink_buf)) || (ring_buf && !aligned16(ring_buf)))
+    return MLA_LOWBIT_ERR_ARG;
+  if (max_pages == 0 || num_pool_pages == 0) return MLA_LOWBIT_ERR_ARG;
+  WriterParams p{};
+  p.c_kv = static_cast<const uint16_t*>(c_kv);
+  p.k_r = static_cast<const uint16_t*>(k_r);
+  p.cu_new = cu_new;
+  p.seqlens_before = seqlens_before;
+  p.block_table = block_table;
+  p.pool = static_cast<uint8_t*>(page_pool);
+  p.sink = static_cast<uint16_t*>(sink_buf);
+  p.ring = static_cast<uint16_t*>(ring_buf);
+  p.tail = static_cast<uint16_t*>(rope_tail);
+  p.batch = batch;
+  p.total_new = total_new;
+  p.max_pages = max_pages;
+  p.num_pool_pages = num_pool_pages;
+  p.P = g.page_size;
+  p.bits = g.latent_bits;
+  p.sink_n = g.sink;
+  p.local = g.local;
+  p.clip = g.clip ? 1 : 0;
+  p.clip_lo = g.clip_lo;
+  p.clip_hi = g.clip_hi;
+  p.clip_frac = g.clip_frac;
+  p.latent_row = g.latent_row;
+  p.latent_meta_off = g.latent_meta_off;
+  p.rope_codes_off = g.rope_codes_off;
+  p.rope_meta_off = g.rope_meta_off;
+  p.page_bytes = g.page_bytes;
+  // pages a call of n tokens can touch: (n - 1) / P + 2
+  p.pages_per_seq_grid = (max_new_per_seq - 1) / g.page_size + 2;
+  const int64_t blocks = static_cast<int64_t>(batch) * p.pages_per_seq_grid;
+  if (blocks > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(writer_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
+}

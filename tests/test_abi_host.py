@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+entry point of include/mla_lowbit.h, the layout query matches the oracle's
+independent byte geometry, and bad arguments are rejected before anything is
+launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_kv_cache_writer_amd import mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mla_lowbit.h")).read()
+    return sorted(set(re.findall(r"\b(mla_lowbit_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert set(names) == set(mla.EXPORTS)
+    lib = mla.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("P", [32, 64, 128, 256])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_layout_query_matches_oracle(orc, P, bits):
+    s = mla.mla_lowbit_layout_query(mla.Layout(P, bits, 0.94 if bits == 2 else 0.0, 4, 128))
+    off = orc.page_offsets(orc.Layout(P, bits, 0.0, 4, 128))
+    assert s["page_bytes"] == off["page_bytes"]
+    assert s["latent_meta_offset"] == off["latent_meta"]
+    assert s["rope_codes_offset"] == off["rope_codes"]
+    assert s["rope_meta_offset"] == off["rope_meta"]
+    assert s["latent_row_bytes"] == off["latent_row"]
+    assert s["sink_bytes_per_seq"] == 4 * 1152 and s["ring_bytes_per_seq"] == 128 * 1152
+    assert s["tail_bytes_per_seq"] == P * 128
+
+
+@pytest.mark.parametrize("bad", [
+    dict(page_size=48), dict(page_size=16), dict(latent_bits=3), dict(latent_clip_q=1.5),
+    dict(latent_clip_q=-0.1), dict(latent_clip_q=float("nan")), dict(sink=65), dict(local=5000),
+    dict(latent_dim=256), dict(rope_dim=128), dict(rope_bits=2), dict(latent_group=64), dict(version=2),
+])
+def test_bad_layouts_rejected(bad):
+    base = dict(page_size=64, latent_bits=4, latent_clip_q=0.0, sink=4, local=128)
+    base.update(bad)
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_lowbit_layout_query(mla.Layout(**base))
+    assert e.value.code == -1
+
+
+def test_workspace_query_and_errors():
+    lay = mla.Layout(128, 4, 0.0, 4, 128)
+    n = mla.mla_lowbit_decode_workspace(lay, 32, 16, 4096)
+    assert n > 0 and n % 4 == 0
+    assert mla.mla_lowbit_decode_workspace(lay, 32, 20, 4096) > n  # two head blocks
+    for args in [(0, 0, 4096), (32, 129, 4096), (32, 16, -1)]:
+        with pytest.raises(mla.MlaError) as e:
+            mla.mla_lowbit_decode_workspace(lay, *args)
+        assert e.value.code == -2
+
+
+def _write(lay, **kw):
+    a = dict(c_kv=16, k_r=16, cu_new=16, seqlens_before=16, batch=1, total_new=1, max_new_per_seq=1,
+             block_table=16, max_pages=1, num_pool_pages=1, page_pool=16, sink_buf=16, ring_buf=16,
+             rope_tail=16)
+    a.update(kw)
+    L = mla.lib()
+    return L.mla_lowbit_write(ctypes.byref(lay.c()), a["c_kv"], a["k_r"], a["cu_new"], a["seqlens_before"],
+                              a["batch"], a["total_new"], a["max_new_per_seq"], a["block_table"],
+                              a["max_pages"], a["num_pool_pages"], a["page_pool"], a["sink_buf"],
+                              a["ring_buf"], a["rope_tail"], None)
+
+
+def test_write_rejects_bad_arguments_without_launch():
+    lay = mla.Layout(64, 4, 0.0, 4, 32)
+    assert _write(lay, c_kv=None) == -2
+    assert _write(lay, rope_tail=None) == -2
+    assert _write(lay, sink_buf=None) == -2
+    assert _write(lay, c_kv=24) == -2          # misaligned
+    assert _write(lay, batch=-1) == -2
+    assert _write(lay, max_pages=0) == -2
+    assert _write(lay, batch=0) == 0           # nothing to do
+    assert _write(lay, total_new=0) == 0
+    bad = mla.Layout(64, 4, 0.0, 4, 32, version=7)
+    assert _write(bad) == -1
+
+
+def _decode(lay, **kw):
+    a = dict(q_lat=256, q_rope=256, batch=1, heads=16, scale=0.07, pool=256, num_pool_pages=4,
+             block_table=256, max_pages=4, seqlens=256, max_seqlen=100, sink=256, ring=256, tail=256,
+             out=256, lse=256, ws=256, ws_bytes=1 << 30)
+    a.update(kw)
+    L = mla.lib()
+    return L.mla_lowbit_decode(ctypes.byref(lay.c()), a["q_lat"], a["q_rope"], a["batch"], a["heads"],
+                               a["scale"], a["pool"], a["num_pool_pages"], a["block_table"],
+                               a["max_pages"], a["seqlens"], a["max_seqlen"], a["sink"], a["ring"],
+                               a["tail"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_rejects_bad_arguments_without_launch():
+    lay = mla.Layout(64, 4, 0.0, 4, 32)
+    assert _decode(lay, q_lat=None) == -2
+    assert _decode(lay, heads=0) == -2
+    assert _decode(lay, heads=129) == -2
+    assert _decode(lay, max_seqlen=4 * 64 + 1) == -2     # beyond the block table
+    assert _decode(lay, ws=512 + 16) == -2               # workspace not 256-B aligned
+    assert _decode(lay, ws_bytes=16) == -4
+    assert _decode(lay, scale=float("inf")) == -2
+    assert _decode(lay, out=258) == -2
+    assert _decode(lay, batch=0) == 0
+    assert _decode(mla.Layout(64, 3, 0.0, 4, 32)) == -1
+
+
+def test_strerror():
+    for c in (0, -1, -2, -3, -4, -5, 99):
+        assert isinstance(mla.strerror(c), str) and mla.strerror(c)

@@ -1,0 +1,191 @@
+"""GPU parity: the HIP writer and decode (through the C ABI) against the CPU
+oracle on the same seeded inputs.  Packed codes, metadata and BF16 copies must
+be bit-exact; decode outputs must be within max relative error 2e-3 per
+(sequence, head) row and lse within 2e-3."""
+import math
+
+import numpy as np
+import pytest
+
+from bit_kv_cache_writer_amd import workloads as wl
+
+from harness import (OracleCache, compare_cache, compare_decode, layouts, perm_block_table,
+                      random_queries, random_tokens, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_kv_cache_writer_amd import mla
+    mla.lib()
+    return torch
+
+
+def _to_dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def _build(torch, name, P, bits, clip, sink, local, lengths, seed, chunks=None):
+    from bit_kv_cache_writer_amd import mla
+    glay, olay = layouts(P, bits, clip, sink, local)
+    B = len(lengths)
+    cap = max(max(lengths), 1)
+    max_pages = (cap + P - 1) // P
+    bt, n_pool = perm_block_table(seed, B, max_pages)
+    toks = [random_tokens(seed * 1000 + b, max(L, 1)) for b, L in enumerate(lengths)]
+    gpu = mla.DeviceCache(glay, B, max_pages, bt, n_pool)
+    ref = OracleCache(olay, B, max_pages, bt, n_pool)
+    # oracle: one bulk append
+    ref.append(np.concatenate([t[0][:L] for t, L in zip(toks, lengths)]),
+               np.concatenate([t[1][:L] for t, L in zip(toks, lengths)]), lengths)
+    # GPU: bulk, or the given chunk schedule (list of per-sequence count lists)
+    chunks = chunks or [lengths]
+    pos = [0] * B
+    for counts in chunks:
+        ckv = np.concatenate([toks[b][0][pos[b]:pos[b] + c] for b, c in enumerate(counts)])
+        kr = np.concatenate([toks[b][1][pos[b]:pos[b] + c] for b, c in enumerate(counts)])
+        say(name, "GPU append", counts[:8])
+        gpu.append(_to_dev(torch, ckv), _to_dev(torch, kr), counts)
+        pos = [p + c for p, c in zip(pos, counts)]
+    torch.cuda.synchronize()
+    assert pos == list(lengths)
+    return gpu, ref
+
+
+CASES = [
+    # name, P, bits, clip, sink, local, lengths, heads
+    ("tiny_c4r4", 64, 4, 0.0, 4, 32, [256], 16),
+    ("tiny_L250_unfinished_page", 64, 4, 0.0, 4, 32, [250], 16),
+    ("c2r4_p128_ragged", 128, 2, 0.94, 4, 128, [700, 1000, 129, 5], 20),
+    ("c4r4_p128_ragged", 128, 4, 0.0, 4, 128, [0, 1, 127, 128, 129, 600, 1300], 16),
+    ("c4r4_p64_h128", 64, 4, 0.0, 4, 128, [300, 513], 128),
+    ("c2r4_p64_h64", 64, 2, 0.94, 4, 128, [1000, 2000], 64),
+    ("c4r4_p32_noprot_h7", 32, 4, 0.0, 0, 0, [64, 95, 200], 7),
+    ("c2r4_p256_allprot", 256, 2, 0.94, 8, 512, [300, 40], 16),
+    ("c4r4_p64_local8", 64, 4, 0.0, 2, 8, [150, 64, 63], 33),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_write_and_decode_parity(torch_cuda, case):
+    torch = torch_cuda
+    name, P, bits, clip, sink, local, lengths, H = case
+    gpu, ref = _build(torch, name, P, bits, clip, sink, local, lengths, seed=len(name))
+    say(name, "compare cache bytes")
+    compare_cache(gpu, ref)
+    ql, qr = random_queries(7 + H, len(lengths), H)
+    scale = 1.0 / math.sqrt(192.0)
+    say(name, "GPU decode", "heads", H)
+    out, lse = gpu.decode(_to_dev(torch, ql), _to_dev(torch, qr), scale)
+    torch.cuda.synchronize()
+    r_out, r_lse = ref.decode(ql, qr, scale)
+    worst = compare_decode(out.cpu().numpy(), lse.cpu().numpy(), r_out, r_lse)
+    say(name, f"worst row rel err {worst:.2e}")
+
+
+def test_chunked_appends_equal_bulk(torch_cuda):
+    """Token-by-token and ragged chunked appends (the decode-step writer) give
+    the same bytes as the oracle's single append."""
+    torch = torch_cuda
+    lengths = [200, 77, 130]
+    sched = [[1, 1, 1]] * 3 + [[60, 0, 5], [1, 70, 0], [64, 2, 64], [0, 1, 58]]
+    done = np.sum(sched, axis=0)
+    sched.append([int(L - d) for L, d in zip(lengths, done)])
+    gpu, ref = _build(torch, "chunked_c2r4", 64, 2, 0.94, 4, 32, lengths, seed=91, chunks=sched)
+    compare_cache(gpu, ref)
+    gpu2, ref2 = _build(torch, "chunked_c4r4", 32, 4, 0.0, 4, 8, lengths, seed=92,
+                        chunks=[[1, 1, 1]] * 7 + [[L - 7 for L in lengths]])
+    compare_cache(gpu2, ref2)
+
+
+def test_decode_edge_inputs(torch_cuda):
+    """Constant groups, all-zero tokens, bf16 subnormals and large outliers."""
+    torch = torch_cuda
+    from bit_kv_cache_writer_amd import mla
+    P, L = 64, 192
+    ckv, kr = random_tokens(5, L)
+    ckv[10] = 0
+    ckv[11] = wl.f32_to_bf16_bits(np.full(512, 0.3, np.float32))
+    ckv[12, :128] = wl.f32_to_bf16_bits(np.full(128, -2.5, np.float32))
+    ckv[13] = wl.f32_to_bf16_bits((np.arange(512) % 7 - 3).astype(np.float32) * 1e-39)
+    ckv[14, 5] = wl.f32_to_bf16_bits(np.float32(3000.0))
+    kr[20:40, 3] = wl.f32_to_bf16_bits(np.float32(-0.0))
+    for bits, clip in ((4, 0.0), (2, 0.94)):
+        glay, olay = layouts(P, bits, clip, 2, 16)
+        bt, n_pool = perm_block_table(3, 1, 3)
+        gpu = mla.DeviceCache(glay, 1, 3, bt, n_pool)
+        ref = OracleCache(olay, 1, 3, bt, n_pool)
+        ref.append(ckv, kr, [L])
+        say("edge inputs", bits)
+        gpu.append(_to_dev(torch, ckv), _to_dev(torch, kr), [L])
+        torch.cuda.synchronize()
+        compare_cache(gpu, ref)
+        ql, qr = random_queries(8, 1, 16)
+        out, lse = gpu.decode(_to_dev(torch, ql), _to_dev(torch, qr), 0.07)
+        torch.cuda.synchronize()
+        r_out, r_lse = ref.decode(ql, qr, 0.07)
+        compare_decode(out.cpu().numpy(), lse.cpu().numpy(), r_out, r_lse)
+
+
+# --------------------------------------------------------------------------
+# the configurations at their full sizes, in the launch configuration the
+# benchmark times; sampled sequences (and, for the many-head ones, a subset
+# of heads) are recomputed by the oracle one by one
+
+FULL = [("tiny_c4r4", [0], None), ("c4r4_h16_b8", [0, 7], None), ("c4r4_h16_b32", [5, 31], None),
+        ("c2r4_h20", [3], None), ("c4r4_h128", [17], [0, 1, 64, 127]),
+        ("c2r4_h64_long", [2], [0, 33, 63])]
+
+
+@pytest.mark.parametrize("wname,seqs,heads_sub", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(torch_cuda, wname, seqs, heads_sub):
+    torch = torch_cuda
+    from bit_kv_cache_writer_amd import mla
+    w = wl.WORKLOADS[wname]
+    glay, olay = layouts(w.page_size, w.latent_bits, w.clip_q, w.sink, w.local)
+    max_pages = w.pages_per_seq()
+    bt, n_pool = wl.block_table(w, max_pages)
+    gpu = mla.DeviceCache(glay, w.batch, max_pages, bt, n_pool)
+    n = w.seqlen
+    ckv_d = torch.empty((w.batch * n, 512), dtype=torch.int16, device="cuda")
+    kr_d = torch.empty((w.batch * n, 64), dtype=torch.int16, device="cuda")
+    say(wname, "generate inputs", w.batch, "x", n)
+    for b in range(w.batch):
+        c, k = wl.seq_tokens(w, b)
+        ckv_d[b * n:(b + 1) * n] = _to_dev(torch, c)
+        kr_d[b * n:(b + 1) * n] = _to_dev(torch, k)
+    say(wname, "GPU bulk write")
+    gpu.append(ckv_d, kr_d, [n] * w.batch)
+    del ckv_d, kr_d
+    ql, qr = wl.queries(w)
+    say(wname, "GPU decode")
+    out, lse = gpu.decode(_to_dev(torch, ql), _to_dev(torch, qr), w.softmax_scale)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    pool = gpu.pool.cpu().numpy()
+    ring, sink, tail = (gpu.ring.cpu().numpy().view(np.uint16), gpu.sink.cpu().numpy().view(np.uint16),
+                        gpu.tail.cpu().numpy().view(np.uint16))
+    hs = list(range(w.heads)) if heads_sub is None else heads_sub
+    for b in seqs:
+        say(wname, "oracle sequence", b)
+        ref = OracleCache(olay, 1, max_pages, bt[b:b + 1], n_pool)
+        c, k = wl.seq_tokens(w, b)
+        ref.append(c, k, [n])
+
+        class View:  # the GPU cache restricted to sequence b
+            pass
+        v = View()
+        import torch as _t
+        v.pool = _t.from_numpy(pool)
+        v.sink = _t.from_numpy(sink[b:b + 1].view(np.int16))
+        v.ring = _t.from_numpy(ring[b:b + 1].view(np.int16))
+        v.tail = _t.from_numpy(tail[b:b + 1].view(np.int16))
+        compare_cache(v, ref)
+        r_out, r_lse = ref.decode(np.ascontiguousarray(ql[b:b + 1, hs]), np.ascontiguousarray(qr[b:b + 1, hs]),
+                                  w.softmax_scale)
+        worst = compare_decode(out[b:b + 1, hs], lse[b:b + 1, hs], r_out, r_lse, seqs=[b])
+        say(wname, f"seq {b} worst row rel err {worst:.2e}")
