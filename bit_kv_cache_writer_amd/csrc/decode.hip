@@ -7,37 +7,39 @@
 // codes dequantized inside the loop -- the same reconstructed content tile
 // feeds both the score (matching) and the output (aggregation).
 //
-// How (one workgroup = 4 waves per (sequence, 16-head block, token split);
-// every wave walks its own 32-token tiles and keeps its own softmax state):
-//  * Codes are loaded straight from the page into the lanes that feed the
-//    score MFMA (v_mfma_f32_16x16x32_f16, M = 16 tokens, N = 16 heads,
-//    K = 32 channels): lane (t, g) holds 8 channels of token t.  They are
-//    unpacked in registers to fp16 x = 1 + code/kappa by OR-ing the code into
-//    the top of an fp16 mantissa (kappa = 16 for 4-bit codes, 4 for 2-bit).
-//  * The per-token group scale s and minimum m are folded after the MFMA:
-//    c = kappa s (x - 1) + m, so
-//      q.c = sum_g kappa s_g (q_g . x_g) + sum_g (m_g - kappa s_g) Q_g,
-//    with Q_g = sum of the query over group g.  The second sum is one more
-//    MFMA whose token operand is the raw fp16 (scale, min) metadata.
-//  * The positional key has a scale/min per channel and page, folded into a
-//    per-page query q' = q s (split into fp16 hi + lo halves) plus a per-page
-//    bias sum_c q_c (m_c - 16 s_c).
-//  * Scores come out of the MFMA with one head per lane, so the softmax
-//    probabilities are already laid out as the A operand of the output MFMA
-//    (M = heads, K = tokens); no transpose of P is needed.
-//  * The unpacked fp16 tile is also written to LDS (token-major rows) and read
-//    back with ds_read_b64_tr_b16, which hands every lane one channel of 4
-//    tokens -- the token-contiguous B operand of the output MFMA.
-//  * The output accumulates sum_j (p_j s_j) x_j per channel; the offset terms
-//    -kappa sum_j fp16(p_j s_j) and sum_j p_j m_j are kept per (head, group)
-//    in fp32 and applied once at the end.  The same rounded fp16 products
-//    enter both sums, so the offset cancels exactly.
-//  * The BF16 tokens (sink, recent window, and -- when the window is shorter
-//    than a page -- the k_R of an unfinished page) run through the same MFMA
-//    pipeline in one extra workgroup per (sequence, head block).
-//  * Each workgroup merges its 4 waves in LDS and writes one partial
-//    (unnormalized output, running max, sum) per head; a second kernel merges
-//    the partials with log-sum-exp weights.
+// How.  One workgroup of 4 waves (one per SIMD) per (sequence, 16-head block,
+// split of the sequence).  Each wave owns a contiguous run of 32-token tiles
+// (so consecutive tiles of a wave share a page); the waves advance in
+// lockstep rounds, one tile each:
+//  1. Scores.  The wave's codes arrive straight in the lanes that feed
+//     v_mfma_f32_16x16x32_f16 (M = 16 tokens, N = 16 heads, K = 32 channels;
+//     lane (t, g) holds 8 channels of token t), the next tile's codes already
+//     in flight.  Codes are unpacked in registers to fp16 x = 1 + code/kappa
+//     by OR-ing the code into the top of an fp16 mantissa (kappa = 16 for
+//     4-bit codes, 4 for 2-bit codes); the x tile also goes to LDS.  Group
+//     scale s and minimum m are folded after the MFMA:
+//       q.c = sum_g kappa s_g (q_g . x_g) + sum_g (m_g - kappa s_g) Q_g,
+//     Q_g = sum of the query over group g; the second sum is one more MFMA on
+//     the raw fp16 (scale, min) metadata.  The positional key's per-(channel,
+//     page) scale/min is folded into a per-page query q' = q s (fp16 hi + lo)
+//     and bias sum_c q_c (m_c - 16 s_c), rebuilt only when the page changes.
+//  2. Softmax.  The four tile maxima meet in LDS; every wave raises the same
+//     running max and turns its scores into fp16 weights P'_g = p s_g per
+//     latent group.  Sums of p, of P'_g and of p m_g stay per lane until the
+//     end.
+//  3. Output.  Wave w owns latent group w (128 output channels) for the four
+//     tiles of the round: A = P'_w, B = the x tile read back with
+//     ds_read_b64_tr_b16 (one channel of 4 tokens per lane).  The output
+//     accumulates sum_j fp16(p_j s_j) x_j; the offsets -kappa sum_j
+//     fp16(p_j s_j) and sum_j p_j m_j are applied at the end -- the same
+//     rounded fp16 products enter both, so they cancel.
+// Tile, page and address arithmetic is wave-uniform (scalar registers); the
+// page ids a workgroup needs are staged in LDS once.  BF16 tokens (sink,
+// recent window and, when the window is shorter than a page, tokens of the
+// unfinished page) are tiles of the same rounds: their rows are converted to
+// fp16 on their way into the x tile.  With several splits each workgroup
+// writes a partial (unnormalized output, max, sum); the last workgroup of a
+// (sequence, head block) merges them with log-sum-exp weights.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -50,16 +52,32 @@ namespace mla {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kThreads = 64 * kDecodeWaves;
-constexpr int kLdsRow = 1056;                    // bytes per token row: 512 fp16 + pad
-constexpr int kWaveLds = kTile * kLdsRow;        // 33792 B per wave
-constexpr float kPrescale = 1.0f / 256.0f;      // keeps q' and Q_g inside fp16 range
+constexpr int kWaves = kDecodeWaves;
+constexpr int kThreads = 64 * kWaves;
+// x-tile row: 512 fp16 + 16 B pad (260 dwords: rows land 4 banks apart, so
+// both the row-wise writes and the transposed reads are conflict-free)
+constexpr int kXRow = 1040;
+constexpr int kXTile = kTile * kXRow;
+// LDS map (bytes)
+constexpr int kOffX = 0;                              // [wave] x tiles
+constexpr int kPTile = 4 * 64 * 16;                   // [group][lane] fp16 x 8
+constexpr int kOffP = kOffX + kWaves * kXTile;        // [wave] P' tiles
+constexpr int kOffMeta = kOffP + kWaves * kPTile;     // [wave][group][32 tokens] dwords
+constexpr int kOffRMeta = kOffMeta + kWaves * 512;    // [wave] k_R metadata of a page
+constexpr int kOffMax = kOffRMeta + kWaves * 256;     // [head][wave] tile maxima
+constexpr int kPageWin = 2048;                        // page ids staged per workgroup
+constexpr int kOffPid = kOffMax + kHeadBlock * kWaves * 4;
+constexpr int kLdsBytes = kOffPid + kPageWin * 4;
+static_assert(kLdsBytes + 16 <= 160 * 1024, "LDS budget of a gfx950 CU");
+constexpr int kStatW = 9;  // per head: sum p, sum P'_g (4), sum p m_g (4)
+static_assert(kWaves * kHeadBlock * kStatW * 4 <= kWaves * kPTile, "final sums reuse the P' area");
+constexpr float kPrescale = 1.0f / 256.0f;  // keeps q' and Q_g inside fp16 range
 constexpr float kNegInf = -INFINITY;
 
 struct DecodeParams {
@@ -71,11 +89,14 @@ struct DecodeParams {
   const uint16_t* sink;
   const uint16_t* ring;
   const uint16_t* tail;
-  float* ws;
+  uint32_t* counters;
+  float* parts;
+  float* out;
+  float* lse;
   int32_t batch, heads, max_pages, num_pool_pages, max_seqlen;
-  int32_t n_hb, n_splits, n_parts;
-  int32_t P, sink_n, local;
-  int64_t latent_row, latent_meta_off, rope_codes_off, rope_meta_off, page_bytes;
+  int32_t n_hb, n_splits;
+  int32_t P, log2P, sink_n, local;
+  int64_t latent_meta_off, rope_codes_off, rope_meta_off, page_bytes;
   float c_log2;  // softmax_scale * log2(e)
 };
 
@@ -87,46 +108,56 @@ __device__ constexpr int chan_off(int d, int s) {
                    : 16 * (d >> 1) + 4 * (d & 1) + (s >> 1) + 8 * (s & 1);
 }
 
-// LDS column (slot order) -> latent channel.
+// x-tile column (slot order) -> latent channel.
 template <int BITS>
 __device__ inline int col_to_channel(int c) {
   return (c & ~31) + chan_off<BITS>((c >> 3) & 3, c & 7);
 }
 
+// Constants kept in VGPRs so that shift-and-merge compiles to one v_and_or_b32
+// per pair (a VOP3 instruction cannot encode two literal constants).
+struct UnpackK {
+  uint32_t m4, m2, e;
+};
+__device__ inline UnpackK unpack_k() {
+  UnpackK k;
+  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(k.e));
+  k.m4 = 0x03C003C0u;
+  k.m2 = 0x03000300u;
+  return k;
+}
+
 // 8 nibbles -> fp16 1 + code/16, slots [n0 n4 n1 n5 n2 n6 n3 n7].
-__device__ inline half8 unpack4(uint32_t w) {
-  const uint32_t M = 0x03C003C0u, E = 0x3C003C00u;
+__device__ inline half8 unpack4(uint32_t w, const UnpackK& k) {
   u32x4 v;
-  v[0] = ((w << 6) & M) | E;
-  v[1] = ((w << 2) & M) | E;
-  v[2] = ((w >> 2) & M) | E;
-  v[3] = ((w >> 6) & M) | E;
+  v[0] = ((w << 6) & k.m4) | k.e;
+  v[1] = ((w << 2) & k.m4) | k.e;
+  v[2] = ((w >> 2) & k.m4) | k.e;
+  v[3] = ((w >> 6) & k.m4) | k.e;
   return __builtin_bit_cast(half8, v);
 }
 
 // 8 of the 16 crumbs of w -> fp16 1 + code/4; hi = 0: crumbs [0 8 1 9 2 10 3 11],
 // hi = 1: crumbs [4 12 5 13 6 14 7 15].
-__device__ inline half8 unpack2(uint32_t w, int hi) {
-  const uint32_t M = 0x03000300u, E = 0x3C003C00u;
+__device__ inline half8 unpack2(uint32_t w, int hi, const UnpackK& k) {
   u32x4 v;
   if (hi == 0) {
-    v[0] = ((w << 8) & M) | E;
-    v[1] = ((w << 6) & M) | E;
-    v[2] = ((w << 4) & M) | E;
-    v[3] = ((w << 2) & M) | E;
+    v[0] = ((w << 8) & k.m2) | k.e;
+    v[1] = ((w << 6) & k.m2) | k.e;
+    v[2] = ((w << 4) & k.m2) | k.e;
+    v[3] = ((w << 2) & k.m2) | k.e;
   } else {
-    v[0] = (w & M) | E;
-    v[1] = ((w >> 2) & M) | E;
-    v[2] = ((w >> 4) & M) | E;
-    v[3] = ((w >> 6) & M) | E;
+    v[0] = (w & k.m2) | k.e;
+    v[1] = ((w >> 2) & k.m2) | k.e;
+    v[2] = ((w >> 4) & k.m2) | k.e;
+    v[3] = ((w >> 6) & k.m2) | k.e;
   }
   return __builtin_bit_cast(half8, v);
 }
 
 __device__ inline float bf16f(uint32_t h16) { return __uint_as_float(h16 << 16); }
-__device__ inline float h2f(uint32_t h16) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h16)));
-}
+__device__ inline float lo_f16(uint32_t w) { return static_cast<float>(__builtin_bit_cast(half2, w)[0]); }
+__device__ inline float hi_f16(uint32_t w) { return static_cast<float>(__builtin_bit_cast(half2, w)[1]); }
 
 __device__ inline f32x4 mfma(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -136,122 +167,45 @@ template <typename T>
 __device__ inline T ldg(const void* p) {
   return *reinterpret_cast<const T*>(p);
 }
+template <typename T>
+__device__ inline T lds_ld(const uint8_t* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+template <typename T>
+__device__ inline void lds_st(uint8_t* p, T v) {
+  *reinterpret_cast<T*>(p) = v;
+}
 
 __device__ inline void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
+// outstanding global load, which would drain the next tile's prefetch.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ inline float lane_group_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Sum / max over the four 16-lane rows (lanes l, l^16, l^32, l^48) with the
+// row-swap permutes (no LDS traffic); every row gets the same result.
+__device__ inline float row_allsum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
-__device__ inline float lane_group_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
-}
-
-// Codes of one 32-token tile in the score-MFMA lane layout.
-template <int BITS>
-struct TileCodes {
-  uint32_t lat[2][BITS == 4 ? 16 : 8];  // [token block][dwords of 4 groups]
-  u32x2 rope[2];
-};
-
-template <int BITS>
-__device__ inline void load_codes(TileCodes<BITS>& tc, const uint8_t* page, int slot0, int n16, int gq,
-                                  const DecodeParams& p) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const uint8_t* row = page + static_cast<int64_t>(slot0 + 16 * kb + n16) * p.latent_row;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (BITS == 4) {
-        const u32x4 v = ldg<u32x4>(row + 64 * i + 16 * gq);
-        tc.lat[kb][4 * i + 0] = v[0];
-        tc.lat[kb][4 * i + 1] = v[1];
-        tc.lat[kb][4 * i + 2] = v[2];
-        tc.lat[kb][4 * i + 3] = v[3];
-      } else {
-        const u32x2 v = ldg<u32x2>(row + 32 * i + 8 * gq);
-        tc.lat[kb][2 * i + 0] = v[0];
-        tc.lat[kb][2 * i + 1] = v[1];
-      }
-    }
-    tc.rope[kb] = ldg<u32x2>(page + p.rope_codes_off + static_cast<int64_t>(slot0 + 16 * kb + n16) * kRopeRowBytes + 8 * gq);
-  }
+__device__ inline float row_allmax(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-template <int BITS>
-__device__ inline half8 chunk_of(const TileCodes<BITS>& tc, int kb, int i, int d) {
-  if constexpr (BITS == 4) return unpack4(tc.lat[kb][4 * i + d]);
-  else return unpack2(tc.lat[kb][2 * i + (d >> 1)], d & 1);
-}
+// ---------------------------------------------------------------------------
+// query operands
 
-// Per-lane softmax / output state of one wave.
-struct WaveState {
-  f32x4 o[32];     // output accumulators: heads 4*gq + r, LDS columns 16k + n16
-  float m;         // running max (log2 domain) of head n16
-  float l;         // partial sum of p over this lane's tokens
-  float csum[4];   // partial sum of fp16(p * s_g) per group
-  float msum[4];   // partial sum of p * m_g per group
-};
-
-__device__ inline void state_init(WaveState& st) {
-#pragma unroll
-  for (int k = 0; k < 32; ++k) st.o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = kNegInf;
-  st.l = 0.f;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) st.csum[g] = st.msum[g] = 0.f;
-}
-
-// Raises the running max to cover a tile with max mt (per head, already
-// reduced over the lane groups) and rescales everything accumulated so far.
-__device__ inline void softmax_raise(WaveState& st, float mt, int gq) {
-  if (!__any(mt > st.m)) return;
-  const float mn = fmaxf(st.m, mt);
-  const float alpha = (mn == kNegInf || st.m == kNegInf) ? (st.m == kNegInf ? 0.f : 1.f) : exp2f(st.m - mn);
-  st.m = mn;
-  st.l *= alpha;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    st.csum[g] *= alpha;
-    st.msum[g] *= alpha;
-  }
-  float ah[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) ah[r] = __shfl(alpha, 4 * gq + r, 64);
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st.o[k][r] *= ah[r];
-  }
-}
-
-// Output MFMAs of one tile: B operand = LDS tile rows read transposed.
-__device__ inline void pv_tile(WaveState& st, const half8 (&pa)[4], const uint8_t* lds, int n16, int gq) {
-  const uint8_t* base = lds + (4 * gq + (n16 >> 2)) * kLdsRow + 8 * (n16 & 3);
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const uint8_t* a1 = base + 32 * k;
-    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(a1));
-    const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(a1 + 16 * kLdsRow));
-    // whole-vector shuffle + bit cast (element-wise casts of the transposed
-    // result were mis-assembled by the compiler)
-    const half8 vb = __builtin_bit_cast(half8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
-    st.o[k] = mfma(pa[k >> 3], vb, st.o[k]);
-  }
-}
-
-// Query operands of one 16-head block, in the slot order of the unpack.
 template <int BITS>
 struct QueryOps {
-  half8 lat[4][4];  // [group][chunk]
+  half8 lat[4][4];  // [group][chunk], slot order of the unpack
   half8 meta;       // (scale, min) slots of the metadata MFMA, prescaled
-  float qg[4];      // sum of q over each group (full, all lanes)
-  float qr[16];     // q_rope channels 16*gq .. 16*gq+15 (fp32)
+  uint32_t qr[8];   // bf16 pairs of q_rope channels 16*gq .. 16*gq+15
 };
 
 template <int BITS>
@@ -259,6 +213,7 @@ __device__ inline void load_query(QueryOps<BITS>& q, const DecodeParams& p, int 
   constexpr float kappa = BITS == 4 ? 16.f : 4.f;
   const bool hv = h < p.heads;
   const uint16_t* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + (hv ? h : 0)) * kLatentDim;
+  float qg[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float v[32];
@@ -274,7 +229,7 @@ __device__ inline void load_query(QueryOps<BITS>& q, const DecodeParams& p, int 
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < 32; ++c) s += v[c];
-    q.qg[i] = lane_group_sum(s);
+    qg[i] = row_allsum(s);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
@@ -283,59 +238,62 @@ __device__ inline void load_query(QueryOps<BITS>& q, const DecodeParams& p, int 
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float a = -kappa * q.qg[i] * kPrescale, c = q.qg[i] * kPrescale;
+    const float a = -kappa * qg[i] * kPrescale, c = qg[i] * kPrescale;
     const _Float16 ah = static_cast<_Float16>(a), ch = static_cast<_Float16>(c);
     const _Float16 al = static_cast<_Float16>(a - static_cast<float>(ah));
     const _Float16 cl = static_cast<_Float16>(c - static_cast<float>(ch));
-    q.meta[2 * i] = gq == 0 ? ah : (gq == 1 ? al : static_cast<_Float16>(0.f));
-    q.meta[2 * i + 1] = gq == 0 ? ch : (gq == 1 ? cl : static_cast<_Float16>(0.f));
+    const _Float16 z = static_cast<_Float16>(0.f);
+    q.meta[2 * i] = gq == 0 ? ah : (gq == 1 ? al : z);
+    q.meta[2 * i + 1] = gq == 0 ? ch : (gq == 1 ? cl : z);
   }
   const uint16_t* qr = p.q_rope + (static_cast<int64_t>(b) * p.heads + (hv ? h : 0)) * kRopeDim + 16 * gq;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const u32x4 w = hv ? ldg<u32x4>(qr + 8 * u) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      q.qr[8 * u + 2 * e] = bf16f(w[e] & 0xFFFFu);
-      q.qr[8 * u + 2 * e + 1] = bf16f(w[e] >> 16);
-    }
+    for (int e = 0; e < 4; ++e) q.qr[4 * u + e] = w[e];
   }
 }
 
-// Per-page positional-key operands: q' = q s / 16 prescaled (hi, lo) and the
-// bias sum_c q_c (m_c - 16 s_c), for channels 16*gq + 8e + slot order.
+// Per-page positional-key operands for channels 16*gq + 8e + slot order:
+// q' = q s * 16 / 256 as fp16 hi + lo, and bias sum_c q_c (m_c - 16 s_c).
 struct RopeOps {
   half8 hi[2], lo[2];
   float bias;
 };
 
-__device__ inline void rope_ops(RopeOps& r, const float (&qr)[16], const uint8_t* page, int gq,
-                                const DecodeParams& p) {
-  const uint16_t* meta = reinterpret_cast<const uint16_t*>(page + p.rope_meta_off);
-  const u32x4 s0 = ldg<u32x4>(meta + 16 * gq), s1 = ldg<u32x4>(meta + 16 * gq + 8);
-  const u32x4 m0 = ldg<u32x4>(meta + kRopeDim + 16 * gq), m1 = ldg<u32x4>(meta + kRopeDim + 16 * gq + 8);
-  float sc[16], mn[16];
+__device__ inline void rope_ops(RopeOps& r, const uint32_t (&qr)[8], const uint8_t* rmeta, int gq) {
+  const u32x4 s0 = lds_ld<u32x4>(rmeta + 32 * gq);
+  const u32x4 s1 = lds_ld<u32x4>(rmeta + 32 * gq + 16);
+  const u32x4 m0 = lds_ld<u32x4>(rmeta + 128 + 32 * gq);
+  const u32x4 m1 = lds_ld<u32x4>(rmeta + 128 + 32 * gq + 16);
+  float sc[16], mn[16], qv[16];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    sc[2 * e] = h2f(s0[e] & 0xFFFFu);
-    sc[2 * e + 1] = h2f(s0[e] >> 16);
-    sc[8 + 2 * e] = h2f(s1[e] & 0xFFFFu);
-    sc[8 + 2 * e + 1] = h2f(s1[e] >> 16);
-    mn[2 * e] = h2f(m0[e] & 0xFFFFu);
-    mn[2 * e + 1] = h2f(m0[e] >> 16);
-    mn[8 + 2 * e] = h2f(m1[e] & 0xFFFFu);
-    mn[8 + 2 * e + 1] = h2f(m1[e] >> 16);
+    sc[2 * e] = lo_f16(s0[e]);
+    sc[2 * e + 1] = hi_f16(s0[e]);
+    sc[8 + 2 * e] = lo_f16(s1[e]);
+    sc[8 + 2 * e + 1] = hi_f16(s1[e]);
+    mn[2 * e] = lo_f16(m0[e]);
+    mn[2 * e + 1] = hi_f16(m0[e]);
+    mn[8 + 2 * e] = lo_f16(m1[e]);
+    mn[8 + 2 * e + 1] = hi_f16(m1[e]);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    qv[2 * k] = bf16f(qr[k] & 0xFFFFu);
+    qv[2 * k + 1] = bf16f(qr[k] >> 16);
   }
   float bias = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) bias += qr[c] * (mn[c] - 16.f * sc[c]);
-  r.bias = lane_group_sum(bias);
+  for (int c = 0; c < 16; ++c) bias += qv[c] * (mn[c] - 16.f * sc[c]);
+  r.bias = row_allsum(bias);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
       const int c = 8 * e + chan_off<4>(0, sl);
-      const float v = qr[c] * sc[c] * (16.f * kPrescale);
+      const float v = qv[c] * sc[c] * (16.f * kPrescale);
       const _Float16 vh = static_cast<_Float16>(v);
       r.hi[e][sl] = vh;
       r.lo[e][sl] = static_cast<_Float16>(v - static_cast<float>(vh));
@@ -343,449 +301,622 @@ __device__ inline void rope_ops(RopeOps& r, const float (&qr)[16], const uint8_t
   }
 }
 
-// Token ranges of sequence b: packed [lo_p, hi_p); BF16 / tail otherwise.
-struct SeqRanges {
-  int L, lo_p, hi_p;
+// ---------------------------------------------------------------------------
+// packed tiles
+
+template <int BITS>
+struct Stage {
+  uint32_t lat[2][BITS == 4 ? 16 : 8];  // [token block][dwords of the 4 groups]
+  u32x2 rope[2];
+  u32x4 ma[2];     // latent metadata of tokens n16 and 16 + n16
+  uint32_t rmeta;  // 4 bytes of the page's k_R metadata (first tile of a page)
 };
 
-__device__ inline SeqRanges seq_ranges(const DecodeParams& p, int b) {
-  SeqRanges r;
-  int L = p.seqlens[b];
-  const int cap = min(p.max_seqlen, p.max_pages * p.P);
-  L = L < 0 ? 0 : (L > cap ? cap : L);
-  r.L = L;
-  r.lo_p = min(p.sink_n, L);
-  const int full = (L / p.P) * p.P;
-  r.hi_p = max(r.lo_p, min(L - p.local, full));
-  return r;
-}
-
-__device__ inline const uint8_t* page_ptr(const DecodeParams& p, int b, int pidx) {
-  if (pidx < 0 || pidx >= p.max_pages) return nullptr;
-  const int id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pidx];
-  if (id < 0 || id >= p.num_pool_pages) return nullptr;
-  return p.pool + static_cast<int64_t>(id) * p.page_bytes;
-}
-
-// One packed tile: tokens j0 .. j0+31 of one page, valid in [vlo, vhi).
-// Latent metadata of a tile: the MFMA operand rows (token n16 of each block)
-// and the values the fold needs (tokens 4*gq + r of each block).
-struct TileMeta {
-  u32x4 ma[2], ms[2][4];
+// Per-lane byte offsets inside a tile (constant over the kernel).
+struct LaneOffs {
+  uint32_t lat, rope, meta;
 };
 
-__device__ inline void load_meta(TileMeta& tm, const uint8_t* page, int slot0, int n16, int gq,
-                                 const DecodeParams& p) {
-  const uint8_t* meta = page + p.latent_meta_off;
+// Loads one 32-token tile whose first slot is slot0 of `page` (a wave-uniform
+// pointer); every address is page base (scalar) + 32-bit lane offset.
+template <int BITS>
+__device__ inline void load_stage(Stage<BITS>& sg, const uint8_t* page, int slot0, bool new_page,
+                                  const LaneOffs& lo, int lane, const DecodeParams& p) {
+  constexpr int kLatRow = kLatentDim * BITS / 8;
+  const uint8_t* lat = page + slot0 * kLatRow;
+  const uint8_t* rope = page + p.rope_codes_off + slot0 * kRopeRowBytes;
+  const uint8_t* meta = page + p.latent_meta_off + slot0 * 16;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    tm.ma[kb] = gq < 2 ? ldg<u32x4>(meta + (slot0 + 16 * kb + n16) * 16) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tm.ms[kb][r] = ldg<u32x4>(meta + (slot0 + 16 * kb + 4 * gq + r) * 16);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (BITS == 4) {
+        const u32x4 v = ldg<u32x4>(lat + lo.lat + (16 * kb * kLatRow + 64 * i));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sg.lat[kb][4 * i + e] = v[e];
+      } else {
+        const u32x2 v = ldg<u32x2>(lat + lo.lat + (16 * kb * kLatRow + 32 * i));
+        sg.lat[kb][2 * i + 0] = v[0];
+        sg.lat[kb][2 * i + 1] = v[1];
+      }
+    }
+    sg.rope[kb] = ldg<u32x2>(rope + lo.rope + 16 * kb * kRopeRowBytes);
+    sg.ma[kb] = ldg<u32x4>(meta + lo.meta + 16 * kb * 16);
   }
+  if (new_page) sg.rmeta = ldg<uint32_t>(page + p.rope_meta_off + 4 * lane);
 }
 
 template <int BITS>
-__device__ void packed_tile(WaveState& st, const QueryOps<BITS>& q, const RopeOps& ro,
-                            const TileCodes<BITS>& tc, const TileMeta& tm, int j0, int vlo, int vhi,
-                            uint8_t* lds, int n16, int gq, const DecodeParams& p) {
+__device__ inline half8 chunk_of(const Stage<BITS>& sg, int kb, int i, int d, const UnpackK& k) {
+  if constexpr (BITS == 4) return unpack4(sg.lat[kb][4 * i + d], k);
+  else return unpack2(sg.lat[kb][2 * i + (d >> 1)], d & 1, k);
+}
+
+// Scores of one packed tile (tokens j0 .. j0+31 of one complete page, valid in
+// [vlo, vhi)), in the log2 domain; the x tile goes to LDS.
+template <int BITS>
+__device__ void packed_scores(float (&sc)[8], const QueryOps<BITS>& q, RopeOps& ro, const Stage<BITS>& sg,
+                              bool new_page, int j0, int vlo, int vhi, uint8_t* xt, uint8_t* meta_lds,
+                              uint8_t* rmeta_lds, int lane, int n16, int gq, const DecodeParams& p) {
   constexpr float kappa = BITS == 4 ? 16.f : 4.f;
-  const u32x4(&ma)[2] = tm.ma;
-  const u32x4(&ms)[2][4] = tm.ms;
+  const UnpackK uk = unpack_k();
+  if (gq == 0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) lds_st<uint32_t>(meta_lds + (g * kTile + 16 * kb + n16) * 4, sg.ma[kb][g]);
+    }
+  }
+  if (new_page) {
+    lds_st<uint32_t>(rmeta_lds + 4 * lane, sg.rmeta);
+    lds_wait();
+    rope_ops(ro, q.qr, rmeta_lds, gq);
+  }
   f32x4 acc[2][5];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int g = 0; g < 5; ++g) acc[kb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint8_t* lrow = lds + (16 * kb + n16) * kLdsRow + 64 * gq;
+    uint8_t* lrow = xt + (16 * kb + n16) * kXRow + 64 * gq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int d = 0; d < 4; ++d) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const half8 x = chunk_of<BITS>(tc, kb, i, d);
+      for (int i = 0; i < 4; ++i) {
+        const half8 x = chunk_of<BITS>(sg, kb, i, d, uk);
         acc[kb][i] = mfma(x, q.lat[i][d], acc[kb][i]);
-        *reinterpret_cast<half8*>(lrow + 256 * i + 16 * d) = x;
+        lds_st<half8>(lrow + 256 * i + 16 * d, x);
       }
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const half8 xr = unpack4(tc.rope[kb][e]);
+      const half8 xr = unpack4(sg.rope[kb][e], uk);
       acc[kb][4] = mfma(xr, ro.hi[e], acc[kb][4]);
       acc[kb][4] = mfma(xr, ro.lo[e], acc[kb][4]);
     }
-    acc[kb][4] = mfma(__builtin_bit_cast(half8, ma[kb]), q.meta, acc[kb][4]);
+    acc[kb][4] = mfma(__builtin_bit_cast(half8, sg.ma[kb]), q.meta, acc[kb][4]);
   }
-  // fold the group scales, mask, online softmax
-  float sc[8];
-  bool valid[8];
-  float tmax = kNegInf;
+  lds_wait();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x4 mg = lds_ld<u32x4>(meta_lds + (g * kTile + 16 * kb + 4 * gq) * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = fmaf(lo_f16(mg[r]), acc[kb][g][r], v[r]);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = j0 + 16 * kb + 4 * gq + r;
-      const u32x4 mm = ms[kb][r];
-      float v = h2f(mm[0] & 0xFFFFu) * acc[kb][0][r];
-      v = fmaf(h2f(mm[1] & 0xFFFFu), acc[kb][1][r], v);
-      v = fmaf(h2f(mm[2] & 0xFFFFu), acc[kb][2][r], v);
-      v = fmaf(h2f(mm[3] & 0xFFFFu), acc[kb][3][r], v);
-      v = fmaf(v, kappa, fmaf(acc[kb][4][r], 256.f, ro.bias));
-      const bool ok = t >= vlo && t < vhi;
-      valid[4 * kb + r] = ok;
-      sc[4 * kb + r] = ok ? v * p.c_log2 : kNegInf;
-      tmax = fmaxf(tmax, sc[4 * kb + r]);
+      const float z = fmaf(v[r], kappa, fmaf(acc[kb][4][r], 256.f, ro.bias));
+      sc[4 * kb + r] = (t >= vlo && t < vhi) ? z * p.c_log2 : kNegInf;
     }
   }
-  tmax = lane_group_max(tmax);
-  softmax_raise(st, tmax, gq);
-  float pr[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    pr[k] = valid[k] ? exp2f(sc[k] - st.m) : 0.f;
-    st.l += pr[k];
-  }
-  half8 pa[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t w = ms[k >> 2][k & 3][g];
-      const float ps = valid[k] ? pr[k] * h2f(w & 0xFFFFu) : 0.f;
-      pa[g][k] = static_cast<_Float16>(ps);
-      st.csum[g] += static_cast<float>(pa[g][k]);
-      st.msum[g] += valid[k] ? pr[k] * h2f(w >> 16) : 0.f;
-    }
-  }
-  lds_wait();
-  pv_tile(st, pa, lds, n16, gq);
 }
 
-// Source of one BF16-path token (sink row, ring slot, or packed latent with
-// the k_R of an unfinished page from the tail buffer).
+// Weights of a packed tile: P'_g = fp16(fp16(p) s_g) per latent group into
+// LDS [group][lane]; adds this lane's sums of p, of the fp16 P'_g and of
+// p m_g to st.
+__device__ inline void packed_weights(const float (&pr)[8], const uint8_t* meta_lds, uint8_t* ptile,
+                                      float (&st)[kStatW], int lane, int gq) {
+  half2 ph[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    st[0] += pr[2 * k] + pr[2 * k + 1];
+    ph[k] = half2{static_cast<_Float16>(pr[2 * k]), static_cast<_Float16>(pr[2 * k + 1])};
+  }
+  const half2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const u32x4 mg0 = lds_ld<u32x4>(meta_lds + (g * kTile + 4 * gq) * 4);
+    const u32x4 mg1 = lds_ld<u32x4>(meta_lds + (g * kTile + 16 + 4 * gq) * 4);
+    half8 pa;
+    float cs = st[1 + g], ms = st[5 + g];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4& mg = (k >> 1) ? mg1 : mg0;
+      const uint32_t w0 = mg[2 * (k & 1)], w1 = mg[2 * (k & 1) + 1];
+      const half2 s2 = {__builtin_bit_cast(half2, w0)[0], __builtin_bit_cast(half2, w1)[0]};
+      const half2 m2 = {__builtin_bit_cast(half2, w0)[1], __builtin_bit_cast(half2, w1)[1]};
+      const half2 ps = ph[k] * s2;
+      cs = __builtin_amdgcn_fdot2(ps, ones, cs, false);
+      ms = __builtin_amdgcn_fdot2(ph[k], m2, ms, false);
+      pa[2 * k] = ps[0];
+      pa[2 * k + 1] = ps[1];
+    }
+    lds_st<half8>(ptile + g * 1024 + 16 * lane, pa);
+    st[1 + g] = cs;
+    st[5 + g] = ms;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// BF16-path tiles
+
+struct SeqRanges {
+  int L, lo_p, hi_p;  // packed tokens are [lo_p, hi_p)
+};
+
+__device__ inline SeqRanges seq_ranges(const DecodeParams& p, int b) {
+  SeqRanges r;
+  int L = uniform(p.seqlens[b]);
+  const int cap = min(p.max_seqlen, p.max_pages * p.P);
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  r.L = L;
+  r.lo_p = min(p.sink_n, L);
+  const int full = (L >> p.log2P) << p.log2P;
+  r.hi_p = max(r.lo_p, min(L - p.local, full));
+  return r;
+}
+
+__device__ inline const uint8_t* page_of_id(const DecodeParams& p, int id) {
+  if (id < 0 || id >= p.num_pool_pages) return nullptr;
+  return p.pool + static_cast<int64_t>(id) * p.page_bytes;
+}
+
+__device__ inline const uint8_t* page_ptr(const DecodeParams& p, int b, int pidx) {
+  if (pidx < 0 || pidx >= p.max_pages) return nullptr;
+  return page_of_id(p, p.block_table[static_cast<int64_t>(b) * p.max_pages + pidx]);
+}
+
+// Source of BF16-path token k: its BF16 row ([c_KV | k_R]) or, for a token of
+// the unfinished page outside the window, its packed latent and the BF16 k_R
+// of the tail buffer.  kind: 0 none, 1 row, 2 packed latent.
 struct DenseSrc {
-  const uint16_t* row;    // bf16 [576] row, or nullptr
-  const uint8_t* page;    // packed latent page when row == nullptr
-  const uint16_t* rope;   // bf16 k_R [64]
+  int kind;
+  const uint16_t* row;
+  const uint8_t* page;
+  const uint16_t* rope;
   int slot;
 };
 
 __device__ inline DenseSrc dense_src(const DecodeParams& p, int b, const SeqRanges& sr, int k) {
-  DenseSrc s{nullptr, nullptr, nullptr, 0};
+  DenseSrc s{0, nullptr, nullptr, nullptr, 0};
   const int n_dense = sr.lo_p + (sr.L - sr.hi_p);
-  if (k >= n_dense) return s;
+  if (k < 0 || k >= n_dense) return s;
   const int j = k < sr.lo_p ? k : sr.hi_p + (k - sr.lo_p);
   if (j < p.sink_n) {
+    s.kind = 1;
     s.row = p.sink + (static_cast<int64_t>(b) * p.sink_n + j) * kRowElems;
   } else if (p.local > 0 && j >= sr.L - p.local) {
+    s.kind = 1;
     s.row = p.ring + (static_cast<int64_t>(b) * p.local + j % p.local) * kRowElems;
   } else {
-    s.page = page_ptr(p, b, j / p.P);
-    s.slot = j % p.P;
-    s.rope = p.tail + (static_cast<int64_t>(b) * p.P + j % p.P) * kRopeDim;
-    if (!s.page) s.rope = nullptr;
+    s.page = page_ptr(p, b, j >> p.log2P);
+    if (s.page) {
+      s.kind = 2;
+      s.slot = j & (p.P - 1);
+      s.rope = p.tail + (static_cast<int64_t>(b) * p.P + s.slot) * kRopeDim;
+    }
   }
-  if (s.row) s.rope = s.row + kLatentDim;
+  if (s.kind == 1) s.rope = s.row + kLatentDim;
   return s;
 }
 
-// fp32 values of latent channels 128 i + 32 gq + (0..31) of a BF16-path token.
+// Scores of one BF16-path tile (dense indices k0 .. k0+31).  Rows are
+// converted to fp16 in the unpack's slot order into the x tile (latent) and
+// copied raw into rbuf (k_R), then fed to the same MFMAs.  (Loads go through
+// registers: an LDS-direct load would make every later LDS read of the kernel
+// wait for all outstanding global loads, prefetches included.)
 template <int BITS>
-__device__ inline void dense_latent(float (&v)[32], const DenseSrc& s, int i, int gq, const DecodeParams& p) {
-  if (s.row) {
+__device__ void dense_scores(float (&sc)[8], const QueryOps<BITS>& q, int b, const SeqRanges& sr, int k0,
+                             uint8_t* xt, uint8_t* rbuf, int lane, int n16, int gq, const DecodeParams& p) {
+  // k_R rows: token 8 u + lane / 8, bytes 16 (lane % 8) .. +15
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const DenseSrc s = dense_src(p, b, sr, k0 + 8 * u + (lane >> 3));
+    const u32x4 w = s.kind ? ldg<u32x4>(s.rope + 8 * (lane & 7)) : u32x4{0, 0, 0, 0};
+    lds_st<u32x4>(rbuf + u * 1024 + 16 * lane, w);
+  }
+  // latent rows: lane handles channels 16 part .. 16 part + 15 of rows
+  // lane / 32 + 2 m, four rows per batch
+  const int part = lane & 31;
+#pragma unroll 1
+  for (int m0 = 0; m0 < kTile / 2; m0 += 4) {
+    u32x4 ra[4], rc[4];
+    int kind[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const u32x4 w = ldg<u32x4>(s.row + 128 * i + 32 * gq + 8 * u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * u + 2 * e] = bf16f(w[e] & 0xFFFFu);
-        v[8 * u + 2 * e + 1] = bf16f(w[e] >> 16);
+      const int t = 2 * (m0 + u) + (lane >> 5);
+      const DenseSrc s = dense_src(p, b, sr, k0 + t);
+      kind[u] = s.kind;
+      ra[u] = u32x4{0, 0, 0, 0};
+      rc[u] = u32x4{0, 0, 0, 0};
+      if (s.kind == 1) {
+        ra[u] = ldg<u32x4>(s.row + 16 * part);
+        rc[u] = ldg<u32x4>(s.row + 16 * part + 8);
+      } else if (s.kind == 2) {
+        const uint8_t* row = s.page + s.slot * (kLatentDim * BITS / 8);
+        if constexpr (BITS == 4) {
+          const u32x2 w = ldg<u32x2>(row + 8 * part);
+          ra[u][0] = w[0];
+          ra[u][1] = w[1];
+        } else {
+          ra[u][0] = ldg<uint32_t>(row + 4 * part);
+        }
+        ra[u][2] = ldg<uint32_t>(s.page + p.latent_meta_off + s.slot * 16 + 4 * (part >> 3));
       }
     }
-  } else if (s.page) {
-    const uint32_t mw = ldg<uint32_t>(s.page + p.latent_meta_off + s.slot * 16 + 4 * i);
-    const float sc = h2f(mw & 0xFFFFu), mn = h2f(mw >> 16);
-    const uint8_t* row = s.page + static_cast<int64_t>(s.slot) * p.latent_row;
-    if constexpr (BITS == 4) {
-      const u32x4 w = ldg<u32x4>(row + 64 * i + 16 * gq);
 #pragma unroll
-      for (int c = 0; c < 32; ++c) v[c] = fmaf(static_cast<float>((w[c >> 3] >> (4 * (c & 7))) & 15u), sc, mn);
-    } else {
-      const u32x2 w = ldg<u32x2>(row + 32 * i + 8 * gq);
+    for (int u = 0; u < 4; ++u) {
+      const int t = 2 * (m0 + u) + (lane >> 5);
+      float v[16];
+      if (kind[u] == 2) {
+        const float scl = lo_f16(ra[u][2]), mn = hi_f16(ra[u][2]);
 #pragma unroll
-      for (int c = 0; c < 32; ++c) v[c] = fmaf(static_cast<float>((w[c >> 4] >> (2 * (c & 15))) & 3u), sc, mn);
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) v[c] = 0.f;
-  }
-}
-
-// One tile of BF16-path tokens (dense indices k0 .. k0+31).
-template <int BITS>
-__device__ void dense_tile(WaveState& st, const QueryOps<BITS>& q, const half8 (&qrp)[2], int b,
-                           const SeqRanges& sr, int k0, uint8_t* lds, int n16, int gq,
-                           const DecodeParams& p) {
-  constexpr float inv_kappa = BITS == 4 ? 1.f / 16.f : 1.f / 4.f;
-  f32x4 acc[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const DenseSrc s = dense_src(p, b, sr, k0 + 16 * kb + n16);
-    uint8_t* lrow = lds + (16 * kb + n16) * kLdsRow + 64 * gq;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[32];
-      dense_latent<BITS>(v, s, i, gq, p);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        half8 x;
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) x[sl] = static_cast<_Float16>(v[chan_off<BITS>(d, sl)]);
-        acc[kb] = mfma(x, q.lat[i][d], acc[kb]);
-        *reinterpret_cast<half8*>(lrow + 256 * i + 16 * d) = x;
-      }
-    }
-    float r[16];
-    if (s.rope) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 w = ldg<u32x4>(s.rope + 16 * gq + 8 * u);
+        for (int c = 0; c < 16; ++c) {
+          const uint32_t code = BITS == 4 ? (ra[u][c >> 3] >> (4 * (c & 7))) & 15u : (ra[u][0] >> (2 * c)) & 3u;
+          v[c] = fmaf(static_cast<float>(code), scl, mn);
+        }
+      } else {  // BF16 row, or zeros for a token past the end
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          r[8 * u + 2 * e] = bf16f(w[e] & 0xFFFFu);
-          r[8 * u + 2 * e + 1] = bf16f(w[e] >> 16);
+          v[2 * e] = bf16f(ra[u][e] & 0xFFFFu);
+          v[2 * e + 1] = bf16f(ra[u][e] >> 16);
+          v[8 + 2 * e] = bf16f(rc[u][e] & 0xFFFFu);
+          v[8 + 2 * e + 1] = bf16f(rc[u][e] >> 16);
         }
       }
-    } else {
+      // columns 16 part .. 16 part + 15 are chunks 2 (part & 1) and 2 (part & 1) + 1
+      // of lane group (part >> 1) & 3 in latent group part >> 3
+      half8 x0, x1;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) r[c] = 0.f;
+      for (int sl = 0; sl < 8; ++sl) {
+        x0[sl] = static_cast<_Float16>(v[chan_off<BITS>(0, sl)]);
+        x1[sl] = static_cast<_Float16>(v[chan_off<BITS>(1, sl)]);
+      }
+      uint8_t* cell = xt + t * kXRow + 32 * part;
+      lds_st<half8>(cell, x0);
+      lds_st<half8>(cell + 16, x1);
     }
+  }
+  lds_wait();
+  // score MFMAs from LDS
+  half8 qrp[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      half8 xr;
+  for (int e = 0; e < 2; ++e) {
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) xr[sl] = static_cast<_Float16>(r[8 * e + chan_off<4>(0, sl)]);
-      acc[kb] = mfma(xr, qrp[e], acc[kb]);
+    for (int sl = 0; sl < 8; ++sl) {
+      const int c = 8 * e + chan_off<4>(0, sl);
+      const uint32_t w = q.qr[c >> 1];
+      qrp[e][sl] = static_cast<_Float16>(bf16f((c & 1) ? (w >> 16) : (w & 0xFFFFu)));
     }
   }
   const int n_dense = sr.lo_p + (sr.L - sr.hi_p);
-  float sc[8];
-  bool valid[8];
-  float tmax = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* lrow = xt + (16 * kb + n16) * kXRow + 64 * gq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) acc = mfma(lds_ld<half8>(lrow + 256 * i + 16 * d), q.lat[i][d], acc);
+    }
+    const uint8_t* rrow = rbuf + (16 * kb + n16) * 128 + 32 * gq;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const u32x4 w = lds_ld<u32x4>(rrow + 16 * e);
+      half8 xr;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const int c = chan_off<4>(0, sl);
+        xr[sl] = static_cast<_Float16>(bf16f((c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu)));
+      }
+      acc = mfma(xr, qrp[e], acc);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int k = k0 + 16 * kb + 4 * gq + r;
-      const bool ok = k < n_dense;
-      valid[4 * kb + r] = ok;
-      sc[4 * kb + r] = ok ? acc[kb][r] * p.c_log2 : kNegInf;
-      tmax = fmaxf(tmax, sc[4 * kb + r]);
+      const bool ok = k0 + 16 * kb + 4 * gq + r < n_dense;
+      sc[4 * kb + r] = ok ? acc[r] * p.c_log2 : kNegInf;
     }
   }
-  tmax = lane_group_max(tmax);
-  softmax_raise(st, tmax, gq);
-  half8 pa1;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float pr = valid[k] ? exp2f(sc[k] - st.m) : 0.f;
-    st.l += pr;
-    pa1[k] = static_cast<_Float16>(pr * inv_kappa);
-  }
-  const half8 pa[4] = {pa1, pa1, pa1, pa1};
-  lds_wait();
-  pv_tile(st, pa, lds, n16, gq);
 }
+
+// First item whose cost prefix reaches c (items: D BF16 tiles of cost
+// kDenseCost, then packed tiles of cost 1).
+__device__ inline int item_of_cost(int c, int D) {
+  return c <= kDenseCost * D ? (c + kDenseCost - 1) / kDenseCost : D + (c - kDenseCost * D);
+}
+
+// ---------------------------------------------------------------------------
 
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_last;
   constexpr float kappa = BITS == 4 ? 16.f : 4.f;
-  const int part = blockIdx.x % p.n_parts;
-  const int hb = (blockIdx.x / p.n_parts) % p.n_hb;
-  const int b = blockIdx.x / (p.n_parts * p.n_hb);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int split = blockIdx.x % p.n_splits;
+  const int grp = blockIdx.x / p.n_splits;  // b * n_hb + hb
+  const int hb = grp % p.n_hb, b = grp / p.n_hb;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
   const int n16 = lane & 15, gq = lane >> 4;
-  const int h = hb * kHeadBlock + n16;
-  uint8_t* lds = smem + wave * kWaveLds;
+  uint8_t* const xt_own = smem + kOffX + wave * kXTile;
+  uint8_t* const p_own = smem + kOffP + wave * kPTile;
+  uint8_t* const meta_own = smem + kOffMeta + wave * 512;
+  uint8_t* const rmeta_own = smem + kOffRMeta + wave * 256;
+  float* const smax = reinterpret_cast<float*>(smem + kOffMax);
+  int* const s_pid = reinterpret_cast<int*>(smem + kOffPid);
 
   QueryOps<BITS> q;
-  load_query<BITS>(q, p, b, h, gq);
-  WaveState st;
-  state_init(st);
+  load_query<BITS>(q, p, b, hb * kHeadBlock + n16, gq);
   const SeqRanges sr = seq_ranges(p, b);
 
-  if (part < p.n_splits) {
-    // packed tokens: absolute 32-token tiles [t_lo, t_hi) of [lo_p, hi_p)
-    const int t_lo = sr.lo_p / kTile, t_hi = (sr.hi_p + kTile - 1) / kTile;
-    const int n_t = sr.hi_p > sr.lo_p ? t_hi - t_lo : 0;
-    const int per = (n_t + p.n_splits - 1) / p.n_splits;
-    const int s_lo = t_lo + part * per, s_hi = min(t_hi, s_lo + per);
-    RopeOps ro;
-    int ro_page = -1;
-    TileCodes<BITS> cur, nxt;
-    const uint8_t* cur_page = nullptr;
-    int tt = s_lo + wave;
-    if (n_t > 0 && tt < s_hi) {
-      cur_page = page_ptr(p, b, (tt * kTile) / p.P);
-      if (cur_page) load_codes<BITS>(cur, cur_page, (tt * kTile) % p.P, n16, gq, p);
-    }
-    for (; n_t > 0 && tt < s_hi; tt += kDecodeWaves) {
-      const int j0 = tt * kTile;
-      const int pidx = j0 / p.P;
-      if (cur_page && pidx != ro_page) {
-        rope_ops(ro, q.qr, cur_page, gq, p);
-        ro_page = pidx;
-      }
-      TileMeta tm;
-      if (cur_page) load_meta(tm, cur_page, j0 % p.P, n16, gq, p);
-      // prefetch the next tile's codes after this tile's metadata, so that
-      // waiting for the metadata never waits for the prefetch
-      const uint8_t* nxt_page = nullptr;
-      const int tn = tt + kDecodeWaves;
-      if (tn < s_hi) {
-        nxt_page = page_ptr(p, b, (tn * kTile) / p.P);
-        if (nxt_page) load_codes<BITS>(nxt, nxt_page, (tn * kTile) % p.P, n16, gq, p);
-      }
-      if (cur_page) packed_tile<BITS>(st, q, ro, cur, tm, j0, sr.lo_p, sr.hi_p, lds, n16, gq, p);
-      cur = nxt;
-      cur_page = nxt_page;
-    }
-  } else {
-    // BF16 path: plain fp16 rope query
-    half8 qrp[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl) qrp[e][sl] = static_cast<_Float16>(q.qr[8 * e + chan_off<4>(0, sl)]);
-    }
-    const int n_dense = sr.lo_p + (sr.L - sr.hi_p);
-    for (int k0 = wave * kTile; k0 < n_dense; k0 += kDecodeWaves * kTile)
-      dense_tile<BITS>(st, q, qrp, b, sr, k0, lds, n16, gq, p);
-  }
+  // this workgroup's items: BF16 tiles first (cost kDenseCost), then packed;
+  // wave w takes the contiguous run [my0, my1)
+  const int n_dense = sr.lo_p + (sr.L - sr.hi_p);
+  const int D = (n_dense + kTile - 1) / kTile;
+  const int t_lo = sr.lo_p / kTile;
+  const int T = sr.hi_p > sr.lo_p ? (sr.hi_p + kTile - 1) / kTile - t_lo : 0;
+  const int cost = kDenseCost * D + T;
+  const int cs = (cost + p.n_splits - 1) / p.n_splits;
+  const int c0 = min(cost, split * cs), c1 = min(cost, c0 + cs);
+  const int i0 = item_of_cost(c0, D), i1 = item_of_cost(c1, D);
+  const int rounds = (i1 - i0 + kWaves - 1) / kWaves;
+  const int my0 = i0 + wave * rounds, my1 = min(i1, my0 + rounds);
 
-  // finish this wave: offsets of the output, totals per head
-  st.l = lane_group_sum(st.l);
-  float cs[4], msum[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    cs[g] = lane_group_sum(st.csum[g]);
-    msum[g] = lane_group_sum(st.msum[g]);
+  // page ids of the packed items, staged once
+  const int ip0 = max(i0, D);
+  int pg_first = 0, n_pg = 0;
+  if (i1 > ip0) {
+    pg_first = ((t_lo + ip0 - D) * kTile) >> p.log2P;
+    n_pg = (((t_lo + i1 - 1 - D) * kTile) >> p.log2P) - pg_first + 1;
   }
-  float corr_c[4][4], corr_m[4][4];  // [row r][group]
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      corr_c[r][g] = __shfl(cs[g], 4 * gq + r, 64);
-      corr_m[r][g] = __shfl(msum[g], 4 * gq + r, 64);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st.o[k][r] = fmaf(kappa, st.o[k][r] - corr_c[r][k >> 3], corr_m[r][k >> 3]);
-  }
-  float mr[4], lr[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mr[r] = __shfl(st.m, 4 * gq + r, 64);
-    lr[r] = __shfl(st.l, 4 * gq + r, 64);
-  }
-
-  // merge the waves of the workgroup in LDS (reusing the tile buffers)
-  __syncthreads();
-  float* mine = reinterpret_cast<float*>(smem + wave * kWaveLds);
-  if (wave > 0) {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mine[(4 * k + r) * 64 + lane] = st.o[k][r];
-    }
-    if (n16 == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        mine[8192 + 4 * gq + r] = mr[r];
-        mine[8192 + 16 + 4 * gq + r] = lr[r];
-      }
-    }
+  const int32_t* bt_row = p.block_table + static_cast<int64_t>(b) * p.max_pages;
+  for (int k = threadIdx.x; k < min(n_pg, kPageWin); k += kThreads) s_pid[k] = bt_row[pg_first + k];
+  if (my0 >= my1) {  // a wave without tiles still feeds zeros to the output MFMAs
+    for (int o = 16 * lane; o < kXTile; o += 64 * 16) lds_st<u32x4>(xt_own + o, u32x4{0, 0, 0, 0});
   }
   __syncthreads();
-  if (wave != 0) return;
-  float mtot[4], f[kDecodeWaves][4], ltot[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) mtot[r] = mr[r];
-#pragma unroll
-  for (int w = 1; w < kDecodeWaves; ++w) {
-    const float* other = reinterpret_cast<const float*>(smem + w * kWaveLds);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mtot[r] = fmaxf(mtot[r], other[8192 + 4 * gq + r]);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    f[0][r] = mr[r] == kNegInf ? 0.f : exp2f(mr[r] - mtot[r]);
-    ltot[r] = f[0][r] * lr[r];
-  }
-#pragma unroll
-  for (int w = 1; w < kDecodeWaves; ++w) {
-    const float* other = reinterpret_cast<const float*>(smem + w * kWaveLds);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mw = other[8192 + 4 * gq + r];
-      f[w][r] = mw == kNegInf ? 0.f : exp2f(mw - mtot[r]);
-      ltot[r] += f[w][r] * other[8192 + 16 + 4 * gq + r];
-    }
-  }
-  float* out = p.ws + ((static_cast<int64_t>(b) * p.n_parts + part) * p.n_hb + hb) * kPartFloats;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int ch = col_to_channel<BITS>(16 * k + n16);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = f[0][r] * st.o[k][r];
-#pragma unroll
-      for (int w = 1; w < kDecodeWaves; ++w) {
-        const float* other = reinterpret_cast<const float*>(smem + w * kWaveLds);
-        v = fmaf(f[w][r], other[(4 * k + r) * 64 + lane], v);
-      }
-      out[(4 * gq + r) * kLatentDim + ch] = v;
-    }
-  }
-  if (n16 == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      out[kHeadBlock * kLatentDim + 4 * gq + r] = mtot[r];
-      out[kHeadBlock * kLatentDim + kHeadBlock + 4 * gq + r] = ltot[r];
-    }
-  }
-}
+  auto page_ptr_of = [&](int pidx) -> const uint8_t* {
+    const int k = pidx - pg_first;
+    const int id = uniform(k < kPageWin ? *reinterpret_cast<volatile int*>(s_pid + k) : bt_row[pidx]);
+    return page_of_id(p, id);
+  };
 
-// Merges the partials of every (sequence, head): log-sum-exp weights.
-__global__ void __launch_bounds__(128) combine_kernel(const float* ws, float* out, float* lse, int heads,
-                                                      int n_hb, int n_parts) {
-  const int bh = blockIdx.x;
-  const int b = bh / heads, h = bh % heads;
-  const int hb = h / kHeadBlock, hl = h % kHeadBlock;
-  const int tid = threadIdx.x;
-  float mtot = kNegInf;
-  for (int s = 0; s < n_parts; ++s) {
-    const float* part = ws + ((static_cast<int64_t>(b) * n_parts + s) * n_hb + hb) * kPartFloats;
-    mtot = fmaxf(mtot, part[kHeadBlock * kLatentDim + hl]);
+  const LaneOffs lo{static_cast<uint32_t>(n16 * (kLatentDim * BITS / 8) + (BITS == 4 ? 16 : 8) * gq),
+                    static_cast<uint32_t>(n16 * kRopeRowBytes + 8 * gq), static_cast<uint32_t>(n16 * 16)};
+
+  // running max: m_run for head n16 (score layout), m_o[r] for heads 4 gq + r
+  // (output layout); identical in every wave.  Output of latent group `wave`:
+  // heads 4 gq + r, columns 16 kk + n16.  Per-lane sums (head n16): st.
+  float m_run = kNegInf;
+  float m_o[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+  f32x4 o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float st[kStatW];
+#pragma unroll
+  for (int k = 0; k < kStatW; ++k) st[k] = 0.f;
+
+  Stage<BITS> cur, nxt;
+  RopeOps ro;
+  int ro_page = -1;
+  // Loads packed item `it` into sg; returns its page index, -1 for a BF16
+  // item or none, -2 for a page missing from the block table.
+  auto stage_for = [&](Stage<BITS>& sg, int it, int prev_page) -> int {
+    if (it >= my1 || it < D) return -1;
+    const int j0 = (t_lo + (it - D)) * kTile;
+    const int pidx = j0 >> p.log2P;
+    const uint8_t* page = page_ptr_of(pidx);
+    if (!page) return -2;
+    load_stage<BITS>(sg, page, j0 & (p.P - 1), pidx != prev_page, lo, lane, p);
+    return pidx;
+  };
+  int cur_pidx = stage_for(cur, my0, ro_page);
+
+  for (int r = 0; r < rounds; ++r) {
+    const int it = my0 + r;
+    const int nxt_pidx = stage_for(nxt, it + 1, cur_pidx >= 0 ? cur_pidx : ro_page);
+
+    // 1. scores of this wave's tile
+    float sc[8];
+    bool has = it < my1;
+    const bool dense = has && it < D;
+    if (dense) {
+      dense_scores<BITS>(sc, q, b, sr, it * kTile, xt_own, p_own, lane, n16, gq, p);
+    } else if (has && cur_pidx >= 0) {
+      const int j0 = (t_lo + (it - D)) * kTile;
+      const bool new_page = cur_pidx != ro_page;
+      packed_scores<BITS>(sc, q, ro, cur, new_page, j0, sr.lo_p, sr.hi_p, xt_own, meta_own, rmeta_own, lane,
+                          n16, gq, p);
+      ro_page = cur_pidx;
+    } else {
+      has = false;
+    }
+    if (!has) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sc[k] = kNegInf;
+    }
+    float tmax = kNegInf;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tmax = fmaxf(tmax, sc[k]);
+    tmax = row_allmax(tmax);
+    if (gq == 0) smax[n16 * kWaves + wave] = tmax;
+    lds_barrier();
+
+    // 2. softmax: common running max, this tile's weights
+    {
+      const f32x4 mv = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + n16 * kWaves));
+      const float rmax = fmaxf(m_run, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+      const float alpha = m_run == kNegInf ? 0.f : exp2f(m_run - rmax);
+      m_run = rmax;
+#pragma unroll
+      for (int k = 0; k < kStatW; ++k) st[k] *= alpha;
+    }
+    if (has) {
+      float pr[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pr[k] = sc[k] == kNegInf ? 0.f : exp2f(sc[k] - m_run);
+      if (dense) {
+        half8 pa;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          st[0] += pr[k];
+          pa[k] = static_cast<_Float16>(pr[k] * (1.f / kappa));
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) lds_st<half8>(p_own + g * 1024 + 16 * lane, pa);
+      } else {
+        packed_weights(pr, meta_own, p_own, st, lane, gq);
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) lds_st<u32x4>(p_own + g * 1024 + 16 * lane, u32x4{0, 0, 0, 0});
+    }
+    // output-layout copy of the running max: heads 4 gq + rr
+    float ah[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x4 mv = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + (4 * gq + rr) * kWaves));
+      const float rmax = fmaxf(m_o[rr], fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+      ah[rr] = m_o[rr] == kNegInf ? 0.f : exp2f(m_o[rr] - rmax);
+      m_o[rr] = rmax;
+    }
+    lds_barrier();
+
+    // 3. output of latent group `wave` for the four tiles of the round
+    if (__any(ah[0] != 1.f || ah[1] != 1.f || ah[2] != 1.f || ah[3] != 1.f)) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) o[k][rr] *= ah[rr];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kWaves; ++t) {
+      const half8 pa = lds_ld<half8>(smem + kOffP + t * kPTile + wave * 1024 + 16 * lane);
+      // B operand: slots 0-3 tokens 4 gq + j, slots 4-7 tokens 16 + 4 gq + j
+      const uint8_t* base =
+          smem + kOffX + t * kXTile + (4 * gq + (n16 >> 2)) * kXRow + 8 * (n16 & 3) + 256 * wave;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const uint8_t* a1 = base + 32 * kk;
+        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a1));
+        const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(a1 + 16 * kXRow));
+        // whole-vector shuffle + bit cast: assembling the operand element by
+        // element from the transposed reads produced wrong code with this compiler
+        const half8 vb = __builtin_bit_cast(half8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[kk] = mfma(pa, vb, o[kk]);
+      }
+    }
+    lds_barrier();
+    cur = nxt;
+    cur_pidx = nxt_pidx;
   }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float ltot = 0.f;
-  for (int s = 0; s < n_parts; ++s) {
-    const float* part = ws + ((static_cast<int64_t>(b) * n_parts + s) * n_hb + hb) * kPartFloats;
-    const float ms = part[kHeadBlock * kLatentDim + hl];
-    if (ms == kNegInf) continue;
-    const float f = exp2f(ms - mtot);
-    ltot = fmaf(f, part[kHeadBlock * kLatentDim + kHeadBlock + hl], ltot);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(part + hl * kLatentDim + 4 * tid);
-    acc += f * o;
+
+  // per-head sums of every wave, through the (now idle) P' area
+  float* const sfin = reinterpret_cast<float*>(smem + kOffP);
+#pragma unroll
+  for (int k = 0; k < kStatW; ++k) {
+    const float v = row_allsum(st[k]);
+    if (gq == 0) sfin[(wave * kHeadBlock + n16) * kStatW + k] = v;
   }
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(bh) * kLatentDim + 4 * tid) = acc * inv;
-  if (tid == 0) lse[bh] = ltot > 0.f ? (mtot + log2f(ltot)) * 0.69314718055994531f : kNegInf;
+  __syncthreads();
+  const bool direct = p.n_splits == 1;
+  float* part = p.parts + (static_cast<int64_t>(grp) * p.n_splits + split) * kPartFloats;
+  float l_h[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int hh = 4 * gq + rr, hg = hb * kHeadBlock + hh;
+    float l = 0.f, c = 0.f, m = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* f = sfin + (w * kHeadBlock + hh) * kStatW;
+      l += f[0];
+      c += f[1 + wave];
+      m += f[5 + wave];
+    }
+    l_h[rr] = l;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const float v = fmaf(kappa, o[kk][rr] - c, m);
+      const int ch = col_to_channel<BITS>(128 * wave + 16 * kk + n16);
+      if (direct) {
+        if (hg < p.heads) p.out[(static_cast<int64_t>(b) * p.heads + hg) * kLatentDim + ch] = v * inv;
+      } else {
+        part[hh * kLatentDim + ch] = v;
+      }
+    }
+  }
+  if (wave == 0 && n16 == 0) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int hh = 4 * gq + rr, hg = hb * kHeadBlock + hh;
+      if (direct) {
+        if (hg < p.heads)
+          p.lse[static_cast<int64_t>(b) * p.heads + hg] =
+              l_h[rr] > 0.f ? (m_o[rr] + log2f(l_h[rr])) * 0.69314718055994531f : kNegInf;
+      } else {
+        part[kHeadBlock * kLatentDim + hh] = m_o[rr];
+        part[kHeadBlock * kLatentDim + kHeadBlock + hh] = l_h[rr];
+      }
+    }
+  }
+  if (direct) return;
+
+  // the last workgroup of this (sequence, head block) merges the partials
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(p.counters + grp, 1u) == static_cast<uint32_t>(p.n_splits - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const float* parts = p.parts + static_cast<int64_t>(grp) * p.n_splits * kPartFloats;
+  // (max, sum) of every split and head into LDS, then per-split weights
+  float* const sml = reinterpret_cast<float*>(smem + kOffX);  // [split][max 16 | sum 16]
+  for (int k = threadIdx.x; k < p.n_splits * 2 * kHeadBlock; k += kThreads)
+    sml[k] = parts[(k / (2 * kHeadBlock)) * kPartFloats + kHeadBlock * kLatentDim + k % (2 * kHeadBlock)];
+  __syncthreads();
+  const int th = threadIdx.x >> 4;          // head of this thread
+  const int c0o = (threadIdx.x & 15) * 32;  // its 32 channels
+  float M = kNegInf;
+  for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, sml[s * 2 * kHeadBlock + th]);
+  f32x4 acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < p.n_splits; ++s) {
+    const float m_s = sml[s * 2 * kHeadBlock + th];
+    const float f = m_s == kNegInf ? 0.f : exp2f(m_s - M);
+    L = fmaf(f, sml[s * 2 * kHeadBlock + kHeadBlock + th], L);
+    const float* ps = parts + static_cast<int64_t>(s) * kPartFloats + th * kLatentDim + c0o;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += f * ldg<f32x4>(ps + 4 * u);
+  }
+  const int hg = hb * kHeadBlock + th;
+  if (hg < p.heads) {
+    const float il = L > 0.f ? 1.f / L : 0.f;
+    float* o2 = p.out + (static_cast<int64_t>(b) * p.heads + hg) * kLatentDim + c0o;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4*>(o2 + 4 * u) = acc[u] * il;
+    if ((threadIdx.x & 15) == 0)
+      p.lse[static_cast<int64_t>(b) * p.heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+  }
+  if (threadIdx.x == 0) p.counters[grp] = 0u;
 }
 
 }  // namespace
@@ -826,7 +957,10 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   p.sink = static_cast<const uint16_t*>(sink_buf);
   p.ring = static_cast<const uint16_t*>(ring_buf);
   p.tail = static_cast<const uint16_t*>(rope_tail);
-  p.ws = static_cast<float*>(workspace);
+  p.counters = static_cast<uint32_t*>(workspace);
+  p.parts = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.counter_bytes);
+  p.out = out;
+  p.lse = lse;
   p.batch = batch;
   p.heads = heads;
   p.max_pages = max_pages;
@@ -834,34 +968,32 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   p.max_seqlen = max_seqlen;
   p.n_hb = plan.n_hb;
   p.n_splits = plan.n_splits;
-  p.n_parts = plan.n_parts;
   p.P = g.page_size;
+  p.log2P = 0;
+  while ((1 << p.log2P) < g.page_size) ++p.log2P;
   p.sink_n = g.sink;
   p.local = g.local;
-  p.latent_row = g.latent_row;
   p.latent_meta_off = g.latent_meta_off;
   p.rope_codes_off = g.rope_codes_off;
   p.rope_meta_off = g.rope_meta_off;
   p.page_bytes = g.page_bytes;
   p.c_log2 = softmax_scale * 1.44269504088896341f;
-  const int64_t blocks = static_cast<int64_t>(batch) * plan.n_hb * plan.n_parts;
+  const int64_t blocks = static_cast<int64_t>(batch) * plan.n_hb * plan.n_splits;
   if (blocks > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
-  const size_t lds = static_cast<size_t>(kDecodeWaves) * kWaveLds;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<4>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess ||
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<2>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
       return MLA_LOWBIT_ERR_HIP;
     attr_set = true;
   }
   if (g.latent_bits == 4)
-    hipLaunchKernelGGL(decode_kernel<4>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), lds, stream, p);
+    hipLaunchKernelGGL(decode_kernel<4>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), kLdsBytes,
+                       stream, p);
   else
-    hipLaunchKernelGGL(decode_kernel<2>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), lds, stream, p);
-  if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(batch * heads)), dim3(128), 0, stream,
-                     p.ws, out, lse, heads, plan.n_hb, plan.n_parts);
+    hipLaunchKernelGGL(decode_kernel<2>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), kLdsBytes,
+                       stream, p);
   return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
 }

@@ -237,22 +237,29 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, xl, xr, lane);
   }
 
-  // k_R of a page that becomes full: per channel over its P tokens.
+  // k_R of a page that becomes full: per channel over its P tokens.  The
+  // page's P rows (tail buffer for tokens of earlier calls, input rows for
+  // new ones) are first staged in LDS with 16-byte loads, all in flight at
+  // once, then reduced per channel from LDS.
+  __shared__ uint4 s_rows[256 * kRopeDim / 8];  // P x 64 bf16
   __shared__ float s_min[kWaves][kRopeDim], s_max[kWaves][kRopeDim];
   __shared__ float s_minf[kRopeDim], s_sf[kRopeDim];
   __shared__ uint8_t s_code[256 * kRopeDim];
   const bool completes = (pg + 1) * P <= end;
   if (completes) {
-    const int c = threadIdx.x & 63, part = threadIdx.x >> 6;
-    auto value = [&](int slot) -> float {
+    for (int i = threadIdx.x; i < P * (kRopeDim / 8); i += kThreads) {
+      const int slot = i >> 3, q = i & 7;
       const int t = pg * P + slot;
-      const uint16_t h = t < sb ? tail[static_cast<int64_t>(slot) * kRopeDim + c]
-                                : p.k_r[(r0 + (t - sb)) * static_cast<int64_t>(kRopeDim) + c];
-      return canon_zero(bf16_to_f32(h));
-    };
+      const uint4* src = t < sb ? reinterpret_cast<const uint4*>(tail + static_cast<int64_t>(slot) * kRopeDim) + q
+                                : reinterpret_cast<const uint4*>(p.k_r + (r0 + (t - sb)) * static_cast<int64_t>(kRopeDim)) + q;
+      s_rows[i] = *src;
+    }
+    __syncthreads();
+    const uint16_t* rows = reinterpret_cast<const uint16_t*>(s_rows);
+    const int c = threadIdx.x & 63, part = threadIdx.x >> 6;
     float mn = 3.0e38f, mx = -3.0e38f;
     for (int s = part; s < P; s += kWaves) {
-      const float v = value(s);
+      const float v = canon_zero(bf16_to_f32(rows[s * kRopeDim + c]));
       mn = fminf(mn, v);
       mx = fmaxf(mx, v);
     }
@@ -281,7 +288,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
     for (int s = part; s < P; s += kWaves) {
       uint32_t code = 0;
       if (sf > 0.0f) {
-        const float t = (value(s) - minf) / sf;
+        const float t = (canon_zero(bf16_to_f32(rows[s * kRopeDim + c])) - minf) / sf;
         float r = rintf(t);
         r = fminf(fmaxf(r, 0.0f), 15.0f);
         code = static_cast<uint32_t>(r);

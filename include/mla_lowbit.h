@@ -152,7 +152,10 @@ int mla_lowbit_decode_workspace(const mla_lowbit_layout* layout, int32_t batch, 
  *   max_seqlen     host bound used for the work split; <= max_pages * P
  *   out            fp32 [batch][heads][512];  lse fp32 [batch][heads]
  *   workspace      device scratch of at least mla_lowbit_decode_workspace()
- *                  bytes, 256-B aligned; contents need no initialization
+ *                  bytes, 256-B aligned.  Its first bytes hold arrival
+ *                  counters: zero-fill the workspace once before its first
+ *                  use; every call leaves the counters at zero again.  Calls
+ *                  that share a workspace must not run concurrently.
  * Queries are converted to fp16 inside the kernel: |q| must be below 65504
  * (values under 2^-14 in magnitude keep an absolute accuracy of 2^-25).
  */
