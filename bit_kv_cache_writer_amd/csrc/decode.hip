@@ -8,16 +8,18 @@
 // feeds both the score (matching) and the output (aggregation).
 //
 // How.  One workgroup of 4 waves (one per SIMD) per (sequence, 16-head block,
-// split of the sequence).  Each wave owns a contiguous run of 32-token tiles
-// (so consecutive tiles of a wave share a page); the waves advance in
+// split of the sequence); two workgroups share a CU, so one fills the other's
+// barrier and memory waits.  Each wave owns a contiguous run of 16-token
+// tiles (consecutive tiles of a wave share a page); the waves advance in
 // lockstep rounds, one tile each:
 //  1. Scores.  The wave's codes arrive straight in the lanes that feed
 //     v_mfma_f32_16x16x32_f16 (M = 16 tokens, N = 16 heads, K = 32 channels;
-//     lane (t, g) holds 8 channels of token t), the next tile's codes already
-//     in flight.  Codes are unpacked in registers to fp16 x = 1 + code/kappa
-//     by OR-ing the code into the top of an fp16 mantissa (kappa = 16 for
-//     4-bit codes, 4 for 2-bit codes); the x tile also goes to LDS.  Group
-//     scale s and minimum m are folded after the MFMA:
+//     lane (t, g) holds 8 channels of token t); the next tile's codes are
+//     requested as soon as these are unpacked.  Codes are unpacked in
+//     registers to fp16 x = 1 + code/kappa by OR-ing the code into the top of
+//     an fp16 mantissa (kappa = 16 for 4-bit codes, 4 for 2-bit codes); the x
+//     tile also goes to LDS.  Group scale s and minimum m are folded after the
+//     MFMA:
 //       q.c = sum_g kappa s_g (q_g . x_g) + sum_g (m_g - kappa s_g) Q_g,
 //     Q_g = sum of the query over group g; the second sum is one more MFMA on
 //     the raw fp16 (scale, min) metadata.  The positional key's per-(channel,
@@ -28,18 +30,19 @@
 //     latent group.  Sums of p, of P'_g and of p m_g stay per lane until the
 //     end.
 //  3. Output.  Wave w owns latent group w (128 output channels) for the four
-//     tiles of the round: A = P'_w, B = the x tile read back with
-//     ds_read_b64_tr_b16 (one channel of 4 tokens per lane).  The output
-//     accumulates sum_j fp16(p_j s_j) x_j; the offsets -kappa sum_j
-//     fp16(p_j s_j) and sum_j p_j m_j are applied at the end -- the same
-//     rounded fp16 products enter both, so they cancel.
+//     tiles of the round, taken in pairs (K = 32 tokens): A = P'_w, B = the x
+//     tiles read back with ds_read_b64_tr_b16 (one channel of 4 tokens per
+//     lane).  The output accumulates sum_j fp16(p_j s_j) x_j; the offsets
+//     -kappa sum_j fp16(p_j s_j) and sum_j p_j m_j are applied at the end --
+//     the same rounded fp16 products enter both, so they cancel.
 // Tile, page and address arithmetic is wave-uniform (scalar registers); the
 // page ids a workgroup needs are staged in LDS once.  BF16 tokens (sink,
 // recent window and, when the window is shorter than a page, tokens of the
 // unfinished page) are tiles of the same rounds: their rows are converted to
 // fp16 on their way into the x tile.  With several splits each workgroup
-// writes a partial (unnormalized output, max, sum); the last workgroup of a
-// (sequence, head block) merges them with log-sum-exp weights.
+// writes a partial (unnormalized output, max, sum) and a second kernel merges
+// them with log-sum-exp weights (the kernel boundary makes the partials of
+// every XCD visible without cache flushes inside the kernel).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -52,6 +55,7 @@ namespace mla {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -66,17 +70,19 @@ constexpr int kXRow = 1040;
 constexpr int kXTile = kTile * kXRow;
 // LDS map (bytes)
 constexpr int kOffX = 0;                              // [wave] x tiles
-constexpr int kPTile = 4 * 64 * 16;                   // [group][lane] fp16 x 8
+constexpr int kPTile = 4 * 64 * 8;                    // [group][lane] fp16 x 4
 constexpr int kOffP = kOffX + kWaves * kXTile;        // [wave] P' tiles
-constexpr int kOffMeta = kOffP + kWaves * kPTile;     // [wave][group][32 tokens] dwords
-constexpr int kOffRMeta = kOffMeta + kWaves * 512;    // [wave] k_R metadata of a page
+constexpr int kOffMeta = kOffP + kWaves * kPTile;     // [wave][group][16 tokens] dwords
+constexpr int kOffRMeta = kOffMeta + kWaves * 256;    // [wave] k_R metadata of a page
 constexpr int kOffMax = kOffRMeta + kWaves * 256;     // [head][wave] tile maxima
-constexpr int kPageWin = 2048;                        // page ids staged per workgroup
-constexpr int kOffPid = kOffMax + kHeadBlock * kWaves * 4;
+constexpr int kOffQr = kOffMax + kHeadBlock * kWaves * 4;  // [head] q_rope, bf16 x 64
+constexpr int kPageWin = 256;                              // page ids staged per workgroup
+constexpr int kOffPid = kOffQr + kHeadBlock * kRopeDim * 2;
 constexpr int kLdsBytes = kOffPid + kPageWin * 4;
-static_assert(kLdsBytes + 16 <= 160 * 1024, "LDS budget of a gfx950 CU");
+static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per gfx950 CU");
 constexpr int kStatW = 9;  // per head: sum p, sum P'_g (4), sum p m_g (4)
 static_assert(kWaves * kHeadBlock * kStatW * 4 <= kWaves * kPTile, "final sums reuse the P' area");
+static_assert(kTile * 128 <= kPTile, "a BF16 tile's k_R rows fit the P' area");
 constexpr float kPrescale = 1.0f / 256.0f;  // keeps q' and Q_g inside fp16 range
 constexpr float kNegInf = -INFINITY;
 
@@ -89,7 +95,6 @@ struct DecodeParams {
   const uint16_t* sink;
   const uint16_t* ring;
   const uint16_t* tail;
-  uint32_t* counters;
   float* parts;
   float* out;
   float* lse;
@@ -205,25 +210,33 @@ template <int BITS>
 struct QueryOps {
   half8 lat[4][4];  // [group][chunk], slot order of the unpack
   half8 meta;       // (scale, min) slots of the metadata MFMA, prescaled
-  uint32_t qr[8];   // bf16 pairs of q_rope channels 16*gq .. 16*gq+15
 };
 
+// q_rope channels 16 gq .. 16 gq + 15 of head h go to qr_lds (row h, 128 B).
 template <int BITS>
-__device__ inline void load_query(QueryOps<BITS>& q, const DecodeParams& p, int b, int h, int gq) {
+__device__ inline void load_query(QueryOps<BITS>& q, uint8_t* qr_lds, const DecodeParams& p, int b, int h, int n16,
+                                  int gq) {
   constexpr float kappa = BITS == 4 ? 16.f : 4.f;
-  const bool hv = h < p.heads;
-  const uint16_t* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + (hv ? h : 0)) * kLatentDim;
+  const int hc = h < p.heads ? h : p.heads - 1;  // rows past the last head compute a copy
+  const uint16_t* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + hc) * kLatentDim + 32 * gq;
+  const uint16_t* qr = p.q_rope + (static_cast<int64_t>(b) * p.heads + hc) * kRopeDim + 16 * gq;
+  u32x4 raw[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw[i][u] = ldg<u32x4>(ql + 128 * i + 8 * u);
+  }
+  const u32x4 r0 = ldg<u32x4>(qr), r1 = ldg<u32x4>(qr + 8);
   float qg[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float v[32];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const u32x4 w = hv ? ldg<u32x4>(ql + 128 * i + 32 * gq + 8 * u) : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        v[8 * u + 2 * e] = bf16f(w[e] & 0xFFFFu);
-        v[8 * u + 2 * e + 1] = bf16f(w[e] >> 16);
+        v[8 * u + 2 * e] = bf16f(raw[i][u][e] & 0xFFFFu);
+        v[8 * u + 2 * e + 1] = bf16f(raw[i][u][e] >> 16);
       }
     }
     float s = 0.f;
@@ -246,13 +259,8 @@ __device__ inline void load_query(QueryOps<BITS>& q, const DecodeParams& p, int 
     q.meta[2 * i] = gq == 0 ? ah : (gq == 1 ? al : z);
     q.meta[2 * i + 1] = gq == 0 ? ch : (gq == 1 ? cl : z);
   }
-  const uint16_t* qr = p.q_rope + (static_cast<int64_t>(b) * p.heads + (hv ? h : 0)) * kRopeDim + 16 * gq;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const u32x4 w = hv ? ldg<u32x4>(qr + 8 * u) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) q.qr[4 * u + e] = w[e];
-  }
+  lds_st<u32x4>(qr_lds + n16 * 128 + 32 * gq, r0);
+  lds_st<u32x4>(qr_lds + n16 * 128 + 32 * gq + 16, r1);
 }
 
 // Per-page positional-key operands for channels 16*gq + 8e + slot order:
@@ -262,7 +270,8 @@ struct RopeOps {
   float bias;
 };
 
-__device__ inline void rope_ops(RopeOps& r, const uint32_t (&qr)[8], const uint8_t* rmeta, int gq) {
+__device__ inline void rope_ops(RopeOps& r, const uint8_t* qr_row, const uint8_t* rmeta, int gq) {
+  const u32x4 q0 = lds_ld<u32x4>(qr_row + 32 * gq), q1 = lds_ld<u32x4>(qr_row + 32 * gq + 16);
   const u32x4 s0 = lds_ld<u32x4>(rmeta + 32 * gq);
   const u32x4 s1 = lds_ld<u32x4>(rmeta + 32 * gq + 16);
   const u32x4 m0 = lds_ld<u32x4>(rmeta + 128 + 32 * gq);
@@ -280,9 +289,11 @@ __device__ inline void rope_ops(RopeOps& r, const uint32_t (&qr)[8], const uint8
     mn[8 + 2 * e + 1] = hi_f16(m1[e]);
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    qv[2 * k] = bf16f(qr[k] & 0xFFFFu);
-    qv[2 * k + 1] = bf16f(qr[k] >> 16);
+  for (int k = 0; k < 4; ++k) {
+    qv[2 * k] = bf16f(q0[k] & 0xFFFFu);
+    qv[2 * k + 1] = bf16f(q0[k] >> 16);
+    qv[8 + 2 * k] = bf16f(q1[k] & 0xFFFFu);
+    qv[8 + 2 * k + 1] = bf16f(q1[k] >> 16);
   }
   float bias = 0.f;
 #pragma unroll
@@ -306,9 +317,9 @@ __device__ inline void rope_ops(RopeOps& r, const uint32_t (&qr)[8], const uint8
 
 template <int BITS>
 struct Stage {
-  uint32_t lat[2][BITS == 4 ? 16 : 8];  // [token block][dwords of the 4 groups]
-  u32x2 rope[2];
-  u32x4 ma[2];     // latent metadata of tokens n16 and 16 + n16
+  uint32_t lat[BITS == 4 ? 16 : 8];  // dwords of the 4 groups
+  u32x2 rope;
+  u32x4 ma;        // latent metadata of token n16
   uint32_t rmeta;  // 4 bytes of the page's k_R metadata (first tile of a page)
 };
 
@@ -317,125 +328,112 @@ struct LaneOffs {
   uint32_t lat, rope, meta;
 };
 
-// Loads one 32-token tile whose first slot is slot0 of `page` (a wave-uniform
+// Loads the 16-token tile whose first slot is slot0 of `page` (a wave-uniform
 // pointer); every address is page base (scalar) + 32-bit lane offset.
 template <int BITS>
 __device__ inline void load_stage(Stage<BITS>& sg, const uint8_t* page, int slot0, bool new_page,
                                   const LaneOffs& lo, int lane, const DecodeParams& p) {
   constexpr int kLatRow = kLatentDim * BITS / 8;
   const uint8_t* lat = page + slot0 * kLatRow;
-  const uint8_t* rope = page + p.rope_codes_off + slot0 * kRopeRowBytes;
-  const uint8_t* meta = page + p.latent_meta_off + slot0 * 16;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (BITS == 4) {
+      const u32x4 v = ldg<u32x4>(lat + lo.lat + 64 * i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (BITS == 4) {
-        const u32x4 v = ldg<u32x4>(lat + lo.lat + (16 * kb * kLatRow + 64 * i));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sg.lat[kb][4 * i + e] = v[e];
-      } else {
-        const u32x2 v = ldg<u32x2>(lat + lo.lat + (16 * kb * kLatRow + 32 * i));
-        sg.lat[kb][2 * i + 0] = v[0];
-        sg.lat[kb][2 * i + 1] = v[1];
-      }
+      for (int e = 0; e < 4; ++e) sg.lat[4 * i + e] = v[e];
+    } else {
+      const u32x2 v = ldg<u32x2>(lat + lo.lat + 32 * i);
+      sg.lat[2 * i + 0] = v[0];
+      sg.lat[2 * i + 1] = v[1];
     }
-    sg.rope[kb] = ldg<u32x2>(rope + lo.rope + 16 * kb * kRopeRowBytes);
-    sg.ma[kb] = ldg<u32x4>(meta + lo.meta + 16 * kb * 16);
   }
+  sg.rope = ldg<u32x2>(page + p.rope_codes_off + slot0 * kRopeRowBytes + lo.rope);
+  sg.ma = ldg<u32x4>(page + p.latent_meta_off + slot0 * 16 + lo.meta);
   if (new_page) sg.rmeta = ldg<uint32_t>(page + p.rope_meta_off + 4 * lane);
 }
 
 template <int BITS>
-__device__ inline half8 chunk_of(const Stage<BITS>& sg, int kb, int i, int d, const UnpackK& k) {
-  if constexpr (BITS == 4) return unpack4(sg.lat[kb][4 * i + d], k);
-  else return unpack2(sg.lat[kb][2 * i + (d >> 1)], d & 1, k);
+__device__ inline half8 chunk_of(const Stage<BITS>& sg, int i, int d, const UnpackK& k) {
+  if constexpr (BITS == 4) return unpack4(sg.lat[4 * i + d], k);
+  else return unpack2(sg.lat[2 * i + (d >> 1)], d & 1, k);
 }
 
-// Scores of one packed tile (tokens j0 .. j0+31 of one complete page, valid in
-// [vlo, vhi)), in the log2 domain; the x tile goes to LDS.
+// Scores of one packed tile (tokens j0 .. j0+15 of one complete page, valid in
+// [vlo, vhi)), in the log2 domain; lane (h, gq) gets tokens 4 gq + r of head h.
+// The x tile goes to LDS.
 template <int BITS>
-__device__ void packed_scores(float (&sc)[8], const QueryOps<BITS>& q, RopeOps& ro, const Stage<BITS>& sg,
+__device__ void packed_scores(float (&sc)[4], const QueryOps<BITS>& q, RopeOps& ro, const Stage<BITS>& sg,
                               bool new_page, int j0, int vlo, int vhi, uint8_t* xt, uint8_t* meta_lds,
-                              uint8_t* rmeta_lds, int lane, int n16, int gq, const DecodeParams& p) {
+                              uint8_t* rmeta_lds, const uint8_t* qr_row, int lane, int n16, int gq,
+                              const DecodeParams& p) {
   constexpr float kappa = BITS == 4 ? 16.f : 4.f;
   const UnpackK uk = unpack_k();
   if (gq == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) lds_st<uint32_t>(meta_lds + (g * kTile + 16 * kb + n16) * 4, sg.ma[kb][g]);
-    }
+    for (int g = 0; g < 4; ++g) lds_st<uint32_t>(meta_lds + (g * kTile + n16) * 4, sg.ma[g]);
   }
   if (new_page) {
     lds_st<uint32_t>(rmeta_lds + 4 * lane, sg.rmeta);
     lds_wait();
-    rope_ops(ro, q.qr, rmeta_lds, gq);
+    rope_ops(ro, qr_row, rmeta_lds, gq);
   }
-  f32x4 acc[2][5];
+  f32x4 acc[5];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int g = 0; g < 5; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint8_t* lrow = xt + n16 * kXRow + 64 * gq;
 #pragma unroll
-    for (int g = 0; g < 5; ++g) acc[kb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint8_t* lrow = xt + (16 * kb + n16) * kXRow + 64 * gq;
+  for (int d = 0; d < 4; ++d) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half8 x = chunk_of<BITS>(sg, kb, i, d, uk);
-        acc[kb][i] = mfma(x, q.lat[i][d], acc[kb][i]);
-        lds_st<half8>(lrow + 256 * i + 16 * d, x);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const half8 x = chunk_of<BITS>(sg, i, d, uk);
+      acc[i] = mfma(x, q.lat[i][d], acc[i]);
+      lds_st<half8>(lrow + 256 * i + 16 * d, x);
     }
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const half8 xr = unpack4(sg.rope[kb][e], uk);
-      acc[kb][4] = mfma(xr, ro.hi[e], acc[kb][4]);
-      acc[kb][4] = mfma(xr, ro.lo[e], acc[kb][4]);
-    }
-    acc[kb][4] = mfma(__builtin_bit_cast(half8, sg.ma[kb]), q.meta, acc[kb][4]);
   }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const half8 xr = unpack4(sg.rope[e], uk);
+    acc[4] = mfma(xr, ro.hi[e], acc[4]);
+    acc[4] = mfma(xr, ro.lo[e], acc[4]);
+  }
+  acc[4] = mfma(__builtin_bit_cast(half8, sg.ma), q.meta, acc[4]);
   lds_wait();
+  u32x4 mg[4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < 4; ++g) mg[g] = lds_ld<u32x4>(meta_lds + (g * kTile + 4 * gq) * 4);
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const u32x4 mg = lds_ld<u32x4>(meta_lds + (g * kTile + 16 * kb + 4 * gq) * 4);
+  for (int g = 0; g < 4; ++g) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = fmaf(lo_f16(mg[r]), acc[kb][g][r], v[r]);
-    }
+    for (int r = 0; r < 4; ++r) v[r] = fmaf(lo_f16(mg[g][r]), acc[g][r], v[r]);
+  }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = j0 + 16 * kb + 4 * gq + r;
-      const float z = fmaf(v[r], kappa, fmaf(acc[kb][4][r], 256.f, ro.bias));
-      sc[4 * kb + r] = (t >= vlo && t < vhi) ? z * p.c_log2 : kNegInf;
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int t = j0 + 4 * gq + r;
+    const float z = fmaf(v[r], kappa, fmaf(acc[4][r], 256.f, ro.bias));
+    sc[r] = (t >= vlo && t < vhi) ? z * p.c_log2 : kNegInf;
   }
 }
 
 // Weights of a packed tile: P'_g = fp16(fp16(p) s_g) per latent group into
 // LDS [group][lane]; adds this lane's sums of p, of the fp16 P'_g and of
 // p m_g to st.
-__device__ inline void packed_weights(const float (&pr)[8], const uint8_t* meta_lds, uint8_t* ptile,
+__device__ inline void packed_weights(const float (&pr)[4], const uint8_t* meta_lds, uint8_t* ptile,
                                       float (&st)[kStatW], int lane, int gq) {
-  half2 ph[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    st[0] += pr[2 * k] + pr[2 * k + 1];
-    ph[k] = half2{static_cast<_Float16>(pr[2 * k]), static_cast<_Float16>(pr[2 * k + 1])};
-  }
+  const half2 ph[2] = {half2{static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1])},
+                       half2{static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])}};
+  st[0] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   const half2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  u32x4 mg[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) mg[g] = lds_ld<u32x4>(meta_lds + (g * kTile + 4 * gq) * 4);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const u32x4 mg0 = lds_ld<u32x4>(meta_lds + (g * kTile + 4 * gq) * 4);
-    const u32x4 mg1 = lds_ld<u32x4>(meta_lds + (g * kTile + 16 + 4 * gq) * 4);
-    half8 pa;
+    half4 pa;
     float cs = st[1 + g], ms = st[5 + g];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const u32x4& mg = (k >> 1) ? mg1 : mg0;
-      const uint32_t w0 = mg[2 * (k & 1)], w1 = mg[2 * (k & 1) + 1];
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t w0 = mg[g][2 * k], w1 = mg[g][2 * k + 1];
       const half2 s2 = {__builtin_bit_cast(half2, w0)[0], __builtin_bit_cast(half2, w1)[0]};
       const half2 m2 = {__builtin_bit_cast(half2, w0)[1], __builtin_bit_cast(half2, w1)[1]};
       const half2 ps = ph[k] * s2;
@@ -444,7 +442,7 @@ __device__ inline void packed_weights(const float (&pr)[8], const uint8_t* meta_
       pa[2 * k] = ps[0];
       pa[2 * k + 1] = ps[1];
     }
-    lds_st<half8>(ptile + g * 1024 + 16 * lane, pa);
+    lds_st<half4>(ptile + g * 512 + 8 * lane, pa);
     st[1 + g] = cs;
     st[5 + g] = ms;
   }
@@ -513,17 +511,18 @@ __device__ inline DenseSrc dense_src(const DecodeParams& p, int b, const SeqRang
   return s;
 }
 
-// Scores of one BF16-path tile (dense indices k0 .. k0+31).  Rows are
+// Scores of one BF16-path tile (dense indices k0 .. k0+15).  Rows are
 // converted to fp16 in the unpack's slot order into the x tile (latent) and
 // copied raw into rbuf (k_R), then fed to the same MFMAs.  (Loads go through
 // registers: an LDS-direct load would make every later LDS read of the kernel
 // wait for all outstanding global loads, prefetches included.)
 template <int BITS>
-__device__ void dense_scores(float (&sc)[8], const QueryOps<BITS>& q, int b, const SeqRanges& sr, int k0,
-                             uint8_t* xt, uint8_t* rbuf, int lane, int n16, int gq, const DecodeParams& p) {
+__device__ void dense_scores(float (&sc)[4], const QueryOps<BITS>& q, const uint8_t* qr_row, int b,
+                             const SeqRanges& sr, int k0, uint8_t* xt, uint8_t* rbuf, int lane, int n16, int gq,
+                             const DecodeParams& p) {
   // k_R rows: token 8 u + lane / 8, bytes 16 (lane % 8) .. +15
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kTile / 8; ++u) {
     const DenseSrc s = dense_src(p, b, sr, k0 + 8 * u + (lane >> 3));
     const u32x4 w = s.kind ? ldg<u32x4>(s.rope + 8 * (lane & 7)) : u32x4{0, 0, 0, 0};
     lds_st<u32x4>(rbuf + u * 1024 + 16 * lane, w);
@@ -595,40 +594,37 @@ __device__ void dense_scores(float (&sc)[8], const QueryOps<BITS>& q, int b, con
   half8 qrp[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
+    const u32x4 w = lds_ld<u32x4>(qr_row + 32 * gq + 16 * e);
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
-      const int c = 8 * e + chan_off<4>(0, sl);
-      const uint32_t w = q.qr[c >> 1];
-      qrp[e][sl] = static_cast<_Float16>(bf16f((c & 1) ? (w >> 16) : (w & 0xFFFFu)));
+      const int c = chan_off<4>(0, sl);
+      qrp[e][sl] = static_cast<_Float16>(bf16f((c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu)));
     }
   }
   const int n_dense = sr.lo_p + (sr.L - sr.hi_p);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const uint8_t* lrow = xt + n16 * kXRow + 64 * gq;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* lrow = xt + (16 * kb + n16) * kXRow + 64 * gq;
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int d = 0; d < 4; ++d) acc = mfma(lds_ld<half8>(lrow + 256 * i + 16 * d), q.lat[i][d], acc);
+  }
+  const uint8_t* rrow = rbuf + n16 * 128 + 32 * gq;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) acc = mfma(lds_ld<half8>(lrow + 256 * i + 16 * d), q.lat[i][d], acc);
+  for (int e = 0; e < 2; ++e) {
+    const u32x4 w = lds_ld<u32x4>(rrow + 16 * e);
+    half8 xr;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const int c = chan_off<4>(0, sl);
+      xr[sl] = static_cast<_Float16>(bf16f((c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu)));
     }
-    const uint8_t* rrow = rbuf + (16 * kb + n16) * 128 + 32 * gq;
+    acc = mfma(xr, qrp[e], acc);
+  }
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const u32x4 w = lds_ld<u32x4>(rrow + 16 * e);
-      half8 xr;
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        const int c = chan_off<4>(0, sl);
-        xr[sl] = static_cast<_Float16>(bf16f((c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu)));
-      }
-      acc = mfma(xr, qrp[e], acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = k0 + 16 * kb + 4 * gq + r < n_dense;
-      sc[4 * kb + r] = ok ? acc[r] * p.c_log2 : kNegInf;
-    }
+  for (int r = 0; r < 4; ++r) {
+    const bool ok = k0 + 4 * gq + r < n_dense;
+    sc[r] = ok ? acc[r] * p.c_log2 : kNegInf;
   }
 }
 
@@ -641,9 +637,8 @@ __device__ inline int item_of_cost(int c, int D) {
 // ---------------------------------------------------------------------------
 
 template <int BITS>
-__global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_last;
   constexpr float kappa = BITS == 4 ? 16.f : 4.f;
   const int split = blockIdx.x % p.n_splits;
   const int grp = blockIdx.x / p.n_splits;  // b * n_hb + hb
@@ -653,13 +648,15 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
   const int n16 = lane & 15, gq = lane >> 4;
   uint8_t* const xt_own = smem + kOffX + wave * kXTile;
   uint8_t* const p_own = smem + kOffP + wave * kPTile;
-  uint8_t* const meta_own = smem + kOffMeta + wave * 512;
+  uint8_t* const meta_own = smem + kOffMeta + wave * 256;
   uint8_t* const rmeta_own = smem + kOffRMeta + wave * 256;
   float* const smax = reinterpret_cast<float*>(smem + kOffMax);
   int* const s_pid = reinterpret_cast<int*>(smem + kOffPid);
+  const uint8_t* const qr_row = smem + kOffQr + n16 * 128;
 
+  // every wave stores the same q_rope rows (identical values)
   QueryOps<BITS> q;
-  load_query<BITS>(q, p, b, hb * kHeadBlock + n16, gq);
+  load_query<BITS>(q, smem + kOffQr, p, b, hb * kHeadBlock + n16, n16, gq);
   const SeqRanges sr = seq_ranges(p, b);
 
   // this workgroup's items: BF16 tiles first (cost kDenseCost), then packed;
@@ -709,7 +706,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int k = 0; k < kStatW; ++k) st[k] = 0.f;
 
-  Stage<BITS> cur, nxt;
+  Stage<BITS> cur;
   RopeOps ro;
   int ro_page = -1;
   // Loads packed item `it` into sg; returns its page index, -1 for a BF16
@@ -727,30 +724,29 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
 
   for (int r = 0; r < rounds; ++r) {
     const int it = my0 + r;
-    const int nxt_pidx = stage_for(nxt, it + 1, cur_pidx >= 0 ? cur_pidx : ro_page);
 
     // 1. scores of this wave's tile
-    float sc[8];
+    float sc[4];
     bool has = it < my1;
     const bool dense = has && it < D;
     if (dense) {
-      dense_scores<BITS>(sc, q, b, sr, it * kTile, xt_own, p_own, lane, n16, gq, p);
+      dense_scores<BITS>(sc, q, qr_row, b, sr, it * kTile, xt_own, p_own, lane, n16, gq, p);
     } else if (has && cur_pidx >= 0) {
       const int j0 = (t_lo + (it - D)) * kTile;
       const bool new_page = cur_pidx != ro_page;
-      packed_scores<BITS>(sc, q, ro, cur, new_page, j0, sr.lo_p, sr.hi_p, xt_own, meta_own, rmeta_own, lane,
-                          n16, gq, p);
+      packed_scores<BITS>(sc, q, ro, cur, new_page, j0, sr.lo_p, sr.hi_p, xt_own, meta_own, rmeta_own, qr_row,
+                          lane, n16, gq, p);
       ro_page = cur_pidx;
     } else {
       has = false;
     }
+    // the codes of this wave's next tile, in flight while the round finishes
+    cur_pidx = stage_for(cur, it + 1, ro_page);
     if (!has) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sc[k] = kNegInf;
+      for (int k = 0; k < 4; ++k) sc[k] = kNegInf;
     }
-    float tmax = kNegInf;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) tmax = fmaxf(tmax, sc[k]);
+    float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     tmax = row_allmax(tmax);
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
@@ -765,24 +761,24 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
       for (int k = 0; k < kStatW; ++k) st[k] *= alpha;
     }
     if (has) {
-      float pr[8];
+      float pr[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) pr[k] = sc[k] == kNegInf ? 0.f : exp2f(sc[k] - m_run);
+      for (int k = 0; k < 4; ++k) pr[k] = sc[k] == kNegInf ? 0.f : exp2f(sc[k] - m_run);
       if (dense) {
-        half8 pa;
+        half4 pa;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 4; ++k) {
           st[0] += pr[k];
           pa[k] = static_cast<_Float16>(pr[k] * (1.f / kappa));
         }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) lds_st<half8>(p_own + g * 1024 + 16 * lane, pa);
+        for (int g = 0; g < 4; ++g) lds_st<half4>(p_own + g * 512 + 8 * lane, pa);
       } else {
         packed_weights(pr, meta_own, p_own, st, lane, gq);
       }
     } else {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) lds_st<u32x4>(p_own + g * 1024 + 16 * lane, u32x4{0, 0, 0, 0});
+      for (int g = 0; g < 4; ++g) lds_st<u32x2>(p_own + g * 512 + 8 * lane, u32x2{0, 0});
     }
     // output-layout copy of the running max: heads 4 gq + rr
     float ah[4];
@@ -795,7 +791,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
     }
     lds_barrier();
 
-    // 3. output of latent group `wave` for the four tiles of the round
+    // 3. output of latent group `wave` for the four tiles of the round, in
+    //    pairs: A slots 0-3 tile t (tokens 4 gq + j), slots 4-7 tile t + 1
     if (__any(ah[0] != 1.f || ah[1] != 1.f || ah[2] != 1.f || ah[3] != 1.f)) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -804,17 +801,18 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < kWaves; ++t) {
-      const half8 pa = lds_ld<half8>(smem + kOffP + t * kPTile + wave * 1024 + 16 * lane);
-      // B operand: slots 0-3 tokens 4 gq + j, slots 4-7 tokens 16 + 4 gq + j
-      const uint8_t* base =
-          smem + kOffX + t * kXTile + (4 * gq + (n16 >> 2)) * kXRow + 8 * (n16 & 3) + 256 * wave;
+    for (int t = 0; t < kWaves; t += 2) {
+      const half4 p0 = lds_ld<half4>(smem + kOffP + t * kPTile + wave * 512 + 8 * lane);
+      const half4 p1 = lds_ld<half4>(smem + kOffP + (t + 1) * kPTile + wave * 512 + 8 * lane);
+      const half8 pa = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const uint8_t* b0 = smem + kOffX + t * kXTile + (4 * gq + (n16 >> 2)) * kXRow + 8 * (n16 & 3) + 256 * wave;
+      const uint8_t* b1 = b0 + kXTile;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const uint8_t* a1 = base + 32 * kk;
-        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a1));
-        const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(a1 + 16 * kXRow));
+        const i16x4 r1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(b0 + 32 * kk));
+        const i16x4 r2 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(b1 + 32 * kk));
         // whole-vector shuffle + bit cast: assembling the operand element by
         // element from the transposed reads produced wrong code with this compiler
         const half8 vb = __builtin_bit_cast(half8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -822,8 +820,6 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
       }
     }
     lds_barrier();
-    cur = nxt;
-    cur_pidx = nxt_pidx;
   }
 
   // per-head sums of every wave, through the (now idle) P' area
@@ -875,48 +871,34 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
       }
     }
   }
-  if (direct) return;
+}
 
-  // the last workgroup of this (sequence, head block) merges the partials
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(p.counters + grp, 1u) == static_cast<uint32_t>(p.n_splits - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* parts = p.parts + static_cast<int64_t>(grp) * p.n_splits * kPartFloats;
-  // (max, sum) of every split and head into LDS, then per-split weights
-  float* const sml = reinterpret_cast<float*>(smem + kOffX);  // [split][max 16 | sum 16]
-  for (int k = threadIdx.x; k < p.n_splits * 2 * kHeadBlock; k += kThreads)
-    sml[k] = parts[(k / (2 * kHeadBlock)) * kPartFloats + kHeadBlock * kLatentDim + k % (2 * kHeadBlock)];
-  __syncthreads();
-  const int th = threadIdx.x >> 4;          // head of this thread
-  const int c0o = (threadIdx.x & 15) * 32;  // its 32 channels
+// Merge of the per-split partials of one (sequence, head): each split s holds
+// O_s = sum_j p_j c_j with p_j = 2^(z_j - m_s) and l_s = sum_j p_j; the result
+// is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+__global__ void __launch_bounds__(128) combine_kernel(const float* __restrict__ parts, float* __restrict__ out,
+                                                      float* __restrict__ lse, int heads, int n_hb, int n_splits) {
+  const int grp = blockIdx.x / kHeadBlock, hh = blockIdx.x % kHeadBlock;
+  const int b = grp / n_hb, hg = (grp % n_hb) * kHeadBlock + hh;
+  if (hg >= heads) return;
+  const float* base = parts + static_cast<int64_t>(grp) * n_splits * kPartFloats;
+  const int c = 4 * threadIdx.x;
   float M = kNegInf;
-  for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, sml[s * 2 * kHeadBlock + th]);
-  f32x4 acc[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, base[s * kPartFloats + kHeadBlock * kLatentDim + hh]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < p.n_splits; ++s) {
-    const float m_s = sml[s * 2 * kHeadBlock + th];
+#pragma unroll 8
+  for (int s = 0; s < n_splits; ++s) {
+    const float* ps = base + static_cast<int64_t>(s) * kPartFloats;
+    const float m_s = ps[kHeadBlock * kLatentDim + hh];
     const float f = m_s == kNegInf ? 0.f : exp2f(m_s - M);
-    L = fmaf(f, sml[s * 2 * kHeadBlock + kHeadBlock + th], L);
-    const float* ps = parts + static_cast<int64_t>(s) * kPartFloats + th * kLatentDim + c0o;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] += f * ldg<f32x4>(ps + 4 * u);
+    L = fmaf(f, ps[kHeadBlock * kLatentDim + kHeadBlock + hh], L);
+    acc += f * ldg<f32x4>(ps + hh * kLatentDim + c);
   }
-  const int hg = hb * kHeadBlock + th;
-  if (hg < p.heads) {
-    const float il = L > 0.f ? 1.f / L : 0.f;
-    float* o2 = p.out + (static_cast<int64_t>(b) * p.heads + hg) * kLatentDim + c0o;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4*>(o2 + 4 * u) = acc[u] * il;
-    if ((threadIdx.x & 15) == 0)
-      p.lse[static_cast<int64_t>(b) * p.heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
-  }
-  if (threadIdx.x == 0) p.counters[grp] = 0u;
+  const float il = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<f32x4*>(out + (static_cast<int64_t>(b) * heads + hg) * kLatentDim + c) = acc * il;
+  if (threadIdx.x == 0)
+    lse[static_cast<int64_t>(b) * heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
 }
 
 }  // namespace
@@ -938,16 +920,17 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   if (batch == 0) return MLA_LOWBIT_OK;
   if (static_cast<int64_t>(max_seqlen) > static_cast<int64_t>(max_pages) * g.page_size)
     return MLA_LOWBIT_ERR_ARG;
-  if (!q_lat || !q_rope || !seqlens || !out || !lse || !workspace || !rope_tail) return MLA_LOWBIT_ERR_ARG;
+  if (!q_lat || !q_rope || !seqlens || !out || !lse || !rope_tail) return MLA_LOWBIT_ERR_ARG;
   if (max_seqlen > 0 && (!page_pool || !block_table || num_pool_pages == 0)) return MLA_LOWBIT_ERR_ARG;
   if (g.sink > 0 && !sink_buf) return MLA_LOWBIT_ERR_ARG;
   if (g.local > 0 && !ring_buf) return MLA_LOWBIT_ERR_ARG;
   if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(out) || !aligned16(rope_tail) ||
       (page_pool && !aligned16(page_pool)) || (sink_buf && !aligned16(sink_buf)) ||
-      (ring_buf && !aligned16(ring_buf)) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      (ring_buf && !aligned16(ring_buf)) || (workspace && !aligned16(workspace)))
     return MLA_LOWBIT_ERR_ARG;
   const DecodePlan plan = plan_decode(g, batch, heads, max_seqlen);
-  if (workspace_bytes < plan.workspace_bytes) return MLA_LOWBIT_ERR_WORKSPACE;
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return MLA_LOWBIT_ERR_WORKSPACE;
   DecodeParams p{};
   p.q_lat = static_cast<const uint16_t*>(q_lat);
   p.q_rope = static_cast<const uint16_t*>(q_rope);
@@ -957,8 +940,7 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   p.sink = static_cast<const uint16_t*>(sink_buf);
   p.ring = static_cast<const uint16_t*>(ring_buf);
   p.tail = static_cast<const uint16_t*>(rope_tail);
-  p.counters = static_cast<uint32_t*>(workspace);
-  p.parts = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.counter_bytes);
+  p.parts = static_cast<float*>(workspace);
   p.out = out;
   p.lse = lse;
   p.batch = batch;
@@ -978,8 +960,9 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   p.rope_meta_off = g.rope_meta_off;
   p.page_bytes = g.page_bytes;
   p.c_log2 = softmax_scale * 1.44269504088896341f;
-  const int64_t blocks = static_cast<int64_t>(batch) * plan.n_hb * plan.n_splits;
-  if (blocks > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
+  const int64_t groups = static_cast<int64_t>(batch) * plan.n_hb;
+  const int64_t blocks = groups * plan.n_splits;
+  if (blocks > 0x7FFFFFFF || groups * kHeadBlock > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<4>),
@@ -995,5 +978,11 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   else
     hipLaunchKernelGGL(decode_kernel<2>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), kLdsBytes,
                        stream, p);
-  return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
+  if (plan.n_splits > 1) {
+    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(groups * kHeadBlock)), dim3(kLatentDim / 4), 0,
+                       stream, p.parts, out, lse, heads, plan.n_hb, plan.n_splits);
+    if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
+  }
+  return MLA_LOWBIT_OK;
 }

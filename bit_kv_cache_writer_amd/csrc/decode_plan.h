@@ -8,21 +8,18 @@
 
 namespace mla {
 
-constexpr int kTile = 32;         // tokens per MFMA tile
+constexpr int kTile = 16;         // tokens per wave and round (the MFMA M dimension)
 constexpr int kHeadBlock = 16;    // heads per MFMA block
 constexpr int kDecodeWaves = 4;   // waves per workgroup (one per SIMD)
 constexpr int kPartFloats = kHeadBlock * kLatentDim + 2 * kHeadBlock;  // O, m, l
-constexpr int kTargetGroups = 256;  // one workgroup per CU of an MI355X
+constexpr int kTargetGroups = 512;  // two workgroups per CU of an MI355X
 constexpr int kDenseCost = 2;       // a BF16 tile costs about two packed tiles
 
 struct DecodePlan {
   int n_hb;        // head blocks of 16
   int n_splits;    // workgroups per (sequence, head block)
-  size_t counter_bytes;
   size_t workspace_bytes;
 };
-
-inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline DecodePlan plan_decode(const Geometry& g, int batch, int heads, int max_seqlen) {
   (void)g;
@@ -38,10 +35,9 @@ inline DecodePlan plan_decode(const Geometry& g, int batch, int heads, int max_s
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   p.n_splits = static_cast<int>(s);
-  p.counter_bytes = round_up(static_cast<size_t>(groups) * sizeof(uint32_t), 256);
-  p.workspace_bytes = p.counter_bytes;
+  p.workspace_bytes = 0;
   if (p.n_splits > 1)
-    p.workspace_bytes += static_cast<size_t>(groups) * p.n_splits * kPartFloats * sizeof(float);
+    p.workspace_bytes = static_cast<size_t>(groups) * p.n_splits * kPartFloats * sizeof(float);
   return p;
 }
 

@@ -211,8 +211,7 @@ class DeviceCache:
         ws_bytes = self.workspace_bytes(H)
         if workspace is None:
             if getattr(self, "_ws", None) is None or self._ws.numel() < ws_bytes:
-                # zero-filled once: the decode leaves its arrival counters at zero
-                self._ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+                self._ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
             workspace = self._ws
         mla_lowbit_decode(self.layout, q_lat, q_rope, B, H, softmax_scale, self.pool,
                           self.num_pool_pages, self.block_table, self.max_pages, self.lengths,

@@ -152,10 +152,11 @@ int mla_lowbit_decode_workspace(const mla_lowbit_layout* layout, int32_t batch, 
  *   max_seqlen     host bound used for the work split; <= max_pages * P
  *   out            fp32 [batch][heads][512];  lse fp32 [batch][heads]
  *   workspace      device scratch of at least mla_lowbit_decode_workspace()
- *                  bytes, 256-B aligned.  Its first bytes hold arrival
- *                  counters: zero-fill the workspace once before its first
- *                  use; every call leaves the counters at zero again.  Calls
- *                  that share a workspace must not run concurrently.
+ *                  bytes, 16-B aligned, contents ignored (it holds the
+ *                  per-split partial results between the attention kernel
+ *                  and the merge kernel of one call; calls that share a
+ *                  workspace must not run concurrently).  May be NULL when
+ *                  the query returns 0 (one split per sequence).
  * Queries are converted to fp16 inside the kernel: |q| must be below 65504
  * (values under 2^-14 in magnitude keep an absolute accuracy of 2^-25).
  */

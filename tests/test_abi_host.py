@@ -55,9 +55,10 @@ def test_bad_layouts_rejected(bad):
 
 def test_workspace_query_and_errors():
     lay = mla.Layout(128, 4, 0.0, 4, 128)
+    part = (16 * 512 + 32) * 4  # one split's partial: 16 heads x 512 outputs + max + sum
     n = mla.mla_lowbit_decode_workspace(lay, 32, 16, 4096)
-    assert n > 0 and n % 4 == 0
-    assert n >= 256 and mla.mla_lowbit_decode_workspace(lay, 1, 16, 0) >= 256
+    assert n > 0 and n % (32 * part) == 0  # whole partials for each of the 32 sequences
+    assert mla.mla_lowbit_decode_workspace(lay, 1, 16, 0) == 0  # one split: no partials
     for args in [(0, 0, 4096), (32, 129, 4096), (32, 16, -1)]:
         with pytest.raises(mla.MlaError) as e:
             mla.mla_lowbit_decode_workspace(lay, *args)
@@ -108,8 +109,10 @@ def test_decode_rejects_bad_arguments_without_launch():
     assert _decode(lay, heads=0) == -2
     assert _decode(lay, heads=129) == -2
     assert _decode(lay, max_seqlen=4 * 64 + 1) == -2     # beyond the block table
-    assert _decode(lay, ws=512 + 16) == -2               # workspace not 256-B aligned
-    assert _decode(lay, ws_bytes=16) == -4
+    # 256 tokens of one sequence split in two: partials need a 16-B aligned workspace
+    assert _decode(lay, max_seqlen=256, ws=512 + 8) == -2
+    assert _decode(lay, max_seqlen=256, ws_bytes=16) == -4
+    assert _decode(lay, max_seqlen=256, ws=None) == -4
     assert _decode(lay, scale=float("inf")) == -2
     assert _decode(lay, out=258) == -2
     assert _decode(lay, batch=0) == 0
