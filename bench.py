@@ -6,7 +6,12 @@ positional key are quantized and packed; this token completes a cache page,
 so the page's k_R is quantized too) and the decode attends over the N cached
 tokens.  The step is repeated over `--layers` distinct caches so that the
 256 MB Infinity Cache cannot hold them (the packed bytes of all layers exceed
-1 GB), and the metric is microseconds per layer.
+1 GB).  The reported value is the decode's microseconds per layer (attention
+and split merge, timed with events on the launch stream); the writer's share
+and the whole step are reported beside it.
+
+`--calibrate-copy` instead times a plain 1 GiB device copy (the reference
+kernel for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes).
 
 Workload: C4R4 decode, 16 heads, latent 512 + rope 64, batch 32 x 4096 cached
 tokens, page 128, sink 4 + local 128 in BF16 (synthetic, seeded inputs).
@@ -28,6 +33,47 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SRC = os.path.join(ROOT, "bit_kv_cache_writer_amd", "csrc", "decode.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode call from the committed counter summary, or None
+    when there is none or the decode source changed since it was taken."""
+    import hashlib
+    path = os.path.join(PROFILES, f"decode_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    with open(DECODE_SRC, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("decode_source_sha256") != digest or "traffic_bytes_per_call" not in fields:
+        return None
+    return int(float(fields["traffic_bytes_per_call"]))
+
+
+def calibrate_copy() -> int:
+    """Plain device copy of known size (1 GiB read + 1 GiB written), 5 times."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                      "gbs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    return 0
 
 
 def algorithmic_decode_bytes(w, L: int) -> dict:
@@ -48,9 +94,10 @@ def algorithmic_decode_bytes(w, L: int) -> dict:
 
 
 def cpu_baseline(w, n_seq_sample: int, budget_s: float = 12.0) -> dict:
-    """The CPU oracle (single thread) doing the same step -- append one token,
-    decode over the cached tokens -- for a sample of sequences, scaled to the
-    whole batch (microseconds per layer)."""
+    """The CPU oracle (single thread) doing the same work for a sample of
+    sequences -- the decode over the N cached tokens (value, scaled to the
+    whole batch, microseconds per layer) and the one-token append before it
+    (reported beside it)."""
     import oracle
     from bit_kv_cache_writer_amd import workloads as wl
 
@@ -58,7 +105,7 @@ def cpu_baseline(w, n_seq_sample: int, budget_s: float = 12.0) -> dict:
     max_pages = w.pages_per_seq()
     pb = oracle.page_bytes(olay)
     ql, qr = wl.queries(w)
-    t_total, done = 0.0, 0
+    t_dec, t_app, done = 0.0, 0.0, 0
     for b in range(n_seq_sample):
         c, k = wl.seq_tokens(w, b)
         bt = np.arange(max_pages, dtype=np.int32).reshape(1, max_pages)
@@ -72,17 +119,20 @@ def cpu_baseline(w, n_seq_sample: int, budget_s: float = 12.0) -> dict:
         t0 = time.perf_counter()
         oracle.write(olay, np.ascontiguousarray(c[n - 1:]), np.ascontiguousarray(k[n - 1:]),
                      np.array([0, 1], np.int32), np.array([n - 1], np.int32), bt, pool, sink, ring, tail)
+        t1 = time.perf_counter()
         oracle.decode(olay, np.ascontiguousarray(ql[b:b + 1]), np.ascontiguousarray(qr[b:b + 1]),
                       w.softmax_scale, pool, bt, np.array([n], np.int32), sink, ring, tail)
-        t_total += time.perf_counter() - t0
+        t2 = time.perf_counter()
+        t_app += t1 - t0
+        t_dec += t2 - t1
         done += 1
-        if t_total > budget_s:
+        if t_app + t_dec > budget_s:
             break
-    us_layer = t_total / done * w.batch * 1e6
-    return {"value": us_layer, "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.batch} sequences (append 1 token + decode over {w.seqlen}), "
-                      f"single-threaded C oracle, scaled x{w.batch / done:.1f}",
-            "sample_seconds": round(t_total, 3)}
+    scale = w.batch / done
+    return {"value": t_dec * scale * 1e6, "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences: decode over {w.seqlen} cached tokens "
+                      f"(fp64 C oracle, one thread), scaled x{scale:.1f}",
+            "append_us_per_layer": t_app * scale * 1e6, "sample_seconds": round(t_app + t_dec, 3)}
 
 
 def main() -> int:
@@ -93,6 +143,7 @@ def main() -> int:
     ap.add_argument("--workload", default="c4r4_h16_b32")
     ap.add_argument("--layers", type=int, default=0, help="0: enough layers for >= 1 GB of packed cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true", help="time a plain 1 GiB copy and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -107,6 +158,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        return calibrate_copy()
     mla.lib()
     w = wl.WORKLOADS[args.workload]
     lay = mla.Layout(w.page_size, w.latent_bits, w.clip_q, w.sink, w.local)
@@ -201,7 +254,7 @@ def main() -> int:
 
     line = {
         "metric": "MLA low-bit decode us/layer and packed-cache HBM GB/s (% of roofline)",
-        "value": round(us_layer, 3),
+        "value": round(dec_us, 3),
         "unit": "us/layer",
         "n_gpus": 1,
         "steps": args.steps,
@@ -215,15 +268,17 @@ def main() -> int:
         "config": {"workload": w.name, "description": w.description, "batch": w.batch, "heads": w.heads,
                    "cached_tokens": n, "page": w.page_size, "paths": w.paths, "sink": w.sink,
                    "local": w.local, "layers_per_step": layers,
-                   "step": "per layer: append 1 token per sequence (completes a page) + decode over N"},
+                   "step": "per layer: append 1 token per sequence (completes a page) + decode over N",
+                   "value": "decode (attention + split merge) us per layer"},
         "decode_us": round(dec_us, 3),
         "write_us": round(us_layer - dec_us, 3),
+        "step_us_per_layer": round(us_layer, 3),
         "packed_cache_gbs": round(packed_gbs, 1),
         "writer_bulk_fill_gbs": round(fill_bytes / (np.median(fill_ms) * 1e-3) / 1e9, 1),
         "wall_s": round(wall, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel (one launch per mla_lowbit_decode)",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
+                     "kernel": "mla_lowbit_decode = decode_kernel + combine_kernel (one call per layer)",
                      "bytes_per_launch": dec_bytes},
         "cpu_baseline": cpu,
         "context_h20": {"raq_mla_us_per_layer": 12.6, "flashmla_us_per_layer": 17.4,

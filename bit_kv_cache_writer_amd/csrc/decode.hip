@@ -212,31 +212,51 @@ struct QueryOps {
   half8 meta;       // (scale, min) slots of the metadata MFMA, prescaled
 };
 
-// q_rope channels 16 gq .. 16 gq + 15 of head h go to qr_lds (row h, 128 B).
-template <int BITS>
-__device__ inline void load_query(QueryOps<BITS>& q, uint8_t* qr_lds, const DecodeParams& p, int b, int h, int n16,
-                                  int gq) {
-  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
-  const int hc = h < p.heads ? h : p.heads - 1;  // rows past the last head compute a copy
-  const uint16_t* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + hc) * kLatentDim + 32 * gq;
-  const uint16_t* qr = p.q_rope + (static_cast<int64_t>(b) * p.heads + hc) * kRopeDim + 16 * gq;
-  u32x4 raw[4][4];
+// Query rows of the 16 heads of a head block, staged in LDS as [head][1024 B]
+// (q_lat) plus [head][128 B] (q_rope): wave w fetches latent group w of every
+// head (lane: head lane / 4, 32 channels), wave 0 also the q_rope rows.
+// Heads past the last one read a copy of the last head.
+__device__ inline void stage_query(uint8_t* ql_lds, uint8_t* qr_lds, const DecodeParams& p, int b, int hb, int wave,
+                                   int lane) {
+  const int h = hb * kHeadBlock + (lane >> 2), part = lane & 3;
+  const int hc = h < p.heads ? h : p.heads - 1;
+  const uint16_t* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + hc) * kLatentDim + 128 * wave + 32 * part;
+  u32x4 v[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) raw[i][u] = ldg<u32x4>(ql + 128 * i + 8 * u);
+  for (int u = 0; u < 4; ++u) v[u] = ldg<u32x4>(ql + 8 * u);
+  u32x4 r[2];
+  if (wave == 0) {
+    const uint16_t* qr = p.q_rope + (static_cast<int64_t>(b) * p.heads + hc) * kRopeDim + 16 * part;
+    r[0] = ldg<u32x4>(qr);
+    r[1] = ldg<u32x4>(qr + 8);
   }
-  const u32x4 r0 = ldg<u32x4>(qr), r1 = ldg<u32x4>(qr + 8);
+  uint8_t* row = ql_lds + (lane >> 2) * 1024 + 2 * (128 * wave + 32 * part);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) lds_st<u32x4>(row + 16 * u, v[u]);
+  if (wave == 0) {
+    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * part, r[0]);
+    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * part + 16, r[1]);
+  }
+}
+
+// MFMA operands of the query from the staged rows: lane (h, gq) takes channels
+// 128 i + 32 gq .. + 31 of head h, in the unpack's slot order; Q_g = sum of
+// the query over group g enters the metadata operand.
+template <int BITS>
+__device__ inline void load_query(QueryOps<BITS>& q, const uint8_t* ql_lds, int n16, int gq) {
+  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
   float qg[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const uint8_t* row = ql_lds + n16 * 1024 + 2 * (128 * i + 32 * gq);
     float v[32];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      const u32x4 w = lds_ld<u32x4>(row + 16 * u);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        v[8 * u + 2 * e] = bf16f(raw[i][u][e] & 0xFFFFu);
-        v[8 * u + 2 * e + 1] = bf16f(raw[i][u][e] >> 16);
+        v[8 * u + 2 * e] = bf16f(w[e] & 0xFFFFu);
+        v[8 * u + 2 * e + 1] = bf16f(w[e] >> 16);
       }
     }
     float s = 0.f;
@@ -259,8 +279,6 @@ __device__ inline void load_query(QueryOps<BITS>& q, uint8_t* qr_lds, const Deco
     q.meta[2 * i] = gq == 0 ? ah : (gq == 1 ? al : z);
     q.meta[2 * i + 1] = gq == 0 ? ch : (gq == 1 ? cl : z);
   }
-  lds_st<u32x4>(qr_lds + n16 * 128 + 32 * gq, r0);
-  lds_st<u32x4>(qr_lds + n16 * 128 + 32 * gq + 16, r1);
 }
 
 // Per-page positional-key operands for channels 16*gq + 8e + slot order:
@@ -358,15 +376,13 @@ __device__ inline half8 chunk_of(const Stage<BITS>& sg, int i, int d, const Unpa
   else return unpack2(sg.lat[2 * i + (d >> 1)], d & 1, k);
 }
 
-// Scores of one packed tile (tokens j0 .. j0+15 of one complete page, valid in
-// [vlo, vhi)), in the log2 domain; lane (h, gq) gets tokens 4 gq + r of head h.
-// The x tile goes to LDS.
+// Score MFMAs of one packed tile: acc[g] = q_g . x_g per latent group,
+// acc[4] = rope and metadata terms / 256.  The x tile goes to LDS.  After
+// this the stage registers are free for the next tile.
 template <int BITS>
-__device__ void packed_scores(float (&sc)[4], const QueryOps<BITS>& q, RopeOps& ro, const Stage<BITS>& sg,
-                              bool new_page, int j0, int vlo, int vhi, uint8_t* xt, uint8_t* meta_lds,
-                              uint8_t* rmeta_lds, const uint8_t* qr_row, int lane, int n16, int gq,
-                              const DecodeParams& p) {
-  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
+__device__ void packed_mfma(f32x4 (&acc)[5], const QueryOps<BITS>& q, RopeOps& ro, const Stage<BITS>& sg,
+                            bool new_page, uint8_t* xt, uint8_t* meta_lds, uint8_t* rmeta_lds, const uint8_t* qr_row,
+                            int lane, int n16, int gq) {
   const UnpackK uk = unpack_k();
   if (gq == 0) {
 #pragma unroll
@@ -377,7 +393,6 @@ __device__ void packed_scores(float (&sc)[4], const QueryOps<BITS>& q, RopeOps& 
     lds_wait();
     rope_ops(ro, qr_row, rmeta_lds, gq);
   }
-  f32x4 acc[5];
 #pragma unroll
   for (int g = 0; g < 5; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint8_t* lrow = xt + n16 * kXRow + 64 * gq;
@@ -397,6 +412,14 @@ __device__ void packed_scores(float (&sc)[4], const QueryOps<BITS>& q, RopeOps& 
     acc[4] = mfma(xr, ro.lo[e], acc[4]);
   }
   acc[4] = mfma(__builtin_bit_cast(half8, sg.ma), q.meta, acc[4]);
+}
+
+// Scores (log2 domain) of the tile tokens j0 .. j0+15, valid in [vlo, vhi):
+// lane (h, gq) gets tokens 4 gq + r of head h.
+template <int BITS>
+__device__ inline void packed_fold(float (&sc)[4], const f32x4 (&acc)[5], float bias, int j0, int vlo, int vhi,
+                                   const uint8_t* meta_lds, int gq, float c_log2) {
+  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
   lds_wait();
   u32x4 mg[4];
 #pragma unroll
@@ -410,8 +433,8 @@ __device__ void packed_scores(float (&sc)[4], const QueryOps<BITS>& q, RopeOps& 
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = j0 + 4 * gq + r;
-    const float z = fmaf(v[r], kappa, fmaf(acc[4][r], 256.f, ro.bias));
-    sc[r] = (t >= vlo && t < vhi) ? z * p.c_log2 : kNegInf;
+    const float z = fmaf(v[r], kappa, fmaf(acc[4][r], 256.f, bias));
+    sc[r] = (t >= vlo && t < vhi) ? z * c_log2 : kNegInf;
   }
 }
 
@@ -653,10 +676,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   float* const smax = reinterpret_cast<float*>(smem + kOffMax);
   int* const s_pid = reinterpret_cast<int*>(smem + kOffPid);
   const uint8_t* const qr_row = smem + kOffQr + n16 * 128;
+  uint8_t* const ql_stage = smem + kOffX;  // query rows, until round 0 writes x tiles
 
-  // every wave stores the same q_rope rows (identical values)
-  QueryOps<BITS> q;
-  load_query<BITS>(q, smem + kOffQr, p, b, hb * kHeadBlock + n16, n16, gq);
+  stage_query(ql_stage, smem + kOffQr, p, b, hb, wave, lane);
   const SeqRanges sr = seq_ranges(p, b);
 
   // this workgroup's items: BF16 tiles first (cost kDenseCost), then packed;
@@ -681,13 +703,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   }
   const int32_t* bt_row = p.block_table + static_cast<int64_t>(b) * p.max_pages;
   for (int k = threadIdx.x; k < min(n_pg, kPageWin); k += kThreads) s_pid[k] = bt_row[pg_first + k];
-  if (my0 >= my1) {  // a wave without tiles still feeds zeros to the output MFMAs
-    for (int o = 16 * lane; o < kXTile; o += 64 * 16) lds_st<u32x4>(xt_own + o, u32x4{0, 0, 0, 0});
-  }
-  __syncthreads();
+  bool pid_staged = false;  // the first tile reads the block table directly
   auto page_ptr_of = [&](int pidx) -> const uint8_t* {
     const int k = pidx - pg_first;
-    const int id = uniform(k < kPageWin ? *reinterpret_cast<volatile int*>(s_pid + k) : bt_row[pidx]);
+    const int id = uniform(pid_staged && k < kPageWin ? *reinterpret_cast<volatile int*>(s_pid + k) : bt_row[pidx]);
     return page_of_id(p, id);
   };
 
@@ -721,6 +740,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
     return pidx;
   };
   int cur_pidx = stage_for(cur, my0, ro_page);
+  pid_staged = true;
+  __syncthreads();  // query rows and page ids staged
+  QueryOps<BITS> q;
+  load_query<BITS>(q, ql_stage, n16, gq);
+  __syncthreads();  // query rows read: the x tiles may be written
+  if (my0 >= my1) {  // a wave without tiles still feeds zeros to the output MFMAs
+    for (int o = 16 * lane; o < kXTile; o += 64 * 16) lds_st<u32x4>(xt_own + o, u32x4{0, 0, 0, 0});
+  }
 
   for (int r = 0; r < rounds; ++r) {
     const int it = my0 + r;
@@ -734,14 +761,18 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
     } else if (has && cur_pidx >= 0) {
       const int j0 = (t_lo + (it - D)) * kTile;
       const bool new_page = cur_pidx != ro_page;
-      packed_scores<BITS>(sc, q, ro, cur, new_page, j0, sr.lo_p, sr.hi_p, xt_own, meta_own, rmeta_own, qr_row,
-                          lane, n16, gq, p);
+      f32x4 acc[5];
+#pragma unroll
+      for (int g = 0; g < 5; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      packed_mfma<BITS>(acc, q, ro, cur, new_page, xt_own, meta_own, rmeta_own, qr_row, lane, n16, gq);
       ro_page = cur_pidx;
+      // the codes of this wave's next tile, in flight while the round finishes
+      cur_pidx = stage_for(cur, it + 1, ro_page);
+      packed_fold<BITS>(sc, acc, ro.bias, j0, sr.lo_p, sr.hi_p, meta_own, gq, p.c_log2);
     } else {
       has = false;
     }
-    // the codes of this wave's next tile, in flight while the round finishes
-    cur_pidx = stage_for(cur, it + 1, ro_page);
+    if (!has || dense) cur_pidx = stage_for(cur, it + 1, ro_page);
     if (!has) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) sc[k] = kNegInf;
@@ -831,11 +862,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   }
   __syncthreads();
   const bool direct = p.n_splits == 1;
+  // partial layout (per split): O as [group][kk][lane] f32x4 over heads
+  // 4 gq + r (the MFMA accumulator layout, so every store is 16 B), then the
+  // running max and the sum of the 16 heads
   float* part = p.parts + (static_cast<int64_t>(grp) * p.n_splits + split) * kPartFloats;
-  float l_h[4];
+  float l_h[4], c_h[4], m_h[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const int hh = 4 * gq + rr, hg = hb * kHeadBlock + hh;
+    const int hh = 4 * gq + rr;
     float l = 0.f, c = 0.f, m = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -845,16 +879,24 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
       m += f[5 + wave];
     }
     l_h[rr] = l;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    c_h[rr] = c;
+    m_h[rr] = m;
+  }
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const float v = fmaf(kappa, o[kk][rr] - c, m);
+  for (int kk = 0; kk < 8; ++kk) {
+    f32x4 v;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(kappa, o[kk][rr] - c_h[rr], m_h[rr]);
+    if (direct) {
       const int ch = col_to_channel<BITS>(128 * wave + 16 * kk + n16);
-      if (direct) {
-        if (hg < p.heads) p.out[(static_cast<int64_t>(b) * p.heads + hg) * kLatentDim + ch] = v * inv;
-      } else {
-        part[hh * kLatentDim + ch] = v;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int hg = hb * kHeadBlock + 4 * gq + rr;
+        if (hg < p.heads)
+          p.out[(static_cast<int64_t>(b) * p.heads + hg) * kLatentDim + ch] = l_h[rr] > 0.f ? v[rr] / l_h[rr] : 0.f;
       }
+    } else {
+      reinterpret_cast<f32x4*>(part)[(wave * 8 + kk) * 64 + lane] = v;
     }
   }
   if (wave == 0 && n16 == 0) {
@@ -873,32 +915,69 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   }
 }
 
-// Merge of the per-split partials of one (sequence, head): each split s holds
-// O_s = sum_j p_j c_j with p_j = 2^(z_j - m_s) and l_s = sum_j p_j; the result
-// is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
-__global__ void __launch_bounds__(128) combine_kernel(const float* __restrict__ parts, float* __restrict__ out,
-                                                      float* __restrict__ lse, int heads, int n_hb, int n_splits) {
-  const int grp = blockIdx.x / kHeadBlock, hh = blockIdx.x % kHeadBlock;
-  const int b = grp / n_hb, hg = (grp % n_hb) * kHeadBlock + hh;
-  if (hg >= heads) return;
+// Merge of the per-split partials of one sequence and head block.  Split s
+// holds O_s = sum_j p_j c_j with p_j = 2^(z_j - m_s) and l_s = sum_j p_j; the
+// result is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+// One workgroup of 64 threads per (sequence, head block, latent group g,
+// 16-column block kk); thread = MFMA lane (n16, gq): column 128 g + 16 kk +
+// n16 of heads 4 gq + r.
+template <int BITS>
+__global__ void __launch_bounds__(64) combine_kernel(const float* __restrict__ parts, float* __restrict__ out,
+                                                     float* __restrict__ lse, int heads, int n_hb, int n_splits) {
+  __shared__ float s_ml[kMaxSplits][2 * kHeadBlock];  // per split: max of the 16 heads, then sums
+  __shared__ float s_M[kHeadBlock], s_L[kHeadBlock];
+  const int grp = blockIdx.x >> 5, gk = blockIdx.x & 31;  // gk = 8 g + kk
+  const int b = grp / n_hb, hb = grp % n_hb;
+  const int t = threadIdx.x, n16 = t & 15, gq = t >> 4;
   const float* base = parts + static_cast<int64_t>(grp) * n_splits * kPartFloats;
-  const int c = 4 * threadIdx.x;
-  float M = kNegInf;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, base[s * kPartFloats + kHeadBlock * kLatentDim + hh]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < n_splits; ++s) {
-    const float* ps = base + static_cast<int64_t>(s) * kPartFloats;
-    const float m_s = ps[kHeadBlock * kLatentDim + hh];
-    const float f = m_s == kNegInf ? 0.f : exp2f(m_s - M);
-    L = fmaf(f, ps[kHeadBlock * kLatentDim + kHeadBlock + hh], L);
-    acc += f * ldg<f32x4>(ps + hh * kLatentDim + c);
+  // this thread's partials of the first splits go out before the (max, sum)
+  // staging, so both latencies overlap
+  constexpr int kEarly = 16;
+  f32x4 v[kEarly];
+#pragma unroll
+  for (int s = 0; s < kEarly; ++s)
+    v[s] = s < n_splits ? ldg<f32x4>(base + static_cast<int64_t>(s) * kPartFloats + 4 * (gk * 64 + t))
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = t; k < n_splits * 2 * kHeadBlock; k += 64)
+    s_ml[k >> 5][k & 31] = base[(k >> 5) * kPartFloats + kHeadBlock * kLatentDim + (k & 31)];
+  __syncthreads();
+  if (t < kHeadBlock) {
+    float M = kNegInf;
+    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, s_ml[s][t]);
+    float L = 0.f;
+    for (int s = 0; s < n_splits; ++s) L = fmaf(s_ml[s][t] == kNegInf ? 0.f : exp2f(s_ml[s][t] - M), s_ml[s][16 + t], L);
+    s_M[t] = M;
+    s_L[t] = L;
   }
-  const float il = L > 0.f ? 1.f / L : 0.f;
-  *reinterpret_cast<f32x4*>(out + (static_cast<int64_t>(b) * heads + hg) * kLatentDim + c) = acc * il;
-  if (threadIdx.x == 0)
-    lse[static_cast<int64_t>(b) * heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+  __syncthreads();
+  float Mh[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) Mh[rr] = s_M[4 * gq + rr];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto add = [&](int s, const f32x4& x) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float m_s = s_ml[s][4 * gq + rr];
+      const float f = m_s == kNegInf ? 0.f : exp2f(m_s - Mh[rr]);
+      acc[rr] = fmaf(f, x[rr], acc[rr]);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < kEarly; ++s)
+    if (s < n_splits) add(s, v[s]);
+#pragma unroll 8
+  for (int s = kEarly; s < n_splits; ++s)
+    add(s, ldg<f32x4>(base + static_cast<int64_t>(s) * kPartFloats + 4 * (gk * 64 + t)));
+  const int ch = col_to_channel<BITS>(16 * gk + n16);
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int hg = hb * kHeadBlock + 4 * gq + rr;
+    const float L = s_L[4 * gq + rr];
+    if (hg < heads) out[(static_cast<int64_t>(b) * heads + hg) * kLatentDim + ch] = L > 0.f ? acc[rr] / L : 0.f;
+  }
+  if (gk == 0 && t < kHeadBlock && hb * kHeadBlock + t < heads)
+    lse[static_cast<int64_t>(b) * heads + hb * kHeadBlock + t] =
+        s_L[t] > 0.f ? (s_M[t] + log2f(s_L[t])) * 0.69314718055994531f : kNegInf;
 }
 
 }  // namespace
@@ -962,7 +1041,7 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   p.c_log2 = softmax_scale * 1.44269504088896341f;
   const int64_t groups = static_cast<int64_t>(batch) * plan.n_hb;
   const int64_t blocks = groups * plan.n_splits;
-  if (blocks > 0x7FFFFFFF || groups * kHeadBlock > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
+  if (blocks > 0x7FFFFFFF || groups * 32 > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<4>),
@@ -980,8 +1059,13 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
                        stream, p);
   if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
   if (plan.n_splits > 1) {
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(groups * kHeadBlock)), dim3(kLatentDim / 4), 0,
-                       stream, p.parts, out, lse, heads, plan.n_hb, plan.n_splits);
+    const dim3 grid(static_cast<uint32_t>(groups * 32));
+    if (g.latent_bits == 4)
+      hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(64), 0, stream, p.parts, out, lse, heads, plan.n_hb,
+                         plan.n_splits);
+    else
+      hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(64), 0, stream, p.parts, out, lse, heads, plan.n_hb,
+                         plan.n_splits);
     if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
   }
   return MLA_LOWBIT_OK;

@@ -14,6 +14,7 @@ constexpr int kDecodeWaves = 4;   // waves per workgroup (one per SIMD)
 constexpr int kPartFloats = kHeadBlock * kLatentDim + 2 * kHeadBlock;  // O, m, l
 constexpr int kTargetGroups = 512;  // two workgroups per CU of an MI355X
 constexpr int kDenseCost = 2;       // a BF16 tile costs about two packed tiles
+constexpr int kMaxSplits = 128;     // splits per (sequence, head block): the merge stages their (max, sum)
 
 struct DecodePlan {
   int n_hb;        // head blocks of 16
@@ -33,6 +34,7 @@ inline DecodePlan plan_decode(const Geometry& g, int batch, int heads, int max_s
   long cap = tiles / (2L * kDecodeWaves);  // >= 2 tiles per wave
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   p.n_splits = static_cast<int>(s);
   p.workspace_bytes = 0;
