@@ -7,42 +7,44 @@
 // codes dequantized inside the loop -- the same reconstructed content tile
 // feeds both the score (matching) and the output (aggregation).
 //
-// How.  One workgroup of 4 waves (one per SIMD) per (sequence, 16-head block,
-// split of the sequence); two workgroups share a CU, so one fills the other's
-// barrier and memory waits.  Each wave owns a contiguous run of 16-token
-// tiles (consecutive tiles of a wave share a page); the waves advance in
-// lockstep rounds, one tile each:
-//  1. Scores.  The wave's codes arrive straight in the lanes that feed
+// How.  Each (sequence, 16-head block) is cut into workgroups of 4 waves (one
+// per SIMD, two workgroups per CU): a few BF16-path workgroups take the
+// protected tokens, the rest split the packed pages.  Each writes a partial
+// (unnormalized output, max, sum); a second kernel merges them with
+// log-sum-exp weights (the kernel boundary makes every XCD's partials
+// visible without cache flushes inside the kernel).
+//
+// Packed workgroup.  Each wave owns a contiguous run of 16-token tiles
+// (consecutive tiles share a page) and keeps a ring of three tile slots in LDS
+// filled by direct global->LDS loads two tiles ahead; the slots hold the codes
+// as stored (XOR-swizzled 16-byte units, so row reads and transposed reads are
+// bank-conflict free).  The waves advance in lockstep rounds, one tile each:
+//  1. Scores: codes come out of LDS in the lanes that feed
 //     v_mfma_f32_16x16x32_f16 (M = 16 tokens, N = 16 heads, K = 32 channels;
-//     lane (t, g) holds 8 channels of token t); the next tile's codes are
-//     requested as soon as these are unpacked.  Codes are unpacked in
-//     registers to fp16 x = 1 + code/kappa by OR-ing the code into the top of
-//     an fp16 mantissa (kappa = 16 for 4-bit codes, 4 for 2-bit codes); the x
-//     tile also goes to LDS.  Group scale s and minimum m are folded after the
-//     MFMA:
+//     lane (t, g) holds 8 channels of token t) and are unpacked in registers
+//     to fp16 x = 1 + code/kappa by OR-ing the code into the top of an fp16
+//     mantissa (kappa = 16 for 4-bit codes, 4 for 2-bit codes).  Group scale s
+//     and minimum m are folded after the MFMA:
 //       q.c = sum_g kappa s_g (q_g . x_g) + sum_g (m_g - kappa s_g) Q_g,
 //     Q_g = sum of the query over group g; the second sum is one more MFMA on
-//     the raw fp16 (scale, min) metadata.  The positional key's per-(channel,
+//     the raw fp16 (scale, min) words.  The positional key's per-(channel,
 //     page) scale/min is folded into a per-page query q' = q s (fp16 hi + lo)
 //     and bias sum_c q_c (m_c - 16 s_c), rebuilt only when the page changes.
-//  2. Softmax.  The four tile maxima meet in LDS; every wave raises the same
-//     running max and turns its scores into fp16 weights P'_g = p s_g per
-//     latent group.  Sums of p, of P'_g and of p m_g stay per lane until the
-//     end.
-//  3. Output.  Wave w owns latent group w (128 output channels) for the four
-//     tiles of the round, taken in pairs (K = 32 tokens): A = P'_w, B = the x
-//     tiles read back with ds_read_b64_tr_b16 (one channel of 4 tokens per
-//     lane).  The output accumulates sum_j fp16(p_j s_j) x_j; the offsets
-//     -kappa sum_j fp16(p_j s_j) and sum_j p_j m_j are applied at the end --
-//     the same rounded fp16 products enter both, so they cancel.
-// Tile, page and address arithmetic is wave-uniform (scalar registers); the
-// page ids a workgroup needs are staged in LDS once.  BF16 tokens (sink,
+//  2. Softmax: the four tile maxima meet in LDS; every wave raises the same
+//     running max and publishes fp16 weights P'_g = p s_g per latent group.
+//     Sums of p, of P'_g and of p m_g stay per lane until the end.
+//  3. Output: wave w owns latent group w (128 output channels).  Its B operand
+//     comes straight from the four code tiles of the round with
+//     ds_read_b64_tr_b4 (16 tokens of one 4-bit channel, or of a 2-bit channel
+//     pair, per lane) and the same mantissa unpack; A = P'_w.  The output
+//     accumulates sum_j fp16(p_j s_j) x_j; the offsets -kappa sum_j
+//     fp16(p_j s_j) and sum_j p_j m_j are applied at the end -- the same
+//     rounded fp16 products enter both, so they cancel.
+// BF16-path workgroup: the same rounds over the protected tokens (sink,
 // recent window and, when the window is shorter than a page, tokens of the
-// unfinished page) are tiles of the same rounds: their rows are converted to
-// fp16 on their way into the x tile.  With several splits each workgroup
-// writes a partial (unnormalized output, max, sum) and a second kernel merges
-// them with log-sum-exp weights (the kernel boundary makes the partials of
-// every XCD visible without cache flushes inside the kernel).
+// unfinished page); their rows are converted to fp16 on their way into an fp16
+// x tile that both the score MFMAs and the transposed output reads use.
+// Tile, page and address arithmetic is wave-uniform (scalar registers).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -61,30 +63,46 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = kDecodeWaves;
 constexpr int kThreads = 64 * kWaves;
-// x-tile row: 512 fp16 + 16 B pad (260 dwords: rows land 4 banks apart, so
-// both the row-wise writes and the transposed reads are conflict-free)
-constexpr int kXRow = 1040;
-constexpr int kXTile = kTile * kXRow;
-// LDS map (bytes)
-constexpr int kOffX = 0;                              // [wave] x tiles
-constexpr int kPTile = 4 * 64 * 8;                    // [group][lane] fp16 x 4
-constexpr int kOffP = kOffX + kWaves * kXTile;        // [wave] P' tiles
-constexpr int kOffMeta = kOffP + kWaves * kPTile;     // [wave][group][16 tokens] dwords
-constexpr int kOffRMeta = kOffMeta + kWaves * 256;    // [wave] k_R metadata of a page
-constexpr int kOffMax = kOffRMeta + kWaves * 256;     // [head][wave] tile maxima
-constexpr int kOffQr = kOffMax + kHeadBlock * kWaves * 4;  // [head] q_rope, bf16 x 64
-constexpr int kPageWin = 256;                              // page ids staged per workgroup
-constexpr int kOffPid = kOffQr + kHeadBlock * kRopeDim * 2;
-constexpr int kLdsBytes = kOffPid + kPageWin * 4;
-static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per gfx950 CU");
-constexpr int kStatW = 9;  // per head: sum p, sum P'_g (4), sum p m_g (4)
-static_assert(kWaves * kHeadBlock * kStatW * 4 <= kWaves * kPTile, "final sums reuse the P' area");
-static_assert(kTile * 128 <= kPTile, "a BF16 tile's k_R rows fit the P' area");
+constexpr int kStatW = 9;      // per head: sum p, sum P'_g (4), sum p m_g (4)
 constexpr float kPrescale = 1.0f / 256.0f;  // keeps q' and Q_g inside fp16 range
 constexpr float kNegInf = -INFINITY;
+
+// BF16-path workgroup LDS map (bytes).  x-tile row: 512 fp16 + 16 B pad (260
+// dwords: rows land 4 banks apart, so row writes and transposed reads are
+// conflict-free).
+constexpr int kXRow = 1040;
+constexpr int kXTile = kTile * kXRow;
+constexpr int kOffX = 0;                                   // [wave] x tiles
+constexpr int kPTile = 4 * 64 * 8;                         // [group][lane] fp16 x 4
+constexpr int kOffP = kOffX + kWaves * kXTile;             // [wave] P' tiles
+constexpr int kOffMax = kOffP + kWaves * kPTile;           // [head][wave] tile maxima
+constexpr int kOffQr = kOffMax + kHeadBlock * kWaves * 4;  // [head] q_rope, bf16 x 64
+constexpr int kDenseLds = kOffQr + kHeadBlock * kRopeDim * 2;
+static_assert(kTile * 128 <= kPTile, "a BF16 tile's k_R rows fit the P' area");
+
+// Packed workgroup LDS map.  A tile slot: latent codes (16 rows, 16-byte
+// units XOR-swizzled by row), k_R codes [16][32 B], latent metadata
+// [16][16 B], the page's k_R metadata (256 B); +64 B so that the slots of
+// consecutive waves start on different banks.
+constexpr int kSlots = 3;
+constexpr int kSlotBytes = 4096 + 512 + 256 + 256 + 64;
+constexpr int kPkOffStage = 0;                                  // [slot][wave]
+constexpr int kPkOffP = kPkOffStage + kSlots * kWaves * kSlotBytes;  // [kb][g][gq][head] x 16 B
+constexpr int kPkPBytes = 2 * 4 * 4 * kHeadBlock * 16;
+constexpr int kPkOffMax = kPkOffP + kPkPBytes;
+constexpr int kPkOffQr = kPkOffMax + kHeadBlock * kWaves * 4;
+constexpr int kPkOffPid = kPkOffQr + kHeadBlock * kRopeDim * 2;
+constexpr int kPackedLds = kPkOffPid + kPageWin * 4;
+static_assert(kWaves * kSlotBytes >= kHeadBlock * kLatentDim * 2, "query rows stage in one slot row");
+
+constexpr int kLdsBytes = kDenseLds > kPackedLds ? kDenseLds : kPackedLds;
+static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per gfx950 CU");
+static_assert(kWaves * kHeadBlock * kStatW * 4 <= kWaves * kPTile, "final sums fit the P' area");
+static_assert(kWaves * kHeadBlock * kStatW * 4 <= kPkPBytes, "final sums fit the P' area");
 
 struct DecodeParams {
   const uint16_t* q_lat;
@@ -99,7 +117,7 @@ struct DecodeParams {
   float* out;
   float* lse;
   int32_t batch, heads, max_pages, num_pool_pages, max_seqlen;
-  int32_t n_hb, n_splits;
+  int32_t n_hb, n_dense, n_splits;
   int32_t P, log2P, sink_n, local;
   int64_t latent_meta_off, rope_codes_off, rope_meta_off, page_bytes;
   float c_log2;  // softmax_scale * log2(e)
@@ -188,6 +206,11 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// 32-bit LDS address of a pointer into shared memory.
+__device__ inline uint32_t lds_addr(const void* ptr) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)ptr));
+}
+
 // Sum / max over the four 16-lane rows (lanes l, l^16, l^32, l^48) with the
 // row-swap permutes (no LDS traffic); every row gets the same result.
 __device__ inline float row_allsum(float v) {
@@ -216,27 +239,39 @@ struct QueryOps {
 // (q_lat) plus [head][128 B] (q_rope): wave w fetches latent group w of every
 // head (lane: head lane / 4, 32 channels), wave 0 also the q_rope rows.
 // Heads past the last one read a copy of the last head.
-__device__ inline void stage_query(uint8_t* ql_lds, uint8_t* qr_lds, const DecodeParams& p, int b, int hb, int wave,
-                                   int lane) {
+struct QueryRows {
+  u32x4 lat[4], rope[2];
+};
+
+__device__ inline void fetch_query(QueryRows& qr, const DecodeParams& p, int b, int hb, int wave, int lane) {
   const int h = hb * kHeadBlock + (lane >> 2), part = lane & 3;
   const int hc = h < p.heads ? h : p.heads - 1;
   const uint16_t* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + hc) * kLatentDim + 128 * wave + 32 * part;
-  u32x4 v[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) v[u] = ldg<u32x4>(ql + 8 * u);
-  u32x4 r[2];
+  for (int u = 0; u < 4; ++u) qr.lat[u] = ldg<u32x4>(ql + 8 * u);
   if (wave == 0) {
-    const uint16_t* qr = p.q_rope + (static_cast<int64_t>(b) * p.heads + hc) * kRopeDim + 16 * part;
-    r[0] = ldg<u32x4>(qr);
-    r[1] = ldg<u32x4>(qr + 8);
+    const uint16_t* qp = p.q_rope + (static_cast<int64_t>(b) * p.heads + hc) * kRopeDim + 16 * part;
+    qr.rope[0] = ldg<u32x4>(qp);
+    qr.rope[1] = ldg<u32x4>(qp + 8);
   }
+}
+
+__device__ inline void store_query(const QueryRows& qr, uint8_t* ql_lds, uint8_t* qr_lds, int wave, int lane) {
+  const int part = lane & 3;
   uint8_t* row = ql_lds + (lane >> 2) * 1024 + 2 * (128 * wave + 32 * part);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) lds_st<u32x4>(row + 16 * u, v[u]);
+  for (int u = 0; u < 4; ++u) lds_st<u32x4>(row + 16 * u, qr.lat[u]);
   if (wave == 0) {
-    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * part, r[0]);
-    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * part + 16, r[1]);
+    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * part, qr.rope[0]);
+    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * part + 16, qr.rope[1]);
   }
+}
+
+__device__ inline void stage_query(uint8_t* ql_lds, uint8_t* qr_lds, const DecodeParams& p, int b, int hb, int wave,
+                                   int lane) {
+  QueryRows qr;
+  fetch_query(qr, p, b, hb, wave, lane);
+  store_query(qr, ql_lds, qr_lds, wave, lane);
 }
 
 // MFMA operands of the query from the staged rows: lane (h, gq) takes channels
@@ -331,132 +366,158 @@ __device__ inline void rope_ops(RopeOps& r, const uint8_t* qr_row, const uint8_t
 }
 
 // ---------------------------------------------------------------------------
-// packed tiles
+// packed tiles, staged in LDS by direct loads
 
 template <int BITS>
-struct Stage {
-  uint32_t lat[BITS == 4 ? 16 : 8];  // dwords of the 4 groups
-  u32x2 rope;
-  u32x4 ma;        // latent metadata of token n16
-  uint32_t rmeta;  // 4 bytes of the page's k_R metadata (first tile of a page)
+struct TileGeom {
+  static constexpr int kLatRow = kLatentDim * BITS / 8;  // bytes of one token's codes
+  static constexpr int kLatBytes = kTile * kLatRow;     // 4096 or 2048
+  static constexpr int kLatLoads = kLatBytes / 1024;    // direct loads of the latent codes
+  static constexpr int kLoads = kLatLoads + 1;          // + k_R codes, latent and k_R metadata
+  static constexpr int kOffRope = kLatBytes;            // [16][32 B]
+  static constexpr int kOffMeta = kLatBytes + 512;      // [16][4 x (fp16 scale, fp16 min)]
+  static constexpr int kOffRMeta = kLatBytes + 768;     // 64 fp16 scales, 64 fp16 mins
 };
 
-// Per-lane byte offsets inside a tile (constant over the kernel).
-struct LaneOffs {
-  uint32_t lat, rope, meta;
-};
-
-// Loads the 16-token tile whose first slot is slot0 of `page` (a wave-uniform
-// pointer); every address is page base (scalar) + 32-bit lane offset.
+// Offset inside a slot of 16-byte unit u of latent row `row` (XOR swizzle).
 template <int BITS>
-__device__ inline void load_stage(Stage<BITS>& sg, const uint8_t* page, int slot0, bool new_page,
-                                  const LaneOffs& lo, int lane, const DecodeParams& p) {
-  constexpr int kLatRow = kLatentDim * BITS / 8;
-  const uint8_t* lat = page + slot0 * kLatRow;
+__device__ inline int lat_unit(int row, int u) {
+  if constexpr (BITS == 4) return row * 256 + ((u ^ row) << 4);
+  else return row * 128 + ((u ^ (row & 7)) << 4);
+}
+
+// 16 bytes from global memory straight into LDS at lds_base + 16 * lane.
+__device__ inline void load_to_lds(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Source offset (inside the tile's latent rows) of the 16 bytes lane `lane`
+// moves with direct load c: the lane writes slot unit 64 c + lane, which
+// holds source unit (that unit) XOR row.
+template <int BITS>
+__device__ inline uint32_t lat_src(int c, int lane) {
+  if constexpr (BITS == 4) {
+    const int row = 4 * c + (lane >> 4);
+    return static_cast<uint32_t>(row * 256 + (((lane & 15) ^ row) << 4));
+  } else {
+    const int pos = 64 * c + lane, row = pos >> 3;
+    return static_cast<uint32_t>(row * 128 + (((pos & 7) ^ (row & 7)) << 4));
+  }
+}
+
+// Issues the direct loads of one 16-token tile (first slot slot0 of a
+// wave-uniform page) into an LDS slot: always TileGeom<BITS>::kLoads
+// vector-memory instructions, so the waits below can count them.
+template <int BITS>
+__device__ inline void dma_tile(uint8_t* slot, const uint8_t* page, int slot0, const uint32_t (&src)[4], int lane,
+                                const DecodeParams& p) {
+  using G = TileGeom<BITS>;
+  if (page) {
+    const uint8_t* lat = page + slot0 * G::kLatRow;
+#pragma unroll
+    for (int c = 0; c < G::kLatLoads; ++c) load_to_lds(lat + src[c], slot + 1024 * c);
+    const uint8_t* s = lane < 32 ? page + p.rope_codes_off + slot0 * kRopeRowBytes + 16 * lane
+                       : lane < 48 ? page + p.latent_meta_off + slot0 * 16 + 16 * (lane - 32)
+                                   : page + p.rope_meta_off + 16 * (lane - 48);
+    load_to_lds(s, slot + G::kOffRope);
+  } else {  // page missing from the block table: the tile is skipped
+#pragma unroll
+    for (int c = 0; c < G::kLoads; ++c) load_to_lds(p.q_lat, slot + 1024 * c);
+  }
+}
+
+// Waits until at most `after` tiles' direct loads are still in flight (the
+// loads of older tiles have landed in LDS).  Only direct loads are in flight
+// in the packed loop, so the count is exact.
+template <int BITS>
+__device__ inline void wait_tiles_after(int after) {
+  constexpr int K = TileGeom<BITS>::kLoads;
+  if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * K) : "memory");
+  else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Scores (log2 domain) of one packed tile (tokens j0 .. j0+15 of a complete
+// page, valid in [vlo, vhi)) from its LDS slot: lane (h, gq) gets tokens
+// 4 gq + r of head h.  md[r] = the metadata words of token 4 gq + r.
+template <int BITS>
+__device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BITS>& q, RopeOps& ro,
+                              const uint8_t* slot, bool new_page, const uint8_t* qr_row, int j0, int vlo, int vhi,
+                              int n16, int gq, float c_log2) {
+  using G = TileGeom<BITS>;
+  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
+  const UnpackK uk = unpack_k();
+  uint32_t lat[BITS == 4 ? 16 : 8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (BITS == 4) {
-      const u32x4 v = ldg<u32x4>(lat + lo.lat + 64 * i);
+      const u32x4 v = lds_ld<u32x4>(slot + lat_unit<4>(n16, 4 * i + gq));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sg.lat[4 * i + e] = v[e];
+      for (int e = 0; e < 4; ++e) lat[4 * i + e] = v[e];
     } else {
-      const u32x2 v = ldg<u32x2>(lat + lo.lat + 32 * i);
-      sg.lat[2 * i + 0] = v[0];
-      sg.lat[2 * i + 1] = v[1];
+      const u32x2 v = lds_ld<u32x2>(slot + lat_unit<2>(n16, 2 * i + (gq >> 1)) + 8 * (gq & 1));
+      lat[2 * i] = v[0];
+      lat[2 * i + 1] = v[1];
     }
   }
-  sg.rope = ldg<u32x2>(page + p.rope_codes_off + slot0 * kRopeRowBytes + lo.rope);
-  sg.ma = ldg<u32x4>(page + p.latent_meta_off + slot0 * 16 + lo.meta);
-  if (new_page) sg.rmeta = ldg<uint32_t>(page + p.rope_meta_off + 4 * lane);
-}
-
-template <int BITS>
-__device__ inline half8 chunk_of(const Stage<BITS>& sg, int i, int d, const UnpackK& k) {
-  if constexpr (BITS == 4) return unpack4(sg.lat[4 * i + d], k);
-  else return unpack2(sg.lat[2 * i + (d >> 1)], d & 1, k);
-}
-
-// Score MFMAs of one packed tile: acc[g] = q_g . x_g per latent group,
-// acc[4] = rope and metadata terms / 256.  The x tile goes to LDS.  After
-// this the stage registers are free for the next tile.
-template <int BITS>
-__device__ void packed_mfma(f32x4 (&acc)[5], const QueryOps<BITS>& q, RopeOps& ro, const Stage<BITS>& sg,
-                            bool new_page, uint8_t* xt, uint8_t* meta_lds, uint8_t* rmeta_lds, const uint8_t* qr_row,
-                            int lane, int n16, int gq) {
-  const UnpackK uk = unpack_k();
-  if (gq == 0) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) lds_st<uint32_t>(meta_lds + (g * kTile + n16) * 4, sg.ma[g]);
-  }
-  if (new_page) {
-    lds_st<uint32_t>(rmeta_lds + 4 * lane, sg.rmeta);
-    lds_wait();
-    rope_ops(ro, qr_row, rmeta_lds, gq);
-  }
+  const u32x2 rope = lds_ld<u32x2>(slot + G::kOffRope + n16 * kRopeRowBytes + 8 * gq);
+  const u32x4 ma = lds_ld<u32x4>(slot + G::kOffMeta + 16 * n16);
+  if (new_page) rope_ops(ro, qr_row, slot + G::kOffRMeta, gq);
+  f32x4 acc[5];
 #pragma unroll
   for (int g = 0; g < 5; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint8_t* lrow = xt + n16 * kXRow + 64 * gq;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const half8 x = chunk_of<BITS>(sg, i, d, uk);
+      const half8 x = BITS == 4 ? unpack4(lat[4 * i + d], uk) : unpack2(lat[2 * i + (d >> 1)], d & 1, uk);
       acc[i] = mfma(x, q.lat[i][d], acc[i]);
-      lds_st<half8>(lrow + 256 * i + 16 * d, x);
     }
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const half8 xr = unpack4(sg.rope[e], uk);
+    const half8 xr = unpack4(rope[e], uk);
     acc[4] = mfma(xr, ro.hi[e], acc[4]);
     acc[4] = mfma(xr, ro.lo[e], acc[4]);
   }
-  acc[4] = mfma(__builtin_bit_cast(half8, sg.ma), q.meta, acc[4]);
-}
-
-// Scores (log2 domain) of the tile tokens j0 .. j0+15, valid in [vlo, vhi):
-// lane (h, gq) gets tokens 4 gq + r of head h.
-template <int BITS>
-__device__ inline void packed_fold(float (&sc)[4], const f32x4 (&acc)[5], float bias, int j0, int vlo, int vhi,
-                                   const uint8_t* meta_lds, int gq, float c_log2) {
-  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
-  lds_wait();
-  u32x4 mg[4];
+  acc[4] = mfma(__builtin_bit_cast(half8, ma), q.meta, acc[4]);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) mg[g] = lds_ld<u32x4>(meta_lds + (g * kTile + 4 * gq) * 4);
+  for (int r = 0; r < 4; ++r) md[r] = lds_ld<u32x4>(slot + G::kOffMeta + 16 * (4 * gq + r));
   float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = fmaf(lo_f16(mg[g][r]), acc[g][r], v[r]);
+    for (int r = 0; r < 4; ++r) v[r] = fmaf(lo_f16(md[r][g]), acc[g][r], v[r]);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = j0 + 4 * gq + r;
-    const float z = fmaf(v[r], kappa, fmaf(acc[4][r], 256.f, bias));
+    const float z = fmaf(v[r], kappa, fmaf(acc[4][r], 256.f, ro.bias));
     sc[r] = (t >= vlo && t < vhi) ? z * c_log2 : kNegInf;
   }
 }
 
-// Weights of a packed tile: P'_g = fp16(fp16(p) s_g) per latent group into
-// LDS [group][lane]; adds this lane's sums of p, of the fp16 P'_g and of
-// p m_g to st.
-__device__ inline void packed_weights(const float (&pr)[4], const uint8_t* meta_lds, uint8_t* ptile,
-                                      float (&st)[kStatW], int lane, int gq) {
+// P' entry of (K block kb, latent group g, reader lane row gq, head h): the 8
+// tokens 8 gq .. 8 gq + 7 of the K block (tiles 2 kb, 2 kb + 1), fp16.
+__device__ inline int p_entry(int kb, int g, int gq, int h) { return (((kb * 4 + g) * 4 + gq) * kHeadBlock + h) * 16; }
+
+// Weights of this wave's packed tile: P'_g = fp16(fp16(p) s_g) into the P'
+// entries its tokens fall in; adds this lane's sums of p, of the fp16 P'_g
+// and of p m_g to st.
+__device__ inline void packed_weights(const float (&pr)[4], const u32x4 (&md)[4], uint8_t* pbase,
+                                      float (&st)[kStatW], int wave, int n16, int gq) {
   const half2 ph[2] = {half2{static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1])},
                        half2{static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])}};
   st[0] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   const half2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
-  u32x4 mg[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) mg[g] = lds_ld<u32x4>(meta_lds + (g * kTile + 4 * gq) * 4);
+  const int at = 8 * (gq & 1);  // tokens 4 gq .. 4 gq + 3 of the tile
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     half4 pa;
     float cs = st[1 + g], ms = st[5 + g];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint32_t w0 = mg[g][2 * k], w1 = mg[g][2 * k + 1];
+      const uint32_t w0 = md[2 * k][g], w1 = md[2 * k + 1][g];
       const half2 s2 = {__builtin_bit_cast(half2, w0)[0], __builtin_bit_cast(half2, w1)[0]};
       const half2 m2 = {__builtin_bit_cast(half2, w0)[1], __builtin_bit_cast(half2, w1)[1]};
       const half2 ps = ph[k] * s2;
@@ -465,9 +526,99 @@ __device__ inline void packed_weights(const float (&pr)[4], const uint8_t* meta_
       pa[2 * k] = ps[0];
       pa[2 * k + 1] = ps[1];
     }
-    lds_st<half4>(ptile + g * 512 + 8 * lane, pa);
+    lds_st<half4>(pbase + p_entry(wave >> 1, g, 2 * (wave & 1) + (gq >> 1), n16) + at, pa);
     st[1 + g] = cs;
     st[5 + g] = ms;
+  }
+}
+
+// 8 crumbs (parity par of 8 nibbles) of w -> fp16 1 + code/4, slots
+// [n0 n4 n1 n5 n2 n6 n3 n7] of the nibbles.
+__device__ inline half8 unpack2_pairs(uint32_t w, int par, const UnpackK& k) {
+  u32x4 v;
+  if (par == 0) {
+    v[0] = ((w << 8) & k.m2) | k.e;
+    v[1] = ((w << 4) & k.m2) | k.e;
+    v[2] = (w & k.m2) | k.e;
+    v[3] = ((w >> 4) & k.m2) | k.e;
+  } else {
+    v[0] = ((w << 6) & k.m2) | k.e;
+    v[1] = ((w << 2) & k.m2) | k.e;
+    v[2] = ((w >> 2) & k.m2) | k.e;
+    v[3] = ((w >> 6) & k.m2) | k.e;
+  }
+  return __builtin_bit_cast(half8, v);
+}
+
+// Output MFMAs of latent group `wave` over the round's four tiles (slot s of
+// every wave).  ds_read_b64_tr_b4: within each 16-lane row, lane i receives
+// nibble i of the 8 bytes each of the row's lanes addressed.  Lane (j, gq)
+// addresses token 8 gq + sigma(j) (j < 8, K block 0) or 32 + 8 gq +
+// sigma(j - 8) (K block 1); sigma undoes the unpack's slot order, so slot k of
+// the unpacked B operand is token 8 gq + k of its K block, as in P'.
+// 4-bit codes: column n16 of block kk = channel 128 g + 16 kk + n16.
+// 2-bit codes: chunk c, parity par -> o[2 c + par], channel 128 g + 32 c +
+// 2 n16 + par.
+template <int BITS>
+__device__ inline void packed_pv(f32x4 (&o)[8], const uint8_t* smem, int s, int wave, int n16, int gq) {
+  const UnpackK uk = unpack_k();
+  const half8 pa0 = lds_ld<half8>(smem + kPkOffP + p_entry(0, wave, gq, n16));
+  const half8 pa1 = lds_ld<half8>(smem + kPkOffP + p_entry(1, wave, gq, n16));
+  const int j = n16 & 7;
+  const int tau = (n16 < 8 ? 0 : 32) + 8 * gq + (((j & 3) << 1) | (j >> 2));
+  const int row = tau & 15;
+  const uint8_t* base = smem + kPkOffStage + (s * kWaves + (tau >> 4)) * kSlotBytes;
+  // The transposed reads go through inline assembly: for an LDS intrinsic the
+  // compiler would first wait for every direct load in flight (the slots being
+  // filled are not the ones read here).  One lgkmcnt wait covers all reads.
+  if constexpr (BITS == 4) {
+    // unit 4 wave + k2 of row `row` at (4 wave ^ (row & 12)) + (k2 ^ (row & 3))
+    uint32_t a[4];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2)
+      a[k2] = lds_addr(base + lat_unit<4>(row, 4 * wave + k2));
+    i32x2 r[8];
+    asm volatile(
+        "ds_read_b64_tr_b4 %0, %8\n\t"
+        "ds_read_b64_tr_b4 %1, %8 offset:8\n\t"
+        "ds_read_b64_tr_b4 %2, %9\n\t"
+        "ds_read_b64_tr_b4 %3, %9 offset:8\n\t"
+        "ds_read_b64_tr_b4 %4, %10\n\t"
+        "ds_read_b64_tr_b4 %5, %10 offset:8\n\t"
+        "ds_read_b64_tr_b4 %6, %11\n\t"
+        "ds_read_b64_tr_b4 %7, %11 offset:8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      o[kk] = mfma(pa0, unpack4(static_cast<uint32_t>(r[kk][0]), uk), o[kk]);
+      o[kk] = mfma(pa1, unpack4(static_cast<uint32_t>(r[kk][1]), uk), o[kk]);
+    }
+  } else {
+    uint32_t a[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+      a[c2] = lds_addr(base + lat_unit<2>(row, 2 * wave + c2));
+    i32x2 r[4];
+    asm volatile(
+        "ds_read_b64_tr_b4 %0, %4\n\t"
+        "ds_read_b64_tr_b4 %1, %4 offset:8\n\t"
+        "ds_read_b64_tr_b4 %2, %5\n\t"
+        "ds_read_b64_tr_b4 %3, %5 offset:8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a[0]), "v"(a[1])
+        : "memory");
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        o[2 * c + par] = mfma(pa0, unpack2_pairs(static_cast<uint32_t>(r[c][0]), par, uk), o[2 * c + par]);
+        o[2 * c + par] = mfma(pa1, unpack2_pairs(static_cast<uint32_t>(r[c][1]), par, uk), o[2 * c + par]);
+      }
+    }
   }
 }
 
@@ -651,191 +802,104 @@ __device__ void dense_scores(float (&sc)[4], const QueryOps<BITS>& q, const uint
   }
 }
 
-// First item whose cost prefix reaches c (items: D BF16 tiles of cost
-// kDenseCost, then packed tiles of cost 1).
-__device__ inline int item_of_cost(int c, int D) {
-  return c <= kDenseCost * D ? (c + kDenseCost - 1) / kDenseCost : D + (c - kDenseCost * D);
+// ---------------------------------------------------------------------------
+// workgroups
+
+struct WgCtx {
+  int b, hb, grp, split, lane, wave, n16, gq;
+};
+
+// Common round step 2 bookkeeping: the tile maxima of the four waves meet in
+// LDS (smax [head][wave]); returns the rescale factor of head n16 (score
+// layout) and updates m_run, and the factors ah of heads 4 gq + r (output
+// layout) and m_o.
+__device__ inline float raise_max(float& m_run, float (&m_o)[4], float (&ah)[4], const float* smax, int n16, int gq) {
+  const f32x4 mv = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + n16 * kWaves));
+  const float rmax = fmaxf(m_run, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+  const float alpha = m_run == kNegInf ? 0.f : exp2f(m_run - rmax);
+  m_run = rmax;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const f32x4 mo = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + (4 * gq + rr) * kWaves));
+    const float ro = fmaxf(m_o[rr], fmaxf(fmaxf(mo[0], mo[1]), fmaxf(mo[2], mo[3])));
+    ah[rr] = m_o[rr] == kNegInf ? 0.f : exp2f(m_o[rr] - ro);
+    m_o[rr] = ro;
+  }
+  return alpha;
 }
 
-// ---------------------------------------------------------------------------
+__device__ inline void rescale_out(f32x4 (&o)[8], const float (&ah)[4]) {
+  if (__any(ah[0] != 1.f || ah[1] != 1.f || ah[2] != 1.f || ah[3] != 1.f)) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) o[k][rr] *= ah[rr];
+    }
+  }
+}
 
+// BF16-path workgroup `ds` of n_dense: BF16 tiles (dense token indices, see
+// dense_src) split evenly; fp16 x tiles in LDS serve both MFMAs.
 template <int BITS>
-__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+__device__ void dense_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], const DecodeParams& p, uint8_t* smem,
+                         const SeqRanges& sr, const WgCtx& cx, int ds) {
   constexpr float kappa = BITS == 4 ? 16.f : 4.f;
-  const int split = blockIdx.x % p.n_splits;
-  const int grp = blockIdx.x / p.n_splits;  // b * n_hb + hb
-  const int hb = grp % p.n_hb, b = grp / p.n_hb;
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int n16 = lane & 15, gq = lane >> 4;
+  const int lane = cx.lane, wave = cx.wave, n16 = cx.n16, gq = cx.gq;
   uint8_t* const xt_own = smem + kOffX + wave * kXTile;
   uint8_t* const p_own = smem + kOffP + wave * kPTile;
-  uint8_t* const meta_own = smem + kOffMeta + wave * 256;
-  uint8_t* const rmeta_own = smem + kOffRMeta + wave * 256;
   float* const smax = reinterpret_cast<float*>(smem + kOffMax);
-  int* const s_pid = reinterpret_cast<int*>(smem + kOffPid);
   const uint8_t* const qr_row = smem + kOffQr + n16 * 128;
   uint8_t* const ql_stage = smem + kOffX;  // query rows, until round 0 writes x tiles
 
-  stage_query(ql_stage, smem + kOffQr, p, b, hb, wave, lane);
-  const SeqRanges sr = seq_ranges(p, b);
-
-  // this workgroup's items: BF16 tiles first (cost kDenseCost), then packed;
-  // wave w takes the contiguous run [my0, my1)
+  stage_query(ql_stage, smem + kOffQr, p, cx.b, cx.hb, wave, lane);
   const int n_dense = sr.lo_p + (sr.L - sr.hi_p);
   const int D = (n_dense + kTile - 1) / kTile;
-  const int t_lo = sr.lo_p / kTile;
-  const int T = sr.hi_p > sr.lo_p ? (sr.hi_p + kTile - 1) / kTile - t_lo : 0;
-  const int cost = kDenseCost * D + T;
-  const int cs = (cost + p.n_splits - 1) / p.n_splits;
-  const int c0 = min(cost, split * cs), c1 = min(cost, c0 + cs);
-  const int i0 = item_of_cost(c0, D), i1 = item_of_cost(c1, D);
+  const int per = (D + p.n_dense - 1) / p.n_dense;
+  const int i0 = min(D, ds * per), i1 = min(D, i0 + per);
   const int rounds = (i1 - i0 + kWaves - 1) / kWaves;
   const int my0 = i0 + wave * rounds, my1 = min(i1, my0 + rounds);
-
-  // page ids of the packed items, staged once
-  const int ip0 = max(i0, D);
-  int pg_first = 0, n_pg = 0;
-  if (i1 > ip0) {
-    pg_first = ((t_lo + ip0 - D) * kTile) >> p.log2P;
-    n_pg = (((t_lo + i1 - 1 - D) * kTile) >> p.log2P) - pg_first + 1;
-  }
-  const int32_t* bt_row = p.block_table + static_cast<int64_t>(b) * p.max_pages;
-  for (int k = threadIdx.x; k < min(n_pg, kPageWin); k += kThreads) s_pid[k] = bt_row[pg_first + k];
-  bool pid_staged = false;  // the first tile reads the block table directly
-  auto page_ptr_of = [&](int pidx) -> const uint8_t* {
-    const int k = pidx - pg_first;
-    const int id = uniform(pid_staged && k < kPageWin ? *reinterpret_cast<volatile int*>(s_pid + k) : bt_row[pidx]);
-    return page_of_id(p, id);
-  };
-
-  const LaneOffs lo{static_cast<uint32_t>(n16 * (kLatentDim * BITS / 8) + (BITS == 4 ? 16 : 8) * gq),
-                    static_cast<uint32_t>(n16 * kRopeRowBytes + 8 * gq), static_cast<uint32_t>(n16 * 16)};
-
-  // running max: m_run for head n16 (score layout), m_o[r] for heads 4 gq + r
-  // (output layout); identical in every wave.  Output of latent group `wave`:
-  // heads 4 gq + r, columns 16 kk + n16.  Per-lane sums (head n16): st.
-  float m_run = kNegInf;
-  float m_o[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-  f32x4 o[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float st[kStatW];
-#pragma unroll
-  for (int k = 0; k < kStatW; ++k) st[k] = 0.f;
-
-  Stage<BITS> cur;
-  RopeOps ro;
-  int ro_page = -1;
-  // Loads packed item `it` into sg; returns its page index, -1 for a BF16
-  // item or none, -2 for a page missing from the block table.
-  auto stage_for = [&](Stage<BITS>& sg, int it, int prev_page) -> int {
-    if (it >= my1 || it < D) return -1;
-    const int j0 = (t_lo + (it - D)) * kTile;
-    const int pidx = j0 >> p.log2P;
-    const uint8_t* page = page_ptr_of(pidx);
-    if (!page) return -2;
-    load_stage<BITS>(sg, page, j0 & (p.P - 1), pidx != prev_page, lo, lane, p);
-    return pidx;
-  };
-  int cur_pidx = stage_for(cur, my0, ro_page);
-  pid_staged = true;
-  __syncthreads();  // query rows and page ids staged
+  lds_barrier();  // query rows staged
   QueryOps<BITS> q;
   load_query<BITS>(q, ql_stage, n16, gq);
-  __syncthreads();  // query rows read: the x tiles may be written
+  lds_barrier();  // query rows read: the x tiles may be written
   if (my0 >= my1) {  // a wave without tiles still feeds zeros to the output MFMAs
-    for (int o = 16 * lane; o < kXTile; o += 64 * 16) lds_st<u32x4>(xt_own + o, u32x4{0, 0, 0, 0});
+    for (int off = 16 * lane; off < kXTile; off += 64 * 16) lds_st<u32x4>(xt_own + off, u32x4{0, 0, 0, 0});
   }
-
+  float m_run = kNegInf;
   for (int r = 0; r < rounds; ++r) {
     const int it = my0 + r;
-
-    // 1. scores of this wave's tile
-    float sc[4];
-    bool has = it < my1;
-    const bool dense = has && it < D;
-    if (dense) {
-      dense_scores<BITS>(sc, q, qr_row, b, sr, it * kTile, xt_own, p_own, lane, n16, gq, p);
-    } else if (has && cur_pidx >= 0) {
-      const int j0 = (t_lo + (it - D)) * kTile;
-      const bool new_page = cur_pidx != ro_page;
-      f32x4 acc[5];
-#pragma unroll
-      for (int g = 0; g < 5; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      packed_mfma<BITS>(acc, q, ro, cur, new_page, xt_own, meta_own, rmeta_own, qr_row, lane, n16, gq);
-      ro_page = cur_pidx;
-      // the codes of this wave's next tile, in flight while the round finishes
-      cur_pidx = stage_for(cur, it + 1, ro_page);
-      packed_fold<BITS>(sc, acc, ro.bias, j0, sr.lo_p, sr.hi_p, meta_own, gq, p.c_log2);
-    } else {
-      has = false;
-    }
-    if (!has || dense) cur_pidx = stage_for(cur, it + 1, ro_page);
-    if (!has) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) sc[k] = kNegInf;
-    }
-    float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    tmax = row_allmax(tmax);
+    const bool has = it < my1;
+    float sc[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+    if (has) dense_scores<BITS>(sc, q, qr_row, cx.b, sr, it * kTile, xt_own, p_own, lane, n16, gq, p);
+    const float tmax = row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
 
-    // 2. softmax: common running max, this tile's weights
-    {
-      const f32x4 mv = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + n16 * kWaves));
-      const float rmax = fmaxf(m_run, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
-      const float alpha = m_run == kNegInf ? 0.f : exp2f(m_run - rmax);
-      m_run = rmax;
-#pragma unroll
-      for (int k = 0; k < kStatW; ++k) st[k] *= alpha;
-    }
-    if (has) {
-      float pr[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pr[k] = sc[k] == kNegInf ? 0.f : exp2f(sc[k] - m_run);
-      if (dense) {
-        half4 pa;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          st[0] += pr[k];
-          pa[k] = static_cast<_Float16>(pr[k] * (1.f / kappa));
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) lds_st<half4>(p_own + g * 512 + 8 * lane, pa);
-      } else {
-        packed_weights(pr, meta_own, p_own, st, lane, gq);
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) lds_st<u32x2>(p_own + g * 512 + 8 * lane, u32x2{0, 0});
-    }
-    // output-layout copy of the running max: heads 4 gq + rr
     float ah[4];
+    const float alpha = raise_max(m_run, m_o, ah, smax, n16, gq);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const f32x4 mv = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + (4 * gq + rr) * kWaves));
-      const float rmax = fmaxf(m_o[rr], fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
-      ah[rr] = m_o[rr] == kNegInf ? 0.f : exp2f(m_o[rr] - rmax);
-      m_o[rr] = rmax;
+    for (int k = 0; k < kStatW; ++k) st[k] *= alpha;
+    half4 pa = {};
+    if (has) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float pr = sc[k] == kNegInf ? 0.f : exp2f(sc[k] - m_run);
+        st[0] += pr;
+        pa[k] = static_cast<_Float16>(pr * (1.f / kappa));
+      }
     }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) lds_st<half4>(p_own + g * 512 + 8 * lane, pa);
     lds_barrier();
 
-    // 3. output of latent group `wave` for the four tiles of the round, in
-    //    pairs: A slots 0-3 tile t (tokens 4 gq + j), slots 4-7 tile t + 1
-    if (__any(ah[0] != 1.f || ah[1] != 1.f || ah[2] != 1.f || ah[3] != 1.f)) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) o[k][rr] *= ah[rr];
-      }
-    }
+    // output of latent group `wave`, tiles in pairs: A slots 0-3 tile t
+    // (tokens 4 gq + j), slots 4-7 tile t + 1
+    rescale_out(o, ah);
 #pragma unroll
     for (int t = 0; t < kWaves; t += 2) {
       const half4 p0 = lds_ld<half4>(smem + kOffP + t * kPTile + wave * 512 + 8 * lane);
       const half4 p1 = lds_ld<half4>(smem + kOffP + (t + 1) * kPTile + wave * 512 + 8 * lane);
-      const half8 pa = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const half8 pa8 = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
       const uint8_t* b0 = smem + kOffX + t * kXTile + (4 * gq + (n16 >> 2)) * kXRow + 8 * (n16 & 3) + 256 * wave;
       const uint8_t* b1 = b0 + kXTile;
 #pragma unroll
@@ -847,14 +911,142 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
         // whole-vector shuffle + bit cast: assembling the operand element by
         // element from the transposed reads produced wrong code with this compiler
         const half8 vb = __builtin_bit_cast(half8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[kk] = mfma(pa, vb, o[kk]);
+        o[kk] = mfma(pa8, vb, o[kk]);
       }
     }
     lds_barrier();
   }
+}
 
-  // per-head sums of every wave, through the (now idle) P' area
-  float* const sfin = reinterpret_cast<float*>(smem + kOffP);
+// Packed workgroup `ps` of n_ps: packed tiles split evenly, each wave a
+// contiguous run; per wave a ring of kSlots LDS slots filled by direct loads.
+// Software-pipelined rounds, two barriers each:
+//   A: output MFMAs of round r-1 (P' and every wave's slot (r-1) % 3) and the
+//      scores of this wave's tile r (slot r % 3)
+//   B: the direct loads of tile r+2 into slot (r+2) % 3 = (r-1) % 3 (free:
+//      all waves are past A), the common running max, P' of round r, the
+//      rescale of the output accumulators
+template <int BITS>
+__device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], const DecodeParams& p, uint8_t* smem,
+                          const SeqRanges& sr, const WgCtx& cx, int ps, int n_ps) {
+  const int lane = cx.lane, wave = cx.wave, n16 = cx.n16, gq = cx.gq;
+  float* const smax = reinterpret_cast<float*>(smem + kPkOffMax);
+  int* const s_pid = reinterpret_cast<int*>(smem + kPkOffPid);
+  const uint8_t* const qr_row = smem + kPkOffQr + n16 * 128;
+  uint8_t* const ql_stage = smem + kPkOffStage + 2 * kWaves * kSlotBytes;  // slot 2 of every wave
+  auto slot_ptr = [&](int s, int w) { return smem + kPkOffStage + (s * kWaves + w) * kSlotBytes; };
+
+  QueryRows qrows;
+  fetch_query(qrows, p, cx.b, cx.hb, wave, lane);
+  const int t_lo = sr.lo_p / kTile;
+  const int T = sr.hi_p > sr.lo_p ? (sr.hi_p + kTile - 1) / kTile - t_lo : 0;
+  const int per = (T + n_ps - 1) / n_ps;
+  const int k0 = min(T, ps * per), k1 = min(T, k0 + per);
+  const int rounds = (k1 - k0 + kWaves - 1) / kWaves;
+  const int my0 = k0 + wave * rounds, my1 = min(k1, my0 + rounds);
+
+  // page ids of this workgroup's tiles (the launch sizes splits so that they
+  // fit the window); loaded together with the query rows
+  int pg_first = 0, n_pg = 0;
+  if (k1 > k0) {
+    pg_first = ((t_lo + k0) * kTile) >> p.log2P;
+    n_pg = min((((t_lo + k1 - 1) * kTile) >> p.log2P) - pg_first + 1, kPageWin);
+  }
+  const int32_t* bt_row = p.block_table + static_cast<int64_t>(cx.b) * p.max_pages + pg_first;
+  constexpr int kPidPerThread = kPageWin / kThreads;
+  int pid[kPidPerThread];
+#pragma unroll
+  for (int i = 0; i < kPidPerThread; ++i) {
+    const int k = threadIdx.x + i * kThreads;
+    pid[i] = k < n_pg ? bt_row[k] : -1;
+  }
+  store_query(qrows, ql_stage, smem + kPkOffQr, wave, lane);
+#pragma unroll
+  for (int i = 0; i < kPidPerThread; ++i) {
+    const int k = threadIdx.x + i * kThreads;
+    if (k < n_pg) s_pid[k] = pid[i];
+  }
+  lds_barrier();  // query rows and page ids staged
+  auto page_of_tile = [&](int it, int& pidx, int& slot0) -> const uint8_t* {
+    const int j0 = (t_lo + it) * kTile;
+    pidx = j0 >> p.log2P;
+    slot0 = j0 & (p.P - 1);
+    const int id = uniform(s_pid[min(max(pidx - pg_first, 0), kPageWin - 1)]);
+    return page_of_id(p, id);
+  };
+  uint32_t src[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) src[c] = lat_src<BITS>(c, lane);
+  auto issue = [&](int it, int s) {
+    int pidx, slot0;
+    const uint8_t* page = page_of_tile(it, pidx, slot0);
+    dma_tile<BITS>(slot_ptr(s, wave), page, slot0, src, lane, p);
+  };
+  if (my0 < my1) issue(my0, 0);
+  if (my0 + 1 < my1) issue(my0 + 1, 1);
+  QueryOps<BITS> q;
+  load_query<BITS>(q, ql_stage, n16, gq);
+  lds_barrier();  // query rows read: slot 2 may be filled
+
+  float m_run = kNegInf;
+  RopeOps ro;
+  int ro_page = -1;
+  for (int r = 0; r <= rounds; ++r) {
+    // A: output of round r - 1, scores of tile r
+    if (r > 0) packed_pv<BITS>(o, smem, (r - 1) % kSlots, wave, n16, gq);
+    const int it = my0 + r;
+    bool has = r < rounds && it < my1;
+    float sc[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+    u32x4 md[4];
+    if (has) {
+      wait_tiles_after<BITS>(it + 1 < my1 ? 1 : 0);  // tile r+1's loads may still fly
+      int pidx, slot0;
+      const uint8_t* page = page_of_tile(it, pidx, slot0);
+      if (page) {
+        packed_scores<BITS>(sc, md, q, ro, slot_ptr(r % kSlots, wave), pidx != ro_page, qr_row, (t_lo + it) * kTile,
+                            sr.lo_p, sr.hi_p, n16, gq, p.c_log2);
+        ro_page = pidx;
+      } else {
+        has = false;
+      }
+    }
+    if (r == rounds) break;
+    const float tmax = row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    if (gq == 0) smax[n16 * kWaves + wave] = tmax;
+    lds_barrier();
+
+    // B: next loads, softmax of round r
+    if (it + 2 < my1) issue(it + 2, (r + 2) % kSlots);
+    float ah[4];
+    const float alpha = raise_max(m_run, m_o, ah, smax, n16, gq);
+#pragma unroll
+    for (int k = 0; k < kStatW; ++k) st[k] *= alpha;
+    if (has) {
+      float pr[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pr[k] = sc[k] == kNegInf ? 0.f : exp2f(sc[k] - m_run);
+      packed_weights(pr, md, smem + kPkOffP, st, wave, n16, gq);
+    } else {  // no tile: zero weights (the slot's stale codes unpack to finite values)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        lds_st<u32x2>(smem + kPkOffP + p_entry(wave >> 1, g, 2 * (wave & 1) + (gq >> 1), n16) + 8 * (gq & 1),
+                      u32x2{0, 0});
+    }
+    rescale_out(o, ah);
+    lds_barrier();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no direct load outlives the workgroup
+}
+
+// Per-head sums of every wave meet in LDS (sums_lds); the partial (or, with
+// one split, the normalized output and lse) is written in natural channel
+// order.  chan(kk, n16) maps an accumulator column to its latent channel.
+template <int BITS, bool kPackedMap>
+__device__ void finish(const DecodeParams& p, uint8_t* sums_lds, const f32x4 (&o)[8], const float (&st)[kStatW],
+                       const float (&m_o)[4], const WgCtx& cx) {
+  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
+  const int wave = cx.wave, n16 = cx.n16, gq = cx.gq;
+  float* const sfin = reinterpret_cast<float*>(sums_lds);
 #pragma unroll
   for (int k = 0; k < kStatW; ++k) {
     const float v = row_allsum(st[k]);
@@ -862,14 +1054,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   }
   __syncthreads();
   const bool direct = p.n_splits == 1;
-  // partial layout (per split): O as [group][kk][lane] f32x4 over heads
-  // 4 gq + r (the MFMA accumulator layout, so every store is 16 B), then the
-  // running max and the sum of the 16 heads
-  float* part = p.parts + (static_cast<int64_t>(grp) * p.n_splits + split) * kPartFloats;
-  float l_h[4], c_h[4], m_h[4];
+  float* part = p.parts + (static_cast<int64_t>(cx.grp) * p.n_splits + cx.split) * kPartFloats;
+  float l_h[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const int hh = 4 * gq + rr;
+    const int hh = 4 * gq + rr, hg = cx.hb * kHeadBlock + hh;
     float l = 0.f, c = 0.f, m = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -879,33 +1068,29 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
       m += f[5 + wave];
     }
     l_h[rr] = l;
-    c_h[rr] = c;
-    m_h[rr] = m;
-  }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    f32x4 v;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(kappa, o[kk][rr] - c_h[rr], m_h[rr]);
-    if (direct) {
-      const int ch = col_to_channel<BITS>(128 * wave + 16 * kk + n16);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int hg = hb * kHeadBlock + 4 * gq + rr;
-        if (hg < p.heads)
-          p.out[(static_cast<int64_t>(b) * p.heads + hg) * kLatentDim + ch] = l_h[rr] > 0.f ? v[rr] / l_h[rr] : 0.f;
+    for (int kk = 0; kk < 8; ++kk) {
+      int ch;
+      if constexpr (kPackedMap)
+        ch = BITS == 4 ? 128 * wave + 16 * kk + n16 : 128 * wave + 32 * (kk >> 1) + 2 * n16 + (kk & 1);
+      else
+        ch = col_to_channel<BITS>(128 * wave + 16 * kk + n16);
+      const float v = fmaf(kappa, o[kk][rr] - c, m);
+      if (direct) {
+        if (hg < p.heads) p.out[(static_cast<int64_t>(cx.b) * p.heads + hg) * kLatentDim + ch] = v * inv;
+      } else {
+        part[hh * kLatentDim + ch] = v;
       }
-    } else {
-      reinterpret_cast<f32x4*>(part)[(wave * 8 + kk) * 64 + lane] = v;
     }
   }
   if (wave == 0 && n16 == 0) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int hh = 4 * gq + rr, hg = hb * kHeadBlock + hh;
+      const int hh = 4 * gq + rr, hg = cx.hb * kHeadBlock + hh;
       if (direct) {
         if (hg < p.heads)
-          p.lse[static_cast<int64_t>(b) * p.heads + hg] =
+          p.lse[static_cast<int64_t>(cx.b) * p.heads + hg] =
               l_h[rr] > 0.f ? (m_o[rr] + log2f(l_h[rr])) * 0.69314718055994531f : kNegInf;
       } else {
         part[kHeadBlock * kLatentDim + hh] = m_o[rr];
@@ -915,69 +1100,82 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   }
 }
 
-// Merge of the per-split partials of one sequence and head block.  Split s
-// holds O_s = sum_j p_j c_j with p_j = 2^(z_j - m_s) and l_s = sum_j p_j; the
-// result is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
-// One workgroup of 64 threads per (sequence, head block, latent group g,
-// 16-column block kk); thread = MFMA lane (n16, gq): column 128 g + 16 kk +
-// n16 of heads 4 gq + r.
 template <int BITS>
+__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  WgCtx cx;
+  cx.split = blockIdx.x % p.n_splits;
+  cx.grp = blockIdx.x / p.n_splits;  // b * n_hb + hb
+  cx.hb = cx.grp % p.n_hb;
+  cx.b = cx.grp / p.n_hb;
+  cx.lane = threadIdx.x & 63;
+  cx.wave = uniform(threadIdx.x >> 6);
+  cx.n16 = cx.lane & 15;
+  cx.gq = cx.lane >> 4;
+  const SeqRanges sr = seq_ranges(p, cx.b);
+  // running max of heads 4 gq + r (identical in every wave), this wave's
+  // output (latent group `wave`: heads 4 gq + r, columns 16 kk + n16) and
+  // per-lane sums (head n16)
+  float m_o[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+  f32x4 o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float st[kStatW];
+#pragma unroll
+  for (int k = 0; k < kStatW; ++k) st[k] = 0.f;
+  if (cx.split < p.n_dense) {
+    dense_wg<BITS>(o, st, m_o, p, smem, sr, cx, cx.split);
+    finish<BITS, false>(p, smem + kOffP, o, st, m_o, cx);
+  } else {
+    packed_wg<BITS>(o, st, m_o, p, smem, sr, cx, cx.split - p.n_dense, p.n_splits - p.n_dense);
+    finish<BITS, true>(p, smem + kPkOffP, o, st, m_o, cx);
+  }
+}
+
+// Merge of the per-split partials of one sequence and head.  Split s holds
+// O_s = sum_j p_j c_j with p_j = 2^(z_j - m_s) and l_s = sum_j p_j; the
+// result is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+// One 64-thread workgroup per (sequence, head, half of the 512 channels);
+// thread t takes 4 channels.
 __global__ void __launch_bounds__(64) combine_kernel(const float* __restrict__ parts, float* __restrict__ out,
                                                      float* __restrict__ lse, int heads, int n_hb, int n_splits) {
-  __shared__ float s_ml[kMaxSplits][2 * kHeadBlock];  // per split: max of the 16 heads, then sums
-  __shared__ float s_M[kHeadBlock], s_L[kHeadBlock];
-  const int grp = blockIdx.x >> 5, gk = blockIdx.x & 31;  // gk = 8 g + kk
-  const int b = grp / n_hb, hb = grp % n_hb;
-  const int t = threadIdx.x, n16 = t & 15, gq = t >> 4;
+  __shared__ float s_m[kMaxSplits], s_l[kMaxSplits];
+  const int grp = blockIdx.x >> 5, hh = (blockIdx.x >> 1) & 15, half = blockIdx.x & 1;
+  const int b = grp / n_hb, hg = (grp % n_hb) * kHeadBlock + hh;
+  if (hg >= heads) return;
   const float* base = parts + static_cast<int64_t>(grp) * n_splits * kPartFloats;
-  // this thread's partials of the first splits go out before the (max, sum)
-  // staging, so both latencies overlap
+  const int t = threadIdx.x, c = 256 * half + 4 * t;
+  // the first splits' partials go out before the (max, sum) staging
   constexpr int kEarly = 16;
   f32x4 v[kEarly];
 #pragma unroll
   for (int s = 0; s < kEarly; ++s)
-    v[s] = s < n_splits ? ldg<f32x4>(base + static_cast<int64_t>(s) * kPartFloats + 4 * (gk * 64 + t))
+    v[s] = s < n_splits ? ldg<f32x4>(base + static_cast<int64_t>(s) * kPartFloats + hh * kLatentDim + c)
                         : f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = t; k < n_splits * 2 * kHeadBlock; k += 64)
-    s_ml[k >> 5][k & 31] = base[(k >> 5) * kPartFloats + kHeadBlock * kLatentDim + (k & 31)];
-  __syncthreads();
-  if (t < kHeadBlock) {
-    float M = kNegInf;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, s_ml[s][t]);
-    float L = 0.f;
-    for (int s = 0; s < n_splits; ++s) L = fmaf(s_ml[s][t] == kNegInf ? 0.f : exp2f(s_ml[s][t] - M), s_ml[s][16 + t], L);
-    s_M[t] = M;
-    s_L[t] = L;
+  for (int s = t; s < n_splits; s += 64) {
+    s_m[s] = base[static_cast<int64_t>(s) * kPartFloats + kHeadBlock * kLatentDim + hh];
+    s_l[s] = base[static_cast<int64_t>(s) * kPartFloats + kHeadBlock * kLatentDim + kHeadBlock + hh];
   }
   __syncthreads();
-  float Mh[4];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) Mh[rr] = s_M[4 * gq + rr];
+  float M = kNegInf;
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, s_m[s]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
   auto add = [&](int s, const f32x4& x) {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float m_s = s_ml[s][4 * gq + rr];
-      const float f = m_s == kNegInf ? 0.f : exp2f(m_s - Mh[rr]);
-      acc[rr] = fmaf(f, x[rr], acc[rr]);
-    }
+    const float f = s_m[s] == kNegInf ? 0.f : exp2f(s_m[s] - M);
+    L = fmaf(f, s_l[s], L);
+    acc += f * x;
   };
 #pragma unroll
   for (int s = 0; s < kEarly; ++s)
     if (s < n_splits) add(s, v[s]);
 #pragma unroll 8
   for (int s = kEarly; s < n_splits; ++s)
-    add(s, ldg<f32x4>(base + static_cast<int64_t>(s) * kPartFloats + 4 * (gk * 64 + t)));
-  const int ch = col_to_channel<BITS>(16 * gk + n16);
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int hg = hb * kHeadBlock + 4 * gq + rr;
-    const float L = s_L[4 * gq + rr];
-    if (hg < heads) out[(static_cast<int64_t>(b) * heads + hg) * kLatentDim + ch] = L > 0.f ? acc[rr] / L : 0.f;
-  }
-  if (gk == 0 && t < kHeadBlock && hb * kHeadBlock + t < heads)
-    lse[static_cast<int64_t>(b) * heads + hb * kHeadBlock + t] =
-        s_L[t] > 0.f ? (s_M[t] + log2f(s_L[t])) * 0.69314718055994531f : kNegInf;
+    add(s, ldg<f32x4>(base + static_cast<int64_t>(s) * kPartFloats + hh * kLatentDim + c));
+  const float il = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<f32x4*>(out + (static_cast<int64_t>(b) * heads + hg) * kLatentDim + c) = acc * il;
+  if (half == 0 && t == 0)
+    lse[static_cast<int64_t>(b) * heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
 }
 
 }  // namespace
@@ -1008,6 +1206,7 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
       (ring_buf && !aligned16(ring_buf)) || (workspace && !aligned16(workspace)))
     return MLA_LOWBIT_ERR_ARG;
   const DecodePlan plan = plan_decode(g, batch, heads, max_seqlen);
+  if (!plan.ok) return MLA_LOWBIT_ERR_UNSUPPORTED;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return MLA_LOWBIT_ERR_WORKSPACE;
   DecodeParams p{};
@@ -1028,6 +1227,7 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   p.num_pool_pages = num_pool_pages;
   p.max_seqlen = max_seqlen;
   p.n_hb = plan.n_hb;
+  p.n_dense = plan.n_dense;
   p.n_splits = plan.n_splits;
   p.P = g.page_size;
   p.log2P = 0;
@@ -1059,13 +1259,8 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
                        stream, p);
   if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
   if (plan.n_splits > 1) {
-    const dim3 grid(static_cast<uint32_t>(groups * 32));
-    if (g.latent_bits == 4)
-      hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(64), 0, stream, p.parts, out, lse, heads, plan.n_hb,
-                         plan.n_splits);
-    else
-      hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(64), 0, stream, p.parts, out, lse, heads, plan.n_hb,
-                         plan.n_splits);
+    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(groups * 32)), dim3(64), 0, stream, p.parts, out,
+                       lse, heads, plan.n_hb, plan.n_splits);
     if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
   }
   return MLA_LOWBIT_OK;

@@ -70,6 +70,7 @@ extern "C" int mla_lowbit_decode_workspace(const mla_lowbit_layout* layout, int3
   if (rc) return rc;
   if (batch < 0 || heads < 1 || heads > mla::kMaxHeads || max_seqlen < 0) return MLA_LOWBIT_ERR_ARG;
   mla::DecodePlan plan = mla::plan_decode(g, batch, heads, max_seqlen);
+  if (!plan.ok) return MLA_LOWBIT_ERR_UNSUPPORTED;
   *bytes = plan.workspace_bytes;
   return MLA_LOWBIT_OK;
 }
