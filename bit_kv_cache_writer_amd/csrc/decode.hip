@@ -22,24 +22,27 @@
 //  1. Scores: codes come out of LDS in the lanes that feed
 //     v_mfma_f32_16x16x32_f16 (M = 16 tokens, N = 16 heads, K = 32 channels;
 //     lane (t, g) holds 8 channels of token t) and are unpacked in registers
-//     to fp16 x = 1 + code/kappa by OR-ing the code into the top of an fp16
-//     mantissa (kappa = 16 for 4-bit codes, 4 for 2-bit codes).  Group scale s
-//     and minimum m are folded after the MFMA:
-//       q.c = sum_g kappa s_g (q_g . x_g) + sum_g (m_g - kappa s_g) Q_g,
+//     by masking alone: a code left in the low mantissa bits of an fp16 with
+//     a zero exponent is the subnormal code * 2^-24 * sigma, sigma the power
+//     of two of its bit position (the matrix cores take fp16 subnormals
+//     exactly).  The query operand carries q / sigma per slot, so the MFMA
+//     sums 2^-24 q_g . code_g; group scale s and minimum m are folded after it:
+//       q.c = 2^24 sum_g s_g (q_g . code_g 2^-24) + sum_g m_g Q_g,
 //     Q_g = sum of the query over group g; the second sum is one more MFMA on
 //     the raw fp16 (scale, min) words.  The positional key's per-(channel,
 //     page) scale/min is folded into a per-page query q' = q s (fp16 hi + lo)
-//     and bias sum_c q_c (m_c - 16 s_c), rebuilt only when the page changes.
+//     against x = 1 + code/16 (the code OR-ed under an fp16 one) and a bias
+//     sum_c q_c (m_c - 16 s_c), rebuilt only when the page changes.
 //  2. Softmax: the four tile maxima meet in LDS; every wave raises the same
-//     running max and publishes fp16 weights P'_g = p s_g per latent group.
-//     Sums of p, of P'_g and of p m_g stay per lane until the end.
+//     running max and publishes fp16 weights P'_g = p s_g / sigma per latent
+//     group.  Sums of p and of p m_g stay per lane until the end.
 //  3. Output: wave w owns latent group w (128 output channels).  Its B operand
 //     comes straight from the four code tiles of the round with
 //     ds_read_b64_tr_b4 (16 tokens of one 4-bit channel, or of a 2-bit channel
-//     pair, per lane) and the same mantissa unpack; A = P'_w.  The output
-//     accumulates sum_j fp16(p_j s_j) x_j; the offsets -kappa sum_j
-//     fp16(p_j s_j) and sum_j p_j m_j are applied at the end -- the same
-//     rounded fp16 products enter both, so they cancel.
+//     pair, per lane) and the same masking unpack; A = P'_w, whose 1/sigma
+//     per token slot cancels the slot's sigma.  The output accumulates
+//     2^-24 sum_j fp16(p_j s_j) code_j; 2^24 and sum_j p_j m_j are applied at
+//     the end.
 // BF16-path workgroup: the same rounds over the protected tokens (sink,
 // recent window and, when the window is shorter than a page, tokens of the
 // unfinished page); their rows are converted to fp16 on their way into an fp16
@@ -67,8 +70,9 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = kDecodeWaves;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStatW = 9;      // per head: sum p, sum P'_g (4), sum p m_g (4)
+constexpr int kStatW = 5;      // per head: sum p, sum p m_g (4)
 constexpr float kPrescale = 1.0f / 256.0f;  // keeps q' and Q_g inside fp16 range
+constexpr float kCodeScale = 16777216.0f;   // 2^24: undoes the subnormal unpack
 constexpr float kNegInf = -INFINITY;
 
 // BF16-path workgroup LDS map (bytes).  x-tile row: 512 fp16 + 16 B pad (260
@@ -97,7 +101,6 @@ constexpr int kPkOffMax = kPkOffP + kPkPBytes;
 constexpr int kPkOffQr = kPkOffMax + kHeadBlock * kWaves * 4;
 constexpr int kPkOffPid = kPkOffQr + kHeadBlock * kRopeDim * 2;
 constexpr int kPackedLds = kPkOffPid + kPageWin * 4;
-static_assert(kWaves * kSlotBytes >= kHeadBlock * kLatentDim * 2, "query rows stage in one slot row");
 
 constexpr int kLdsBytes = kDenseLds > kPackedLds ? kDenseLds : kPackedLds;
 static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per gfx950 CU");
@@ -140,18 +143,18 @@ __device__ inline int col_to_channel(int c) {
 // Constants kept in VGPRs so that shift-and-merge compiles to one v_and_or_b32
 // per pair (a VOP3 instruction cannot encode two literal constants).
 struct UnpackK {
-  uint32_t m4, m2, e;
+  uint32_t m4, e;
 };
 __device__ inline UnpackK unpack_k() {
   UnpackK k;
   asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(k.e));
   k.m4 = 0x03C003C0u;
-  k.m2 = 0x03000300u;
   return k;
 }
 
-// 8 nibbles -> fp16 1 + code/16, slots [n0 n4 n1 n5 n2 n6 n3 n7].
-__device__ inline half8 unpack4(uint32_t w, const UnpackK& k) {
+// 8 nibbles -> fp16 1 + code/16, slots [n0 n4 n1 n5 n2 n6 n3 n7] (the
+// positional-key codes, whose scale/min fold is per channel).
+__device__ inline half8 unpack4_biased(uint32_t w, const UnpackK& k) {
   u32x4 v;
   v[0] = ((w << 6) & k.m4) | k.e;
   v[1] = ((w << 2) & k.m4) | k.e;
@@ -160,22 +163,37 @@ __device__ inline half8 unpack4(uint32_t w, const UnpackK& k) {
   return __builtin_bit_cast(half8, v);
 }
 
-// 8 of the 16 crumbs of w -> fp16 1 + code/4; hi = 0: crumbs [0 8 1 9 2 10 3 11],
-// hi = 1: crumbs [4 12 5 13 6 14 7 15].
-__device__ inline half8 unpack2(uint32_t w, int hi, const UnpackK& k) {
+// Latent-code unpack by masking: slot value = code * 2^-24 * sigma (an fp16
+// subnormal, the code sitting at bit log2(sigma) of a zero-exponent half).
+// 8 nibbles -> slots [n0 n4 n1 n5 n2 n6 n3 n7], sigma = 16 in slots 2, 3, 6, 7.
+__device__ inline half8 unpack4(uint32_t w) {
+  const uint32_t t = w >> 8;
+  const u32x4 v = {w & 0x000F000Fu, w & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u};
+  return __builtin_bit_cast(half8, v);
+}
+
+// 8 of the 16 crumbs of w; hi = 0: crumbs [0 8 1 9 2 10 3 11], sigma 1, 4,
+// 16, 64 per slot pair; hi = 1: crumbs [4 12 5 13 6 14 7 15], sigma 256, 4,
+// 16, 64.
+__device__ inline half8 unpack2(uint32_t w, int hi) {
   u32x4 v;
   if (hi == 0) {
-    v[0] = ((w << 8) & k.m2) | k.e;
-    v[1] = ((w << 6) & k.m2) | k.e;
-    v[2] = ((w << 4) & k.m2) | k.e;
-    v[3] = ((w << 2) & k.m2) | k.e;
+    v = u32x4{w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u};
   } else {
-    v[0] = (w & k.m2) | k.e;
-    v[1] = ((w >> 2) & k.m2) | k.e;
-    v[2] = ((w >> 4) & k.m2) | k.e;
-    v[3] = ((w >> 6) & k.m2) | k.e;
+    const uint32_t t = w >> 8;
+    v = u32x4{w & 0x03000300u, t & 0x000C000Cu, t & 0x00300030u, t & 0x00C000C0u};
   }
   return __builtin_bit_cast(half8, v);
+}
+
+// sigma of slot sl of latent chunk d (the unpacks above).
+template <int BITS>
+__device__ constexpr float slot_sigma(int d, int sl) {
+  if constexpr (BITS == 4) {
+    return (sl & 2) ? 16.f : 1.f;
+  } else {
+    return (sl >> 1) == 0 ? ((d & 1) ? 256.f : 1.f) : ((sl >> 1) == 1 ? 4.f : ((sl >> 1) == 2 ? 16.f : 64.f));
+  }
 }
 
 __device__ inline float bf16f(uint32_t h16) { return __uint_as_float(h16 << 16); }
@@ -235,83 +253,90 @@ struct QueryOps {
   half8 meta;       // (scale, min) slots of the metadata MFMA, prescaled
 };
 
-// Query rows of the 16 heads of a head block, staged in LDS as [head][1024 B]
-// (q_lat) plus [head][128 B] (q_rope): wave w fetches latent group w of every
-// head (lane: head lane / 4, 32 channels), wave 0 also the q_rope rows.
-// Heads past the last one read a copy of the last head.
+// Query staging.  Wave w fetches latent group w of the 16 heads of a head
+// block straight into the operand layout (lane (h, gq): channels
+// 128 w + 32 gq .. + 31 of head h) and wave 0 also the q_rope rows (lane:
+// head lane / 4, 16 channels).  Heads past the last one read a copy of the
+// last head.
 struct QueryRows {
   u32x4 lat[4], rope[2];
 };
 
 __device__ inline void fetch_query(QueryRows& qr, const DecodeParams& p, int b, int hb, int wave, int lane) {
-  const int h = hb * kHeadBlock + (lane >> 2), part = lane & 3;
+  const int n16 = lane & 15, gq = lane >> 4;
+  const int h = hb * kHeadBlock + n16;
   const int hc = h < p.heads ? h : p.heads - 1;
-  const uint16_t* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + hc) * kLatentDim + 128 * wave + 32 * part;
+  const uint16_t* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + hc) * kLatentDim + 128 * wave + 32 * gq;
 #pragma unroll
   for (int u = 0; u < 4; ++u) qr.lat[u] = ldg<u32x4>(ql + 8 * u);
   if (wave == 0) {
-    const uint16_t* qp = p.q_rope + (static_cast<int64_t>(b) * p.heads + hc) * kRopeDim + 16 * part;
+    const int hr = hb * kHeadBlock + (lane >> 2);
+    const int hrc = hr < p.heads ? hr : p.heads - 1;
+    const uint16_t* qp = p.q_rope + (static_cast<int64_t>(b) * p.heads + hrc) * kRopeDim + 16 * (lane & 3);
     qr.rope[0] = ldg<u32x4>(qp);
     qr.rope[1] = ldg<u32x4>(qp + 8);
   }
 }
 
-__device__ inline void store_query(const QueryRows& qr, uint8_t* ql_lds, uint8_t* qr_lds, int wave, int lane) {
-  const int part = lane & 3;
-  uint8_t* row = ql_lds + (lane >> 2) * 1024 + 2 * (128 * wave + 32 * part);
+// LDS image of the converted query: [group][chunk][lane] fp16 x 8 operands,
+// then [head][group] fp32 group sums.
+constexpr int kQopsSums = 4 * 4 * 64 * 16;
+constexpr int kQopsBytes = kQopsSums + kHeadBlock * 4 * 4;
+
+// Wave w converts its latent group: fp16 operands in the unpack's slot order
+// (divided by the slot's sigma for the masking unpack when kSigma) and Q_w =
+// sum of the group's 128 channels, both into the LDS image; wave 0 also
+// stores the q_rope rows as [head][128 B].
+template <int BITS, bool kSigma>
+__device__ inline void publish_query(const QueryRows& qr, uint8_t* qops, uint8_t* qr_lds, int wave, int lane) {
+  const int n16 = lane & 15, gq = lane >> 4;
+  float v[32];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) lds_st<u32x4>(row + 16 * u, qr.lat[u]);
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * u + 2 * e] = bf16f(qr.lat[u][e] & 0xFFFFu);
+      v[8 * u + 2 * e + 1] = bf16f(qr.lat[u][e] >> 16);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) s += v[c];
+  const float qsum = row_allsum(s);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    half8 x;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl)
+      x[sl] = static_cast<_Float16>(kSigma ? v[chan_off<BITS>(d, sl)] * (1.f / slot_sigma<BITS>(d, sl))
+                                           : v[chan_off<BITS>(d, sl)]);
+    lds_st<half8>(qops + ((wave * 4 + d) * 64 + lane) * 16, x);
+  }
+  if (gq == 0) lds_st<float>(qops + kQopsSums + (n16 * 4 + wave) * 4, qsum);
   if (wave == 0) {
-    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * part, qr.rope[0]);
-    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * part + 16, qr.rope[1]);
+    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * (lane & 3), qr.rope[0]);
+    lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * (lane & 3) + 16, qr.rope[1]);
   }
 }
 
-__device__ inline void stage_query(uint8_t* ql_lds, uint8_t* qr_lds, const DecodeParams& p, int b, int hb, int wave,
-                                   int lane) {
-  QueryRows qr;
-  fetch_query(qr, p, b, hb, wave, lane);
-  store_query(qr, ql_lds, qr_lds, wave, lane);
-}
-
-// MFMA operands of the query from the staged rows: lane (h, gq) takes channels
-// 128 i + 32 gq .. + 31 of head h, in the unpack's slot order; Q_g = sum of
-// the query over group g enters the metadata operand.
+// MFMA operands of the whole query from the LDS image; Q_g enters the
+// metadata operand (min slots; the scale slots stay zero).
 template <int BITS>
-__device__ inline void load_query(QueryOps<BITS>& q, const uint8_t* ql_lds, int n16, int gq) {
-  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
-  float qg[4];
+__device__ inline void load_query(QueryOps<BITS>& q, const uint8_t* qops, int lane) {
+  const int n16 = lane & 15, gq = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint8_t* row = ql_lds + n16 * 1024 + 2 * (128 * i + 32 * gq);
-    float v[32];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 w = lds_ld<u32x4>(row + 16 * u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * u + 2 * e] = bf16f(w[e] & 0xFFFFu);
-        v[8 * u + 2 * e + 1] = bf16f(w[e] >> 16);
-      }
-    }
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) s += v[c];
-    qg[i] = row_allsum(s);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl) q.lat[i][d][sl] = static_cast<_Float16>(v[chan_off<BITS>(d, sl)]);
-    }
+    for (int d = 0; d < 4; ++d) q.lat[i][d] = lds_ld<half8>(qops + ((i * 4 + d) * 64 + lane) * 16);
   }
+  const f32x4 qg = lds_ld<f32x4>(qops + kQopsSums + n16 * 16);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float a = -kappa * qg[i] * kPrescale, c = qg[i] * kPrescale;
-    const _Float16 ah = static_cast<_Float16>(a), ch = static_cast<_Float16>(c);
-    const _Float16 al = static_cast<_Float16>(a - static_cast<float>(ah));
+    const float c = qg[i] * kPrescale;
+    const _Float16 ch = static_cast<_Float16>(c);
     const _Float16 cl = static_cast<_Float16>(c - static_cast<float>(ch));
     const _Float16 z = static_cast<_Float16>(0.f);
-    q.meta[2 * i] = gq == 0 ? ah : (gq == 1 ? al : z);
+    q.meta[2 * i] = z;
     q.meta[2 * i + 1] = gq == 0 ? ch : (gq == 1 ? cl : z);
   }
 }
@@ -445,7 +470,6 @@ __device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BIT
                               const uint8_t* slot, bool new_page, const uint8_t* qr_row, int j0, int vlo, int vhi,
                               int n16, int gq, float c_log2) {
   using G = TileGeom<BITS>;
-  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
   const UnpackK uk = unpack_k();
   uint32_t lat[BITS == 4 ? 16 : 8];
 #pragma unroll
@@ -470,13 +494,13 @@ __device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BIT
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const half8 x = BITS == 4 ? unpack4(lat[4 * i + d], uk) : unpack2(lat[2 * i + (d >> 1)], d & 1, uk);
+      const half8 x = BITS == 4 ? unpack4(lat[4 * i + d]) : unpack2(lat[2 * i + (d >> 1)], d & 1);
       acc[i] = mfma(x, q.lat[i][d], acc[i]);
     }
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const half8 xr = unpack4(rope[e], uk);
+    const half8 xr = unpack4_biased(rope[e], uk);
     acc[4] = mfma(xr, ro.hi[e], acc[4]);
     acc[4] = mfma(xr, ro.lo[e], acc[4]);
   }
@@ -492,7 +516,7 @@ __device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BIT
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = j0 + 4 * gq + r;
-    const float z = fmaf(v[r], kappa, fmaf(acc[4][r], 256.f, ro.bias));
+    const float z = fmaf(v[r], kCodeScale, fmaf(acc[4][r], 256.f, ro.bias));
     sc[r] = (t >= vlo && t < vhi) ? z * c_log2 : kNegInf;
   }
 }
@@ -501,52 +525,43 @@ __device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BIT
 // tokens 8 gq .. 8 gq + 7 of the K block (tiles 2 kb, 2 kb + 1), fp16.
 __device__ inline int p_entry(int kb, int g, int gq, int h) { return (((kb * 4 + g) * 4 + gq) * kHeadBlock + h) * 16; }
 
-// Weights of this wave's packed tile: P'_g = fp16(fp16(p) s_g) into the P'
-// entries its tokens fall in; adds this lane's sums of p, of the fp16 P'_g
-// and of p m_g to st.
+// Weights of this wave's packed tile: P'_g = fp16(fp16(fp16(p) / sigma) s_g) into
+// the P' entries its tokens fall in (tokens 4 gq + 2, 4 gq + 3 land in the
+// output unpack's sigma = 16 slots); adds this lane's sums of p and of p m_g
+// to st.
 __device__ inline void packed_weights(const float (&pr)[4], const u32x4 (&md)[4], uint8_t* pbase,
                                       float (&st)[kStatW], int wave, int n16, int gq) {
   const half2 ph[2] = {half2{static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1])},
                        half2{static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])}};
   st[0] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  const half2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  const half2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+  const half2 pw[2] = {ph[0], ph[1] * sixteenth};
   const int at = 8 * (gq & 1);  // tokens 4 gq .. 4 gq + 3 of the tile
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     half4 pa;
-    float cs = st[1 + g], ms = st[5 + g];
+    float ms = st[1 + g];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const uint32_t w0 = md[2 * k][g], w1 = md[2 * k + 1][g];
       const half2 s2 = {__builtin_bit_cast(half2, w0)[0], __builtin_bit_cast(half2, w1)[0]};
       const half2 m2 = {__builtin_bit_cast(half2, w0)[1], __builtin_bit_cast(half2, w1)[1]};
-      const half2 ps = ph[k] * s2;
-      cs = __builtin_amdgcn_fdot2(ps, ones, cs, false);
+      const half2 ps = pw[k] * s2;
       ms = __builtin_amdgcn_fdot2(ph[k], m2, ms, false);
       pa[2 * k] = ps[0];
       pa[2 * k + 1] = ps[1];
     }
     lds_st<half4>(pbase + p_entry(wave >> 1, g, 2 * (wave & 1) + (gq >> 1), n16) + at, pa);
-    st[1 + g] = cs;
-    st[5 + g] = ms;
+    st[1 + g] = ms;
   }
 }
 
-// 8 crumbs (parity par of 8 nibbles) of w -> fp16 1 + code/4, slots
-// [n0 n4 n1 n5 n2 n6 n3 n7] of the nibbles.
-__device__ inline half8 unpack2_pairs(uint32_t w, int par, const UnpackK& k) {
-  u32x4 v;
-  if (par == 0) {
-    v[0] = ((w << 8) & k.m2) | k.e;
-    v[1] = ((w << 4) & k.m2) | k.e;
-    v[2] = (w & k.m2) | k.e;
-    v[3] = ((w >> 4) & k.m2) | k.e;
-  } else {
-    v[0] = ((w << 6) & k.m2) | k.e;
-    v[1] = ((w << 2) & k.m2) | k.e;
-    v[2] = ((w >> 2) & k.m2) | k.e;
-    v[3] = ((w >> 6) & k.m2) | k.e;
-  }
+// 8 crumbs (parity par of 8 nibbles) of w by masking, slots
+// [n0 n4 n1 n5 n2 n6 n3 n7] of the nibbles, sigma = 16 in slots 2, 3, 6, 7
+// (as unpack4).
+__device__ inline half8 unpack2_pairs(uint32_t w, int par) {
+  const uint32_t u = par == 0 ? w : w >> 2, t = u >> 8;
+  const u32x4 v = {u & 0x00030003u, u & 0x00300030u, t & 0x00030003u, t & 0x00300030u};
   return __builtin_bit_cast(half8, v);
 }
 
@@ -561,7 +576,6 @@ __device__ inline half8 unpack2_pairs(uint32_t w, int par, const UnpackK& k) {
 // 2 n16 + par.
 template <int BITS>
 __device__ inline void packed_pv(f32x4 (&o)[8], const uint8_t* smem, int s, int wave, int n16, int gq) {
-  const UnpackK uk = unpack_k();
   const half8 pa0 = lds_ld<half8>(smem + kPkOffP + p_entry(0, wave, gq, n16));
   const half8 pa1 = lds_ld<half8>(smem + kPkOffP + p_entry(1, wave, gq, n16));
   const int j = n16 & 7;
@@ -593,8 +607,8 @@ __device__ inline void packed_pv(f32x4 (&o)[8], const uint8_t* smem, int s, int 
         : "memory");
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      o[kk] = mfma(pa0, unpack4(static_cast<uint32_t>(r[kk][0]), uk), o[kk]);
-      o[kk] = mfma(pa1, unpack4(static_cast<uint32_t>(r[kk][1]), uk), o[kk]);
+      o[kk] = mfma(pa0, unpack4(static_cast<uint32_t>(r[kk][0])), o[kk]);
+      o[kk] = mfma(pa1, unpack4(static_cast<uint32_t>(r[kk][1])), o[kk]);
     }
   } else {
     uint32_t a[2];
@@ -615,8 +629,8 @@ __device__ inline void packed_pv(f32x4 (&o)[8], const uint8_t* smem, int s, int 
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int par = 0; par < 2; ++par) {
-        o[2 * c + par] = mfma(pa0, unpack2_pairs(static_cast<uint32_t>(r[c][0]), par, uk), o[2 * c + par]);
-        o[2 * c + par] = mfma(pa1, unpack2_pairs(static_cast<uint32_t>(r[c][1]), par, uk), o[2 * c + par]);
+        o[2 * c + par] = mfma(pa0, unpack2_pairs(static_cast<uint32_t>(r[c][0]), par), o[2 * c + par]);
+        o[2 * c + par] = mfma(pa1, unpack2_pairs(static_cast<uint32_t>(r[c][1]), par), o[2 * c + par]);
       }
     }
   }
@@ -849,19 +863,24 @@ __device__ void dense_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], co
   uint8_t* const p_own = smem + kOffP + wave * kPTile;
   float* const smax = reinterpret_cast<float*>(smem + kOffMax);
   const uint8_t* const qr_row = smem + kOffQr + n16 * 128;
-  uint8_t* const ql_stage = smem + kOffX;  // query rows, until round 0 writes x tiles
+  uint8_t* const qops = smem + kOffX;  // converted query, until round 0 writes x tiles
 
-  stage_query(ql_stage, smem + kOffQr, p, cx.b, cx.hb, wave, lane);
+  {
+    QueryRows qrows;
+    fetch_query(qrows, p, cx.b, cx.hb, wave, lane);
+    publish_query<BITS, false>(qrows, qops, smem + kOffQr, wave, lane);
+  }
+  static_assert(kQopsBytes <= kWaves * kXTile, "the converted query fits the x tiles");
   const int n_dense = sr.lo_p + (sr.L - sr.hi_p);
   const int D = (n_dense + kTile - 1) / kTile;
   const int per = (D + p.n_dense - 1) / p.n_dense;
   const int i0 = min(D, ds * per), i1 = min(D, i0 + per);
   const int rounds = (i1 - i0 + kWaves - 1) / kWaves;
   const int my0 = i0 + wave * rounds, my1 = min(i1, my0 + rounds);
-  lds_barrier();  // query rows staged
+  lds_barrier();  // query converted
   QueryOps<BITS> q;
-  load_query<BITS>(q, ql_stage, n16, gq);
-  lds_barrier();  // query rows read: the x tiles may be written
+  load_query<BITS>(q, qops, lane);
+  lds_barrier();  // query read: the x tiles may be written
   if (my0 >= my1) {  // a wave without tiles still feeds zeros to the output MFMAs
     for (int off = 16 * lane; off < kXTile; off += 64 * 16) lds_st<u32x4>(xt_own + off, u32x4{0, 0, 0, 0});
   }
@@ -933,7 +952,8 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   float* const smax = reinterpret_cast<float*>(smem + kPkOffMax);
   int* const s_pid = reinterpret_cast<int*>(smem + kPkOffPid);
   const uint8_t* const qr_row = smem + kPkOffQr + n16 * 128;
-  uint8_t* const ql_stage = smem + kPkOffStage + 2 * kWaves * kSlotBytes;  // slot 2 of every wave
+  uint8_t* const qops = smem + kPkOffStage + 2 * kWaves * kSlotBytes;  // slot 2 of every wave
+  static_assert(kQopsBytes <= kWaves * kSlotBytes, "the converted query fits one slot row");
   auto slot_ptr = [&](int s, int w) { return smem + kPkOffStage + (s * kWaves + w) * kSlotBytes; };
 
   QueryRows qrows;
@@ -960,13 +980,12 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     const int k = threadIdx.x + i * kThreads;
     pid[i] = k < n_pg ? bt_row[k] : -1;
   }
-  store_query(qrows, ql_stage, smem + kPkOffQr, wave, lane);
 #pragma unroll
   for (int i = 0; i < kPidPerThread; ++i) {
     const int k = threadIdx.x + i * kThreads;
     if (k < n_pg) s_pid[k] = pid[i];
   }
-  lds_barrier();  // query rows and page ids staged
+  lds_barrier();  // page ids staged
   auto page_of_tile = [&](int it, int& pidx, int& slot0) -> const uint8_t* {
     const int j0 = (t_lo + it) * kTile;
     pidx = j0 >> p.log2P;
@@ -984,9 +1003,12 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   };
   if (my0 < my1) issue(my0, 0);
   if (my0 + 1 < my1) issue(my0 + 1, 1);
+  // the query is converted while the first tiles are in flight; slot 2,
+  // which holds it, is first filled after the round-0 barrier
+  publish_query<BITS, true>(qrows, qops, smem + kPkOffQr, wave, lane);
+  lds_barrier();  // query converted
   QueryOps<BITS> q;
-  load_query<BITS>(q, ql_stage, n16, gq);
-  lds_barrier();  // query rows read: slot 2 may be filled
+  load_query<BITS>(q, qops, lane);
 
   float m_run = kNegInf;
   RopeOps ro;
@@ -1044,7 +1066,8 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
 template <int BITS, bool kPackedMap>
 __device__ void finish(const DecodeParams& p, uint8_t* sums_lds, const f32x4 (&o)[8], const float (&st)[kStatW],
                        const float (&m_o)[4], const WgCtx& cx) {
-  constexpr float kappa = BITS == 4 ? 16.f : 4.f;
+  // packed: output MFMAs summed 2^-24 fp16(p s) code; BF16 path: p / kappa x
+  constexpr float out_scale = kPackedMap ? kCodeScale : (BITS == 4 ? 16.f : 4.f);
   const int wave = cx.wave, n16 = cx.n16, gq = cx.gq;
   float* const sfin = reinterpret_cast<float*>(sums_lds);
 #pragma unroll
@@ -1059,13 +1082,12 @@ __device__ void finish(const DecodeParams& p, uint8_t* sums_lds, const f32x4 (&o
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int hh = 4 * gq + rr, hg = cx.hb * kHeadBlock + hh;
-    float l = 0.f, c = 0.f, m = 0.f;
+    float l = 0.f, m = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float* f = sfin + (w * kHeadBlock + hh) * kStatW;
       l += f[0];
-      c += f[1 + wave];
-      m += f[5 + wave];
+      m += f[1 + wave];
     }
     l_h[rr] = l;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1076,7 +1098,7 @@ __device__ void finish(const DecodeParams& p, uint8_t* sums_lds, const f32x4 (&o
         ch = BITS == 4 ? 128 * wave + 16 * kk + n16 : 128 * wave + 32 * (kk >> 1) + 2 * n16 + (kk & 1);
       else
         ch = col_to_channel<BITS>(128 * wave + 16 * kk + n16);
-      const float v = fmaf(kappa, o[kk][rr] - c, m);
+      const float v = fmaf(out_scale, o[kk][rr], m);
       if (direct) {
         if (hg < p.heads) p.out[(static_cast<int64_t>(cx.b) * p.heads + hg) * kLatentDim + ch] = v * inv;
       } else {
