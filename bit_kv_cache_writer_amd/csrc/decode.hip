@@ -30,9 +30,9 @@
 //       q.c = 2^24 sum_g s_g (q_g . code_g 2^-24) + sum_g m_g Q_g,
 //     Q_g = sum of the query over group g; the second sum is one more MFMA on
 //     the raw fp16 (scale, min) words.  The positional key's per-(channel,
-//     page) scale/min is folded into a per-page query q' = q s (fp16 hi + lo)
-//     against x = 1 + code/16 (the code OR-ed under an fp16 one) and a bias
-//     sum_c q_c (m_c - 16 s_c), rebuilt only when the page changes.
+//     page) scale/min is folded into a per-page query q' = q s / sigma
+//     against the same masked codes, and a bias sum_c q_c m_c, rebuilt only
+//     when the page changes.
 //  2. Softmax: the four tile maxima meet in LDS; every wave raises the same
 //     running max and publishes fp16 weights P'_g = p s_g / sigma per latent
 //     group.  Sums of p and of p m_g stay per lane until the end.
@@ -106,6 +106,9 @@ constexpr int kLdsBytes = kDenseLds > kPackedLds ? kDenseLds : kPackedLds;
 static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per gfx950 CU");
 static_assert(kWaves * kHeadBlock * kStatW * 4 <= kWaves * kPTile, "final sums fit the P' area");
 static_assert(kWaves * kHeadBlock * kStatW * 4 <= kPkPBytes, "final sums fit the P' area");
+static_assert(kPartRowBytes <= kWaves * kXTile && kPartRowBytes <= kSlots * kWaves * kSlotBytes,
+              "a partial's fp16 rows stage in the tile area");
+static_assert(kPartRowBytes % (16 * kThreads) == 0, "the staged rows leave in whole 16-byte passes");
 
 struct DecodeParams {
   const uint16_t* q_lat;
@@ -116,7 +119,7 @@ struct DecodeParams {
   const uint16_t* sink;
   const uint16_t* ring;
   const uint16_t* tail;
-  float* parts;
+  uint8_t* parts;
   float* out;
   float* lse;
   int32_t batch, heads, max_pages, num_pool_pages, max_seqlen;
@@ -138,29 +141,6 @@ __device__ constexpr int chan_off(int d, int s) {
 template <int BITS>
 __device__ inline int col_to_channel(int c) {
   return (c & ~31) + chan_off<BITS>((c >> 3) & 3, c & 7);
-}
-
-// Constants kept in VGPRs so that shift-and-merge compiles to one v_and_or_b32
-// per pair (a VOP3 instruction cannot encode two literal constants).
-struct UnpackK {
-  uint32_t m4, e;
-};
-__device__ inline UnpackK unpack_k() {
-  UnpackK k;
-  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(k.e));
-  k.m4 = 0x03C003C0u;
-  return k;
-}
-
-// 8 nibbles -> fp16 1 + code/16, slots [n0 n4 n1 n5 n2 n6 n3 n7] (the
-// positional-key codes, whose scale/min fold is per channel).
-__device__ inline half8 unpack4_biased(uint32_t w, const UnpackK& k) {
-  u32x4 v;
-  v[0] = ((w << 6) & k.m4) | k.e;
-  v[1] = ((w << 2) & k.m4) | k.e;
-  v[2] = ((w >> 2) & k.m4) | k.e;
-  v[3] = ((w >> 6) & k.m4) | k.e;
-  return __builtin_bit_cast(half8, v);
 }
 
 // Latent-code unpack by masking: slot value = code * 2^-24 * sigma (an fp16
@@ -341,8 +321,10 @@ __device__ inline void load_query(QueryOps<BITS>& q, const uint8_t* qops, int la
   }
 }
 
-// Per-page positional-key operands for channels 16*gq + 8e + slot order:
-// q' = q s * 16 / 256 as fp16 hi + lo, and bias sum_c q_c (m_c - 16 s_c).
+// Per-page positional-key operands for channels 16*gq + 8e + slot order
+// (masking unpack, as the latent codes): q' = q s / sigma, prescaled, as fp16
+// hi + lo (a bf16 times an fp16 needs more bits than one fp16 holds);
+// bias = sum_c q_c m_c over the lane row's 64 channels.
 struct RopeOps {
   half8 hi[2], lo[2];
   float bias;
@@ -375,14 +357,14 @@ __device__ inline void rope_ops(RopeOps& r, const uint8_t* qr_row, const uint8_t
   }
   float bias = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) bias += qv[c] * (mn[c] - 16.f * sc[c]);
+  for (int c = 0; c < 16; ++c) bias = fmaf(qv[c], mn[c], bias);
   r.bias = row_allsum(bias);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
       const int c = 8 * e + chan_off<4>(0, sl);
-      const float v = qv[c] * sc[c] * (16.f * kPrescale);
+      const float v = qv[c] * sc[c] * (kPrescale / slot_sigma<4>(0, sl));
       const _Float16 vh = static_cast<_Float16>(v);
       r.hi[e][sl] = vh;
       r.lo[e][sl] = static_cast<_Float16>(v - static_cast<float>(vh));
@@ -462,6 +444,12 @@ __device__ inline void wait_tiles_after(int after) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Score from the MFMA sums: latent 2^-24 sum_g s_g q_g.code_g (v), metadata
+// kPrescale sum_g m_g Q_g (meta), positional 2^-24 kPrescale q s.code (rope).
+__device__ inline float score_of(float v, float meta, float rope, float bias) {
+  return fmaf(fmaf(rope, 1.f / kPrescale, v), kCodeScale, fmaf(meta, 1.f / kPrescale, bias));
+}
+
 // Scores (log2 domain) of one packed tile (tokens j0 .. j0+15 of a complete
 // page, valid in [vlo, vhi)) from its LDS slot: lane (h, gq) gets tokens
 // 4 gq + r of head h.  md[r] = the metadata words of token 4 gq + r.
@@ -470,7 +458,6 @@ __device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BIT
                               const uint8_t* slot, bool new_page, const uint8_t* qr_row, int j0, int vlo, int vhi,
                               int n16, int gq, float c_log2) {
   using G = TileGeom<BITS>;
-  const UnpackK uk = unpack_k();
   uint32_t lat[BITS == 4 ? 16 : 8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -487,9 +474,9 @@ __device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BIT
   const u32x2 rope = lds_ld<u32x2>(slot + G::kOffRope + n16 * kRopeRowBytes + 8 * gq);
   const u32x4 ma = lds_ld<u32x4>(slot + G::kOffMeta + 16 * n16);
   if (new_page) rope_ops(ro, qr_row, slot + G::kOffRMeta, gq);
-  f32x4 acc[5];
+  f32x4 acc[6];
 #pragma unroll
-  for (int g = 0; g < 5; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < 6; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
@@ -500,9 +487,9 @@ __device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BIT
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const half8 xr = unpack4_biased(rope[e], uk);
-    acc[4] = mfma(xr, ro.hi[e], acc[4]);
-    acc[4] = mfma(xr, ro.lo[e], acc[4]);
+    const half8 xr = unpack4(rope[e]);
+    acc[5] = mfma(xr, ro.hi[e], acc[5]);
+    acc[5] = mfma(xr, ro.lo[e], acc[5]);
   }
   acc[4] = mfma(__builtin_bit_cast(half8, ma), q.meta, acc[4]);
 #pragma unroll
@@ -513,10 +500,15 @@ __device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BIT
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = fmaf(lo_f16(md[r][g]), acc[g][r], v[r]);
   }
+  if (j0 >= vlo && j0 + kTile <= vhi) {  // whole tile valid
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = score_of(v[r], acc[4][r], acc[5][r], ro.bias) * c_log2;
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = j0 + 4 * gq + r;
-    const float z = fmaf(v[r], kCodeScale, fmaf(acc[4][r], 256.f, ro.bias));
+    const float z = score_of(v[r], acc[4][r], acc[5][r], ro.bias);
     sc[r] = (t >= vlo && t < vhi) ? z * c_log2 : kNegInf;
   }
 }
@@ -606,10 +598,9 @@ __device__ inline void packed_pv(f32x4 (&o)[8], const uint8_t* smem, int s, int 
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      o[kk] = mfma(pa0, unpack4(static_cast<uint32_t>(r[kk][0])), o[kk]);
-      o[kk] = mfma(pa1, unpack4(static_cast<uint32_t>(r[kk][1])), o[kk]);
-    }
+    for (int kk = 0; kk < 8; ++kk) o[kk] = mfma(pa0, unpack4(static_cast<uint32_t>(r[kk][0])), o[kk]);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) o[kk] = mfma(pa1, unpack4(static_cast<uint32_t>(r[kk][1])), o[kk]);
   } else {
     uint32_t a[2];
 #pragma unroll
@@ -628,10 +619,14 @@ __device__ inline void packed_pv(f32x4 (&o)[8], const uint8_t* smem, int s, int 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int par = 0; par < 2; ++par) {
+      for (int par = 0; par < 2; ++par)
         o[2 * c + par] = mfma(pa0, unpack2_pairs(static_cast<uint32_t>(r[c][0]), par), o[2 * c + par]);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
         o[2 * c + par] = mfma(pa1, unpack2_pairs(static_cast<uint32_t>(r[c][1]), par), o[2 * c + par]);
-      }
     }
   }
 }
@@ -826,24 +821,49 @@ struct WgCtx {
 // Common round step 2 bookkeeping: the tile maxima of the four waves meet in
 // LDS (smax [head][wave]); returns the rescale factor of head n16 (score
 // layout) and updates m_run, and the factors ah of heads 4 gq + r (output
-// layout) and m_o.
-__device__ inline float raise_max(float& m_run, float (&m_o)[4], float (&ah)[4], const float* smax, int n16, int gq) {
+// layout) and m_o.  The reference max only moves when a tile max exceeds it
+// by more than kMaxSlack (log2 units): weights stay below 2^kMaxSlack, and
+// most rounds keep every factor at exactly 1 so that the rescale is skipped.
+// Both layouts apply the same rule to the same maxima, so they agree.
+constexpr float kMaxSlack = 8.f;
+__device__ inline float lazy_max(float m, float tile_max) { return tile_max > m + kMaxSlack ? tile_max : m; }
+
+// 2^x on the transcendental unit; results below the fp32 normal range flush
+// to zero, which only drops softmax weights under 2^-126.
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Every head of the wave keeps its max (all factors 1) unless `raised`; the
+// output-layout maxima are only touched then.
+__device__ inline float raise_max(float& m_run, float (&m_o)[4], float (&ah)[4], bool& raised, const float* smax,
+                                  int n16, int gq) {
   const f32x4 mv = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + n16 * kWaves));
-  const float rmax = fmaxf(m_run, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
-  const float alpha = m_run == kNegInf ? 0.f : exp2f(m_run - rmax);
+  const float rmax = lazy_max(m_run, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+  raised = __any(rmax != m_run);
+  const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - rmax);
   m_run = rmax;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const f32x4 mo = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + (4 * gq + rr) * kWaves));
-    const float ro = fmaxf(m_o[rr], fmaxf(fmaxf(mo[0], mo[1]), fmaxf(mo[2], mo[3])));
-    ah[rr] = m_o[rr] == kNegInf ? 0.f : exp2f(m_o[rr] - ro);
-    m_o[rr] = ro;
+  for (int rr = 0; rr < 4; ++rr) ah[rr] = 1.f;
+  if (raised) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x4 mo = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + (4 * gq + rr) * kWaves));
+      const float ro = lazy_max(m_o[rr], fmaxf(fmaxf(mo[0], mo[1]), fmaxf(mo[2], mo[3])));
+      ah[rr] = m_o[rr] == kNegInf ? 0.f : fast_exp2(m_o[rr] - ro);
+      m_o[rr] = ro;
+    }
   }
   return alpha;
 }
 
-__device__ inline void rescale_out(f32x4 (&o)[8], const float (&ah)[4]) {
-  if (__any(ah[0] != 1.f || ah[1] != 1.f || ah[2] != 1.f || ah[3] != 1.f)) {
+__device__ inline void rescale_stats(float (&st)[kStatW], float alpha, bool raised) {
+  if (raised) {
+#pragma unroll
+    for (int k = 0; k < kStatW; ++k) st[k] *= alpha;
+  }
+}
+
+__device__ inline void rescale_out(f32x4 (&o)[8], const float (&ah)[4], bool raised) {
+  if (raised) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
 #pragma unroll
@@ -895,14 +915,14 @@ __device__ void dense_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], co
     lds_barrier();
 
     float ah[4];
-    const float alpha = raise_max(m_run, m_o, ah, smax, n16, gq);
-#pragma unroll
-    for (int k = 0; k < kStatW; ++k) st[k] *= alpha;
+    bool raised;
+    const float alpha = raise_max(m_run, m_o, ah, raised, smax, n16, gq);
+    rescale_stats(st, alpha, raised);
     half4 pa = {};
     if (has) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float pr = sc[k] == kNegInf ? 0.f : exp2f(sc[k] - m_run);
+        const float pr = sc[k] == kNegInf ? 0.f : fast_exp2(sc[k] - m_run);
         st[0] += pr;
         pa[k] = static_cast<_Float16>(pr * (1.f / kappa));
       }
@@ -913,7 +933,7 @@ __device__ void dense_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], co
 
     // output of latent group `wave`, tiles in pairs: A slots 0-3 tile t
     // (tokens 4 gq + j), slots 4-7 tile t + 1
-    rescale_out(o, ah);
+    rescale_out(o, ah, raised);
 #pragma unroll
     for (int t = 0; t < kWaves; t += 2) {
       const half4 p0 = lds_ld<half4>(smem + kOffP + t * kPTile + wave * 512 + 8 * lane);
@@ -1040,13 +1060,13 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     // B: next loads, softmax of round r
     if (it + 2 < my1) issue(it + 2, (r + 2) % kSlots);
     float ah[4];
-    const float alpha = raise_max(m_run, m_o, ah, smax, n16, gq);
-#pragma unroll
-    for (int k = 0; k < kStatW; ++k) st[k] *= alpha;
+    bool raised;
+    const float alpha = raise_max(m_run, m_o, ah, raised, smax, n16, gq);
+    rescale_stats(st, alpha, raised);
     if (has) {
       float pr[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) pr[k] = sc[k] == kNegInf ? 0.f : exp2f(sc[k] - m_run);
+      for (int k = 0; k < 4; ++k) pr[k] = sc[k] == kNegInf ? 0.f : fast_exp2(sc[k] - m_run);
       packed_weights(pr, md, smem + kPkOffP, st, wave, n16, gq);
     } else {  // no tile: zero weights (the slot's stale codes unpack to finite values)
 #pragma unroll
@@ -1054,7 +1074,7 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
         lds_st<u32x2>(smem + kPkOffP + p_entry(wave >> 1, g, 2 * (wave & 1) + (gq >> 1), n16) + 8 * (gq & 1),
                       u32x2{0, 0});
     }
-    rescale_out(o, ah);
+    rescale_out(o, ah, raised);
     lds_barrier();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no direct load outlives the workgroup
@@ -1064,8 +1084,8 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
 // one split, the normalized output and lse) is written in natural channel
 // order.  chan(kk, n16) maps an accumulator column to its latent channel.
 template <int BITS, bool kPackedMap>
-__device__ void finish(const DecodeParams& p, uint8_t* sums_lds, const f32x4 (&o)[8], const float (&st)[kStatW],
-                       const float (&m_o)[4], const WgCtx& cx) {
+__device__ void finish(const DecodeParams& p, uint8_t* sums_lds, uint8_t* stage, const f32x4 (&o)[8],
+                       const float (&st)[kStatW], const float (&m_o)[4], const WgCtx& cx) {
   // packed: output MFMAs summed 2^-24 fp16(p s) code; BF16 path: p / kappa x
   constexpr float out_scale = kPackedMap ? kCodeScale : (BITS == 4 ? 16.f : 4.f);
   const int wave = cx.wave, n16 = cx.n16, gq = cx.gq;
@@ -1077,7 +1097,7 @@ __device__ void finish(const DecodeParams& p, uint8_t* sums_lds, const f32x4 (&o
   }
   __syncthreads();
   const bool direct = p.n_splits == 1;
-  float* part = p.parts + (static_cast<int64_t>(cx.grp) * p.n_splits + cx.split) * kPartFloats;
+  uint8_t* part = p.parts + (static_cast<int64_t>(cx.grp) * p.n_splits + cx.split) * kPartBytes;
   float l_h[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -1098,12 +1118,20 @@ __device__ void finish(const DecodeParams& p, uint8_t* sums_lds, const f32x4 (&o
         ch = BITS == 4 ? 128 * wave + 16 * kk + n16 : 128 * wave + 32 * (kk >> 1) + 2 * n16 + (kk & 1);
       else
         ch = col_to_channel<BITS>(128 * wave + 16 * kk + n16);
-      const float v = fmaf(out_scale, o[kk][rr], m);
+      const float v = fmaf(out_scale, o[kk][rr], m) * inv;
       if (direct) {
-        if (hg < p.heads) p.out[(static_cast<int64_t>(cx.b) * p.heads + hg) * kLatentDim + ch] = v * inv;
+        if (hg < p.heads) p.out[(static_cast<int64_t>(cx.b) * p.heads + hg) * kLatentDim + ch] = v;
       } else {
-        part[hh * kLatentDim + ch] = v;
+        lds_st<_Float16>(stage + 2 * (hh * kLatentDim + ch), static_cast<_Float16>(v));
       }
+    }
+  }
+  if (!direct) {  // the staged fp16 rows leave in 16-byte pieces
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPartRowBytes / (16 * kThreads); ++i) {
+      const int off = 16 * (threadIdx.x + kThreads * i);
+      *reinterpret_cast<u32x4*>(part + off) = lds_ld<u32x4>(stage + off);
     }
   }
   if (wave == 0 && n16 == 0) {
@@ -1115,8 +1143,9 @@ __device__ void finish(const DecodeParams& p, uint8_t* sums_lds, const f32x4 (&o
           p.lse[static_cast<int64_t>(cx.b) * p.heads + hg] =
               l_h[rr] > 0.f ? (m_o[rr] + log2f(l_h[rr])) * 0.69314718055994531f : kNegInf;
       } else {
-        part[kHeadBlock * kLatentDim + hh] = m_o[rr];
-        part[kHeadBlock * kLatentDim + kHeadBlock + hh] = l_h[rr];
+        float* const ml = reinterpret_cast<float*>(part + kPartRowBytes);
+        ml[hh] = m_o[rr];
+        ml[kHeadBlock + hh] = l_h[rr];
       }
     }
   }
@@ -1147,57 +1176,59 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   for (int k = 0; k < kStatW; ++k) st[k] = 0.f;
   if (cx.split < p.n_dense) {
     dense_wg<BITS>(o, st, m_o, p, smem, sr, cx, cx.split);
-    finish<BITS, false>(p, smem + kOffP, o, st, m_o, cx);
+    finish<BITS, false>(p, smem + kOffP, smem + kOffX, o, st, m_o, cx);
   } else {
     packed_wg<BITS>(o, st, m_o, p, smem, sr, cx, cx.split - p.n_dense, p.n_splits - p.n_dense);
-    finish<BITS, true>(p, smem + kPkOffP, o, st, m_o, cx);
+    finish<BITS, true>(p, smem + kPkOffP, smem + kPkOffStage, o, st, m_o, cx);
   }
 }
 
-// Merge of the per-split partials of one sequence and head.  Split s holds
-// O_s = sum_j p_j c_j with p_j = 2^(z_j - m_s) and l_s = sum_j p_j; the
-// result is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
-// One 64-thread workgroup per (sequence, head, half of the 512 channels);
-// thread t takes 4 channels.
-__global__ void __launch_bounds__(64) combine_kernel(const float* __restrict__ parts, float* __restrict__ out,
+// Merge of the split partials of one (sequence, head): grid = (sequence, head
+// block) x 16 heads, 64 threads x 8 channels.  A partial row holds the split's
+// normalized output O_s / l_s (fp16); the merge weights it by
+// 2^(m_s - M) l_s.
+__global__ void __launch_bounds__(64) combine_kernel(const uint8_t* __restrict__ parts, float* __restrict__ out,
                                                      float* __restrict__ lse, int heads, int n_hb, int n_splits) {
   __shared__ float s_m[kMaxSplits], s_l[kMaxSplits];
-  const int grp = blockIdx.x >> 5, hh = (blockIdx.x >> 1) & 15, half = blockIdx.x & 1;
+  const int grp = blockIdx.x >> 4, hh = blockIdx.x & 15;
   const int b = grp / n_hb, hg = (grp % n_hb) * kHeadBlock + hh;
   if (hg >= heads) return;
-  const float* base = parts + static_cast<int64_t>(grp) * n_splits * kPartFloats;
-  const int t = threadIdx.x, c = 256 * half + 4 * t;
-  // the first splits' partials go out before the (max, sum) staging
+  const uint8_t* base = parts + static_cast<int64_t>(grp) * n_splits * kPartBytes;
+  const int t = threadIdx.x, c = 8 * t;
+  const uint8_t* row = base + 2 * (hh * kLatentDim + c);
+  // the first splits' rows go out before the (max, sum) staging
   constexpr int kEarly = 16;
-  f32x4 v[kEarly];
+  u32x4 v[kEarly];
 #pragma unroll
   for (int s = 0; s < kEarly; ++s)
-    v[s] = s < n_splits ? ldg<f32x4>(base + static_cast<int64_t>(s) * kPartFloats + hh * kLatentDim + c)
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[s] = s < n_splits ? ldg<u32x4>(row + static_cast<int64_t>(s) * kPartBytes) : u32x4{0, 0, 0, 0};
   for (int s = t; s < n_splits; s += 64) {
-    s_m[s] = base[static_cast<int64_t>(s) * kPartFloats + kHeadBlock * kLatentDim + hh];
-    s_l[s] = base[static_cast<int64_t>(s) * kPartFloats + kHeadBlock * kLatentDim + kHeadBlock + hh];
+    const float* ml = reinterpret_cast<const float*>(base + static_cast<int64_t>(s) * kPartBytes + kPartRowBytes);
+    s_m[s] = ml[hh];
+    s_l[s] = ml[kHeadBlock + hh];
   }
   __syncthreads();
   float M = kNegInf;
   for (int s = 0; s < n_splits; ++s) M = fmaxf(M, s_m[s]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  auto add = [&](int s, const f32x4& x) {
-    const float f = s_m[s] == kNegInf ? 0.f : exp2f(s_m[s] - M);
-    L = fmaf(f, s_l[s], L);
-    acc += f * x;
+  auto add = [&](int s, const u32x4& x) {
+    const float w = s_m[s] == kNegInf ? 0.f : fast_exp2(s_m[s] - M) * s_l[s];
+    L += w;
+    const half8 h = __builtin_bit_cast(half8, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, static_cast<float>(h[e]), acc[e]);
   };
 #pragma unroll
   for (int s = 0; s < kEarly; ++s)
     if (s < n_splits) add(s, v[s]);
 #pragma unroll 8
-  for (int s = kEarly; s < n_splits; ++s)
-    add(s, ldg<f32x4>(base + static_cast<int64_t>(s) * kPartFloats + hh * kLatentDim + c));
+  for (int s = kEarly; s < n_splits; ++s) add(s, ldg<u32x4>(row + static_cast<int64_t>(s) * kPartBytes));
   const float il = L > 0.f ? 1.f / L : 0.f;
-  *reinterpret_cast<f32x4*>(out + (static_cast<int64_t>(b) * heads + hg) * kLatentDim + c) = acc * il;
-  if (half == 0 && t == 0)
-    lse[static_cast<int64_t>(b) * heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+  float* dst = out + (static_cast<int64_t>(b) * heads + hg) * kLatentDim + c;
+  *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0] * il, acc[1] * il, acc[2] * il, acc[3] * il};
+  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4] * il, acc[5] * il, acc[6] * il, acc[7] * il};
+  if (t == 0) lse[static_cast<int64_t>(b) * heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
 }
 
 }  // namespace
@@ -1240,7 +1271,7 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   p.sink = static_cast<const uint16_t*>(sink_buf);
   p.ring = static_cast<const uint16_t*>(ring_buf);
   p.tail = static_cast<const uint16_t*>(rope_tail);
-  p.parts = static_cast<float*>(workspace);
+  p.parts = static_cast<uint8_t*>(workspace);
   p.out = out;
   p.lse = lse;
   p.batch = batch;
@@ -1281,7 +1312,7 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
                        stream, p);
   if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
   if (plan.n_splits > 1) {
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(groups * 32)), dim3(64), 0, stream, p.parts, out,
+    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(groups * 16)), dim3(64), 0, stream, p.parts, out,
                        lse, heads, plan.n_hb, plan.n_splits);
     if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
   }

@@ -11,7 +11,9 @@ namespace mla {
 constexpr int kTile = 16;          // tokens per wave and round (the MFMA M dimension)
 constexpr int kHeadBlock = 16;     // heads per MFMA block
 constexpr int kDecodeWaves = 4;    // waves per workgroup (one per SIMD)
-constexpr int kPartFloats = kHeadBlock * kLatentDim + 2 * kHeadBlock;  // O [16][512], m, l
+// A split's partial: O / l as fp16 [16 heads][512], then fp32 m[16], l[16].
+constexpr int kPartRowBytes = kHeadBlock * kLatentDim * 2;
+constexpr int kPartBytes = kPartRowBytes + 2 * kHeadBlock * 4;
 constexpr int kTargetGroups = 512;  // two workgroups per CU of an MI355X
 constexpr int kDenseTilesPerWg = 8;  // BF16-path tiles per workgroup (two rounds)
 constexpr int kMaxSplits = 128;     // workgroups per (sequence, head block)
@@ -53,7 +55,7 @@ inline DecodePlan plan_decode(const Geometry& g, int batch, int heads, int max_s
   p.n_splits = p.n_dense + static_cast<int>(s);
   p.workspace_bytes = 0;
   if (p.n_splits > 1)
-    p.workspace_bytes = static_cast<size_t>(groups) * p.n_splits * kPartFloats * sizeof(float);
+    p.workspace_bytes = static_cast<size_t>(groups) * p.n_splits * kPartBytes;
   return p;
 }
 

@@ -55,7 +55,7 @@ def test_bad_layouts_rejected(bad):
 
 def test_workspace_query_and_errors():
     lay = mla.Layout(128, 4, 0.0, 4, 128)
-    part = (16 * 512 + 32) * 4  # one split's partial: 16 heads x 512 outputs + max + sum
+    part = 16 * 512 * 2 + 32 * 4  # one split's partial: 16 heads x 512 fp16 outputs + fp32 max, sum
     n = mla.mla_lowbit_decode_workspace(lay, 32, 16, 4096)
     assert n > 0 and n % (32 * part) == 0  # whole partials for each of the 32 sequences
     assert mla.mla_lowbit_decode_workspace(lay, 1, 16, 0) == 0  # one split: no partials
