@@ -1077,7 +1077,9 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     rescale_out(o, ah, raised);
     lds_barrier();
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no direct load outlives the workgroup
+  // no direct load outlives the workgroup, and every wave's last reads of P'
+  // and of the slots are done before finish reuses that LDS
+  __syncthreads();
 }
 
 // Per-head sums of every wave meet in LDS (sums_lds); the partial (or, with
