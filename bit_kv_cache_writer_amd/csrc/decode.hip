@@ -1021,8 +1021,9 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     const uint8_t* page = page_of_tile(it, pidx, slot0);
     dma_tile<BITS>(slot_ptr(s, wave), page, slot0, src, lane, p);
   };
+  // only the first tile goes out with the opening burst (every workgroup
+  // starts at once); the second follows round 0's scores
   if (my0 < my1) issue(my0, 0);
-  if (my0 + 1 < my1) issue(my0 + 1, 1);
   // the query is converted while the first tiles are in flight; slot 2,
   // which holds it, is first filled after the round-0 barrier
   publish_query<BITS, true>(qrows, qops, smem + kPkOffQr, wave, lane);
@@ -1041,7 +1042,7 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     float sc[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
     u32x4 md[4];
     if (has) {
-      wait_tiles_after<BITS>(it + 1 < my1 ? 1 : 0);  // tile r+1's loads may still fly
+      wait_tiles_after<BITS>(r > 0 && it + 1 < my1 ? 1 : 0);  // tile r+1's loads may still fly
       int pidx, slot0;
       const uint8_t* page = page_of_tile(it, pidx, slot0);
       if (page) {
@@ -1053,6 +1054,7 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
       }
     }
     if (r == rounds) break;
+    if (r == 0 && it + 1 < my1) issue(it + 1, 1);
     const float tmax = row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
