@@ -50,6 +50,7 @@
 // Tile, page and address arithmetic is wave-uniform (scalar registers).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -125,6 +126,7 @@ struct DecodeParams {
   int32_t batch, heads, max_pages, num_pool_pages, max_seqlen;
   int32_t n_hb, n_dense, n_splits;
   int32_t P, log2P, sink_n, local;
+  int32_t t_lo, t_count;  // packed tiles of the longest possible sequence: [t_lo, t_lo + t_count)
   int64_t latent_meta_off, rope_codes_off, rope_meta_off, page_bytes;
   float c_log2;  // softmax_scale * log2(e)
 };
@@ -450,48 +452,67 @@ __device__ inline float score_of(float v, float meta, float rope, float bias) {
   return fmaf(fmaf(rope, 1.f / kPrescale, v), kCodeScale, fmaf(meta, 1.f / kPrescale, bias));
 }
 
-// Scores (log2 domain) of one packed tile (tokens j0 .. j0+15 of a complete
-// page, valid in [vlo, vhi)) from its LDS slot: lane (h, gq) gets tokens
-// 4 gq + r of head h.  md[r] = the metadata words of token 4 gq + r.
+// Score inputs of one packed tile from its LDS slot: lane (t, gq) gets the
+// latent codes of channels 32 gq .. + 31 of every 128-channel group of token
+// t, its k_R codes (channels 16 gq .. + 15) and its latent metadata.
 template <int BITS>
-__device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BITS>& q, RopeOps& ro,
-                              const uint8_t* slot, bool new_page, const uint8_t* qr_row, int j0, int vlo, int vhi,
-                              int n16, int gq, float c_log2) {
-  using G = TileGeom<BITS>;
+struct ScoreIn {
   uint32_t lat[BITS == 4 ? 16 : 8];
+  u32x2 rope;
+  u32x4 ma;
+};
+
+template <int BITS>
+__device__ inline void load_score_in(ScoreIn<BITS>& si, const uint8_t* slot, int n16, int gq) {
+  using G = TileGeom<BITS>;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (BITS == 4) {
       const u32x4 v = lds_ld<u32x4>(slot + lat_unit<4>(n16, 4 * i + gq));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) lat[4 * i + e] = v[e];
+      for (int e = 0; e < 4; ++e) si.lat[4 * i + e] = v[e];
     } else {
       const u32x2 v = lds_ld<u32x2>(slot + lat_unit<2>(n16, 2 * i + (gq >> 1)) + 8 * (gq & 1));
-      lat[2 * i] = v[0];
-      lat[2 * i + 1] = v[1];
+      si.lat[2 * i] = v[0];
+      si.lat[2 * i + 1] = v[1];
     }
   }
-  const u32x2 rope = lds_ld<u32x2>(slot + G::kOffRope + n16 * kRopeRowBytes + 8 * gq);
-  const u32x4 ma = lds_ld<u32x4>(slot + G::kOffMeta + 16 * n16);
-  if (new_page) rope_ops(ro, qr_row, slot + G::kOffRMeta, gq);
-  f32x4 acc[6];
+  si.rope = lds_ld<u32x2>(slot + G::kOffRope + n16 * kRopeRowBytes + 8 * gq);
+  si.ma = lds_ld<u32x4>(slot + G::kOffMeta + 16 * n16);
+}
+
+// Score MFMAs of one packed tile: acc[g] = 2^-24 q_g . code_g per latent
+// group g, acc[4] = kPrescale sum_g m_g Q_g (metadata), acc[5] = 2^-24
+// kPrescale q_R s . code_R (positional key).
+template <int BITS>
+__device__ inline void score_mfma(f32x4 (&acc)[6], const ScoreIn<BITS>& si, const QueryOps<BITS>& q,
+                                  const RopeOps& ro) {
 #pragma unroll
   for (int g = 0; g < 6; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const half8 x = BITS == 4 ? unpack4(lat[4 * i + d]) : unpack2(lat[2 * i + (d >> 1)], d & 1);
+      const half8 x = BITS == 4 ? unpack4(si.lat[4 * i + d]) : unpack2(si.lat[2 * i + (d >> 1)], d & 1);
       acc[i] = mfma(x, q.lat[i][d], acc[i]);
     }
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const half8 xr = unpack4(rope[e]);
+    const half8 xr = unpack4(si.rope[e]);
     acc[5] = mfma(xr, ro.hi[e], acc[5]);
     acc[5] = mfma(xr, ro.lo[e], acc[5]);
   }
-  acc[4] = mfma(__builtin_bit_cast(half8, ma), q.meta, acc[4]);
+  acc[4] = mfma(__builtin_bit_cast(half8, si.ma), q.meta, acc[4]);
+}
+
+// Scores (log2 domain) of one packed tile (tokens j0 .. j0+15 of a complete
+// page, valid in [vlo, vhi); none when !has) from its MFMA sums: lane (h, gq)
+// gets tokens 4 gq + r of head h.  md[r] = the metadata words of token 4 gq + r.
+template <int BITS>
+__device__ inline void score_finish(float (&sc)[4], u32x4 (&md)[4], const f32x4 (&acc)[6], const uint8_t* slot,
+                                    float bias, bool has, int j0, int vlo, int vhi, int gq, float c_log2) {
+  using G = TileGeom<BITS>;
 #pragma unroll
   for (int r = 0; r < 4; ++r) md[r] = lds_ld<u32x4>(slot + G::kOffMeta + 16 * (4 * gq + r));
   float v[4] = {0.f, 0.f, 0.f, 0.f};
@@ -500,16 +521,16 @@ __device__ void packed_scores(float (&sc)[4], u32x4 (&md)[4], const QueryOps<BIT
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = fmaf(lo_f16(md[r][g]), acc[g][r], v[r]);
   }
-  if (j0 >= vlo && j0 + kTile <= vhi) {  // whole tile valid
+  if (has && j0 >= vlo && j0 + kTile <= vhi) {  // whole tile valid
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = score_of(v[r], acc[4][r], acc[5][r], ro.bias) * c_log2;
+    for (int r = 0; r < 4; ++r) sc[r] = score_of(v[r], acc[4][r], acc[5][r], bias) * c_log2;
     return;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = j0 + 4 * gq + r;
-    const float z = score_of(v[r], acc[4][r], acc[5][r], ro.bias);
-    sc[r] = (t >= vlo && t < vhi) ? z * c_log2 : kNegInf;
+    const float z = score_of(v[r], acc[4][r], acc[5][r], bias);
+    sc[r] = (has && t >= vlo && t < vhi) ? z * c_log2 : kNegInf;
   }
 }
 
@@ -976,14 +997,20 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   static_assert(kQopsBytes <= kWaves * kSlotBytes, "the converted query fits one slot row");
   auto slot_ptr = [&](int s, int w) { return smem + kPkOffStage + (s * kWaves + w) * kSlotBytes; };
 
-  QueryRows qrows;
-  fetch_query(qrows, p, cx.b, cx.hb, wave, lane);
-  const int t_lo = sr.lo_p / kTile;
-  const int T = sr.hi_p > sr.lo_p ? (sr.hi_p + kTile - 1) / kTile - t_lo : 0;
+  // The tiles are split by the batch's longest possible packed range
+  // (p.t_lo, p.t_count, from max_seqlen), not by this sequence's length, so
+  // that the first page id, the page-id window and the query rows are all
+  // requested at once; tiles past the sequence's own packed range are skipped.
+  const int t_lo = p.t_lo, T = p.t_count;
   const int per = (T + n_ps - 1) / n_ps;
   const int k0 = min(T, ps * per), k1 = min(T, k0 + per);
   const int rounds = (k1 - k0 + kWaves - 1) / kWaves;
   const int my0 = k0 + wave * rounds, my1 = min(k1, my0 + rounds);
+  int id0 = -1;  // page id of this wave's first tile
+  if (my0 < my1)
+    id0 = uniform(p.block_table[static_cast<int64_t>(cx.b) * p.max_pages + (((t_lo + my0) * kTile) >> p.log2P)]);
+  QueryRows qrows;
+  fetch_query(qrows, p, cx.b, cx.hb, wave, lane);
 
   // page ids of this workgroup's tiles (the launch sizes splits so that they
   // fit the window); loaded together with the query rows
@@ -1000,12 +1027,23 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     const int k = threadIdx.x + i * kThreads;
     pid[i] = k < n_pg ? bt_row[k] : -1;
   }
+  uint32_t src[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) src[c] = lat_src<BITS>(c, lane);
+  // the first tile goes out as soon as its page id is in; only it joins the
+  // opening burst (every workgroup starts at once), the second follows round
+  // 0's scores
+  if (my0 < my1)
+    dma_tile<BITS>(slot_ptr(0, wave), page_of_id(p, id0), ((t_lo + my0) * kTile) & (p.P - 1), src, lane, p);
+  // this sequence's packed tiles end at my_end (the sequence may be shorter
+  // than the longest one)
+  const int t_end = sr.hi_p > sr.lo_p ? (sr.hi_p + kTile - 1) / kTile - t_lo : 0;
+  const int my_end = min(my1, t_end);
 #pragma unroll
   for (int i = 0; i < kPidPerThread; ++i) {
     const int k = threadIdx.x + i * kThreads;
     if (k < n_pg) s_pid[k] = pid[i];
   }
-  lds_barrier();  // page ids staged
   auto page_of_tile = [&](int it, int& pidx, int& slot0) -> const uint8_t* {
     const int j0 = (t_lo + it) * kTile;
     pidx = j0 >> p.log2P;
@@ -1013,54 +1051,55 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     const int id = uniform(s_pid[min(max(pidx - pg_first, 0), kPageWin - 1)]);
     return page_of_id(p, id);
   };
-  uint32_t src[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) src[c] = lat_src<BITS>(c, lane);
   auto issue = [&](int it, int s) {
     int pidx, slot0;
     const uint8_t* page = page_of_tile(it, pidx, slot0);
     dma_tile<BITS>(slot_ptr(s, wave), page, slot0, src, lane, p);
   };
-  // only the first tile goes out with the opening burst (every workgroup
-  // starts at once); the second follows round 0's scores
-  if (my0 < my1) issue(my0, 0);
   // the query is converted while the first tiles are in flight; slot 2,
   // which holds it, is first filled after the round-0 barrier
   publish_query<BITS, true>(qrows, qops, smem + kPkOffQr, wave, lane);
-  lds_barrier();  // query converted
+  // zero weights for round 0's output MFMAs (no previous round)
+  for (int off = 16 * threadIdx.x; off < kPkPBytes; off += 16 * kThreads)
+    lds_st<u32x4>(smem + kPkOffP + off, u32x4{0, 0, 0, 0});
+  lds_barrier();  // page ids staged, query converted, P' zeroed
   QueryOps<BITS> q;
   load_query<BITS>(q, qops, lane);
 
   float m_run = kNegInf;
   RopeOps ro;
   int ro_page = -1;
-  for (int r = 0; r <= rounds; ++r) {
-    // A: output of round r - 1, scores of tile r
-    if (r > 0) packed_pv<BITS>(o, smem, (r - 1) % kSlots, wave, n16, gq);
+  for (int r = 0; r < rounds; ++r) {
+    // A: output of round r - 1 (P' is zero before round 0) and scores of
+    // tile r, their LDS reads under one wait so that the two sets of MFMAs
+    // and unpacks can interleave
     const int it = my0 + r;
-    bool has = r < rounds && it < my1;
-    float sc[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-    u32x4 md[4];
+    bool has = it < my_end;
+    int pidx = 0, slot0 = 0;
     if (has) {
-      wait_tiles_after<BITS>(r > 0 && it + 1 < my1 ? 1 : 0);  // tile r+1's loads may still fly
-      int pidx, slot0;
-      const uint8_t* page = page_of_tile(it, pidx, slot0);
-      if (page) {
-        packed_scores<BITS>(sc, md, q, ro, slot_ptr(r % kSlots, wave), pidx != ro_page, qr_row, (t_lo + it) * kTile,
-                            sr.lo_p, sr.hi_p, n16, gq, p.c_log2);
-        ro_page = pidx;
-      } else {
-        has = false;
-      }
+      wait_tiles_after<BITS>(r > 0 && it + 1 < my_end ? 1 : 0);  // tile r+1's loads may still fly
+      has = page_of_tile(it, pidx, slot0) != nullptr;
     }
-    if (r == rounds) break;
-    if (r == 0 && it + 1 < my1) issue(it + 1, 1);
+    const uint8_t* const slot = slot_ptr(r % kSlots, wave);
+    if (has && pidx != ro_page) {
+      rope_ops(ro, qr_row, slot + TileGeom<BITS>::kOffRMeta, gq);
+      ro_page = pidx;
+    }
+    ScoreIn<BITS> si;
+    load_score_in<BITS>(si, slot, n16, gq);
+    packed_pv<BITS>(o, smem, (r + kSlots - 1) % kSlots, wave, n16, gq);
+    f32x4 acc[6];
+    score_mfma<BITS>(acc, si, q, ro);
+    float sc[4];
+    u32x4 md[4];
+    score_finish<BITS>(sc, md, acc, slot, ro.bias, has, (t_lo + it) * kTile, sr.lo_p, sr.hi_p, gq, p.c_log2);
+    if (r == 0 && it + 1 < my_end) issue(it + 1, 1);
     const float tmax = row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
 
     // B: next loads, softmax of round r
-    if (it + 2 < my1) issue(it + 2, (r + 2) % kSlots);
+    if (it + 2 < my_end) issue(it + 2, (r + 2) % kSlots);
     float ah[4];
     bool raised;
     const float alpha = raise_max(m_run, m_o, ah, raised, smax, n16, gq);
@@ -1079,6 +1118,7 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     rescale_out(o, ah, raised);
     lds_barrier();
   }
+  if (rounds > 0) packed_pv<BITS>(o, smem, (rounds + kSlots - 1) % kSlots, wave, n16, gq);  // the last round's output
   // no direct load outlives the workgroup, and every wave's last reads of P'
   // and of the slots are done before finish reuses that LDS
   __syncthreads();
@@ -1296,6 +1336,13 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   p.rope_meta_off = g.rope_meta_off;
   p.page_bytes = g.page_bytes;
   p.c_log2 = softmax_scale * 1.44269504088896341f;
+  {  // packed range of a sequence of max_seqlen tokens (the longest one)
+    const int64_t ml = max_seqlen;
+    const int64_t lo = std::min<int64_t>(g.sink, ml);
+    const int64_t hi = std::max<int64_t>(lo, std::min<int64_t>(ml - g.local, (ml / g.page_size) * g.page_size));
+    p.t_lo = static_cast<int32_t>(lo / kTile);
+    p.t_count = hi > lo ? static_cast<int32_t>((hi + kTile - 1) / kTile - p.t_lo) : 0;
+  }
   const int64_t groups = static_cast<int64_t>(batch) * plan.n_hb;
   const int64_t blocks = groups * plan.n_splits;
   if (blocks > 0x7FFFFFFF || groups * 32 > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
