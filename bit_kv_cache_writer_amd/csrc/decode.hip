@@ -1044,17 +1044,10 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     const int k = threadIdx.x + i * kThreads;
     if (k < n_pg) s_pid[k] = pid[i];
   }
-  auto page_of_tile = [&](int it, int& pidx, int& slot0) -> const uint8_t* {
-    const int j0 = (t_lo + it) * kTile;
-    pidx = j0 >> p.log2P;
-    slot0 = j0 & (p.P - 1);
-    const int id = uniform(s_pid[min(max(pidx - pg_first, 0), kPageWin - 1)]);
-    return page_of_id(p, id);
-  };
-  auto issue = [&](int it, int s) {
-    int pidx, slot0;
-    const uint8_t* page = page_of_tile(it, pidx, slot0);
-    dma_tile<BITS>(slot_ptr(s, wave), page, slot0, src, lane, p);
+  // staged page id of tile it (not yet wave-uniform: read early, used later)
+  auto pid_at = [&](int it) { return s_pid[min(max((((t_lo + it) * kTile) >> p.log2P) - pg_first, 0), kPageWin - 1)]; };
+  auto issue = [&](int it, int id, int s) {
+    dma_tile<BITS>(slot_ptr(s, wave), page_of_id(p, id), ((t_lo + it) * kTile) & (p.P - 1), src, lane, p);
   };
   // the query is converted while the first tiles are in flight; slot 2,
   // which holds it, is first filled after the round-0 barrier
@@ -1075,31 +1068,32 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     // and unpacks can interleave
     const int it = my0 + r;
     bool has = it < my_end;
-    int pidx = 0, slot0 = 0;
-    if (has) {
-      wait_tiles_after<BITS>(r > 0 && it + 1 < my_end ? 1 : 0);  // tile r+1's loads may still fly
-      has = page_of_tile(it, pidx, slot0) != nullptr;
-    }
+    if (has) wait_tiles_after<BITS>(r > 0 && it + 1 < my_end ? 1 : 0);  // tile r+1's loads may still fly
     const uint8_t* const slot = slot_ptr(r % kSlots, wave);
-    if (has && pidx != ro_page) {
+    const int pidx = ((t_lo + it) * kTile) >> p.log2P;
+    if (has && pidx != ro_page) {  // (a page missing from the block table only spoils its own tiles)
       rope_ops(ro, qr_row, slot + TileGeom<BITS>::kOffRMeta, gq);
       ro_page = pidx;
     }
+    // page ids of this tile and of the tiles issued this round, read with
+    // the tile's LDS inputs
+    const int id_cur = pid_at(it), id_1 = pid_at(it + 1), id_2 = pid_at(it + 2);
     ScoreIn<BITS> si;
     load_score_in<BITS>(si, slot, n16, gq);
     packed_pv<BITS>(o, smem, (r + kSlots - 1) % kSlots, wave, n16, gq);
+    has = has && page_of_id(p, uniform(id_cur)) != nullptr;
     f32x4 acc[6];
     score_mfma<BITS>(acc, si, q, ro);
     float sc[4];
     u32x4 md[4];
     score_finish<BITS>(sc, md, acc, slot, ro.bias, has, (t_lo + it) * kTile, sr.lo_p, sr.hi_p, gq, p.c_log2);
-    if (r == 0 && it + 1 < my_end) issue(it + 1, 1);
+    if (r == 0 && it + 1 < my_end) issue(it + 1, uniform(id_1), 1);
     const float tmax = row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
 
     // B: next loads, softmax of round r
-    if (it + 2 < my_end) issue(it + 2, (r + 2) % kSlots);
+    if (it + 2 < my_end) issue(it + 2, uniform(id_2), (r + 2) % kSlots);
     float ah[4];
     bool raised;
     const float alpha = raise_max(m_run, m_o, ah, raised, smax, n16, gq);
