@@ -107,9 +107,6 @@ constexpr int kLdsBytes = kDenseLds > kPackedLds ? kDenseLds : kPackedLds;
 static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per gfx950 CU");
 static_assert(kWaves * kHeadBlock * kStatW * 4 <= kWaves * kPTile, "final sums fit the P' area");
 static_assert(kWaves * kHeadBlock * kStatW * 4 <= kPkPBytes, "final sums fit the P' area");
-static_assert(kPartRowBytes <= kWaves * kXTile && kPartRowBytes <= kSlots * kWaves * kSlotBytes,
-              "a partial's fp16 rows stage in the tile area");
-static_assert(kPartRowBytes % (16 * kThreads) == 0, "the staged rows leave in whole 16-byte passes");
 
 struct DecodeParams {
   const uint16_t* q_lat;
@@ -1118,58 +1115,57 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   __syncthreads();
 }
 
-// Per-head sums of every wave meet in LDS (sums_lds); the partial (or, with
-// one split, the normalized output and lse) is written in natural channel
-// order.  chan(kk, n16) maps an accumulator column to its latent channel.
+// Per-head sums of every wave meet in LDS (sums_lds, [wave][sum][head]); each
+// lane then turns its accumulators (heads 4 gq + r of one channel per column
+// block kk) into the split's partial, stored straight from registers in the
+// channel-major layout [channel][16 heads] fp16 (four heads = 8 bytes per
+// lane and block), or, with one split, into the normalized output and lse.
+// chan(kk, n16) maps an accumulator column to its latent channel.
 template <int BITS, bool kPackedMap>
-__device__ void finish(const DecodeParams& p, uint8_t* sums_lds, uint8_t* stage, const f32x4 (&o)[8],
-                       const float (&st)[kStatW], const float (&m_o)[4], const WgCtx& cx) {
+__device__ void finish(const DecodeParams& p, uint8_t* sums_lds, const f32x4 (&o)[8], const float (&st)[kStatW],
+                       const float (&m_o)[4], const WgCtx& cx) {
   // packed: output MFMAs summed 2^-24 fp16(p s) code; BF16 path: p / kappa x
   constexpr float out_scale = kPackedMap ? kCodeScale : (BITS == 4 ? 16.f : 4.f);
   const int wave = cx.wave, n16 = cx.n16, gq = cx.gq;
-  float* const sfin = reinterpret_cast<float*>(sums_lds);
 #pragma unroll
   for (int k = 0; k < kStatW; ++k) {
     const float v = row_allsum(st[k]);
-    if (gq == 0) sfin[(wave * kHeadBlock + n16) * kStatW + k] = v;
+    if (gq == 0) lds_st<float>(sums_lds + ((wave * kStatW + k) * kHeadBlock + n16) * 4, v);
   }
-  __syncthreads();
+  lds_barrier();
+  // sums over the waves for heads 4 gq .. 4 gq + 3: l and sum p m_g of this
+  // wave's latent group g = wave
+  f32x4 lq = {0.f, 0.f, 0.f, 0.f}, mq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    lq += lds_ld<f32x4>(sums_lds + ((w * kStatW) * kHeadBlock + 4 * gq) * 4);
+    mq += lds_ld<f32x4>(sums_lds + ((w * kStatW + 1 + wave) * kHeadBlock + 4 * gq) * 4);
+  }
+  float inv[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) inv[rr] = lq[rr] > 0.f ? 1.f / lq[rr] : 0.f;
   const bool direct = p.n_splits == 1;
-  uint8_t* part = p.parts + (static_cast<int64_t>(cx.grp) * p.n_splits + cx.split) * kPartBytes;
-  float l_h[4];
+  uint8_t* const part = p.parts + (static_cast<int64_t>(cx.grp) * p.n_splits + cx.split) * kPartBytes;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int hh = 4 * gq + rr, hg = cx.hb * kHeadBlock + hh;
-    float l = 0.f, m = 0.f;
+  for (int kk = 0; kk < 8; ++kk) {
+    int ch;
+    if constexpr (kPackedMap)
+      ch = BITS == 4 ? 128 * wave + 16 * kk + n16 : 128 * wave + 32 * (kk >> 1) + 2 * n16 + (kk & 1);
+    else
+      ch = col_to_channel<BITS>(128 * wave + 16 * kk + n16);
+    float v[4];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* f = sfin + (w * kHeadBlock + hh) * kStatW;
-      l += f[0];
-      m += f[1 + wave];
-    }
-    l_h[rr] = l;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(out_scale, o[kk][rr], mq[rr]) * inv[rr];
+    if (direct) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      int ch;
-      if constexpr (kPackedMap)
-        ch = BITS == 4 ? 128 * wave + 16 * kk + n16 : 128 * wave + 32 * (kk >> 1) + 2 * n16 + (kk & 1);
-      else
-        ch = col_to_channel<BITS>(128 * wave + 16 * kk + n16);
-      const float v = fmaf(out_scale, o[kk][rr], m) * inv;
-      if (direct) {
-        if (hg < p.heads) p.out[(static_cast<int64_t>(cx.b) * p.heads + hg) * kLatentDim + ch] = v;
-      } else {
-        lds_st<_Float16>(stage + 2 * (hh * kLatentDim + ch), static_cast<_Float16>(v));
+      for (int rr = 0; rr < 4; ++rr) {
+        const int hg = cx.hb * kHeadBlock + 4 * gq + rr;
+        if (hg < p.heads) p.out[(static_cast<int64_t>(cx.b) * p.heads + hg) * kLatentDim + ch] = v[rr];
       }
-    }
-  }
-  if (!direct) {  // the staged fp16 rows leave in 16-byte pieces
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kPartRowBytes / (16 * kThreads); ++i) {
-      const int off = 16 * (threadIdx.x + kThreads * i);
-      *reinterpret_cast<u32x4*>(part + off) = lds_ld<u32x4>(stage + off);
+    } else {
+      const half4 h = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]), static_cast<_Float16>(v[2]),
+                       static_cast<_Float16>(v[3])};
+      *reinterpret_cast<half4*>(part + 2 * (ch * kHeadBlock + 4 * gq)) = h;
     }
   }
   if (wave == 0 && n16 == 0) {
@@ -1179,11 +1175,11 @@ __device__ void finish(const DecodeParams& p, uint8_t* sums_lds, uint8_t* stage,
       if (direct) {
         if (hg < p.heads)
           p.lse[static_cast<int64_t>(cx.b) * p.heads + hg] =
-              l_h[rr] > 0.f ? (m_o[rr] + log2f(l_h[rr])) * 0.69314718055994531f : kNegInf;
+              lq[rr] > 0.f ? (m_o[rr] + log2f(lq[rr])) * 0.69314718055994531f : kNegInf;
       } else {
         float* const ml = reinterpret_cast<float*>(part + kPartRowBytes);
         ml[hh] = m_o[rr];
-        ml[kHeadBlock + hh] = l_h[rr];
+        ml[kHeadBlock + hh] = lq[rr];
       }
     }
   }
@@ -1214,59 +1210,99 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   for (int k = 0; k < kStatW; ++k) st[k] = 0.f;
   if (cx.split < p.n_dense) {
     dense_wg<BITS>(o, st, m_o, p, smem, sr, cx, cx.split);
-    finish<BITS, false>(p, smem + kOffP, smem + kOffX, o, st, m_o, cx);
+    finish<BITS, false>(p, smem + kOffP, o, st, m_o, cx);
   } else {
     packed_wg<BITS>(o, st, m_o, p, smem, sr, cx, cx.split - p.n_dense, p.n_splits - p.n_dense);
-    finish<BITS, true>(p, smem + kPkOffP, smem + kPkOffStage, o, st, m_o, cx);
+    finish<BITS, true>(p, smem + kPkOffP, o, st, m_o, cx);
   }
 }
 
-// Merge of the split partials of one (sequence, head): grid = (sequence, head
-// block) x 16 heads, 64 threads x 8 channels.  A partial row holds the split's
-// normalized output O_s / l_s (fp16); the merge weights it by
-// 2^(m_s - M) l_s.
+// Merge of the split partials of one (sequence, head block): grid =
+// (sequence, head block) x 16 blocks of 32 channels, 64 threads; thread t takes
+// channel 32 block + t / 2, heads 8 (t % 2) .. + 7 (16 bytes of the
+// channel-major partial rows).  A partial holds the split's normalized output
+// O_s / l_s (fp16) and (m_s, l_s); the merge weights split s by
+// 2^(m_s - M) l_s / sum over splits, M = max_s m_s, per head (the weights are
+// formed by all 64 threads: head t % 16, every fourth split).
 __global__ void __launch_bounds__(64) combine_kernel(const uint8_t* __restrict__ parts, float* __restrict__ out,
                                                      float* __restrict__ lse, int heads, int n_hb, int n_splits) {
-  __shared__ float s_m[kMaxSplits], s_l[kMaxSplits];
-  const int grp = blockIdx.x >> 4, hh = blockIdx.x & 15;
-  const int b = grp / n_hb, hg = (grp % n_hb) * kHeadBlock + hh;
-  if (hg >= heads) return;
-  const uint8_t* base = parts + static_cast<int64_t>(grp) * n_splits * kPartBytes;
-  const int t = threadIdx.x, c = 8 * t;
-  const uint8_t* row = base + 2 * (hh * kLatentDim + c);
-  // the first splits' rows go out before the (max, sum) staging
+  __shared__ __attribute__((aligned(16))) float s_ml[kMaxSplits * 2 * kHeadBlock];  // [split][m 16, l 16]
+  __shared__ __attribute__((aligned(16))) float s_w[kMaxSplits * kHeadBlock];  // [split][head] weights
+  __shared__ __attribute__((aligned(16))) float s_red[9 * kHeadBlock];  // partial max, partial sums, 1 / sum
+  const int grp = blockIdx.x >> 4, cb = blockIdx.x & 15;
+  const int b = grp / n_hb, hb = grp % n_hb;
+  const uint8_t* const base = parts + static_cast<int64_t>(grp) * n_splits * kPartBytes;
+  const int t = threadIdx.x, c = 32 * cb + (t >> 1), h0 = 8 * (t & 1);
+  const uint8_t* const row = base + 2 * (c * kHeadBlock + h0);
+  // every split's (max, sum) block (8 x 16 bytes) goes out first, all at once,
+  // then the first splits' rows; the weights are formed while the rows fly
+  // (addresses are clamped to the last split rather than branched around, so
+  // that every load is in flight before the first wait)
+  const int n_ml = (n_splits * 8 + 63) / 64;  // pieces per thread
+  constexpr int kMlPieces = kMaxSplits * 8 / 64;
+  u32x4 ml[kMlPieces];
+#pragma unroll
+  for (int k = 0; k < kMlPieces; ++k) {
+    const int i = min(t + 64 * k, n_splits * 8 - 1);  // piece i: split i / 8, floats 4 (i % 8) .. + 3
+    if (k < n_ml) ml[k] = ldg<u32x4>(base + static_cast<int64_t>(i >> 3) * kPartBytes + kPartRowBytes + 16 * (i & 7));
+  }
   constexpr int kEarly = 16;
   u32x4 v[kEarly];
 #pragma unroll
-  for (int s = 0; s < kEarly; ++s)
-    v[s] = s < n_splits ? ldg<u32x4>(row + static_cast<int64_t>(s) * kPartBytes) : u32x4{0, 0, 0, 0};
-  for (int s = t; s < n_splits; s += 64) {
-    const float* ml = reinterpret_cast<const float*>(base + static_cast<int64_t>(s) * kPartBytes + kPartRowBytes);
-    s_m[s] = ml[hh];
-    s_l[s] = ml[kHeadBlock + hh];
+  for (int s = 0; s < kEarly; ++s) v[s] = ldg<u32x4>(row + static_cast<int64_t>(min(s, n_splits - 1)) * kPartBytes);
+#pragma unroll
+  for (int k = 0; k < kMlPieces; ++k) {
+    if (k < n_ml) *reinterpret_cast<u32x4*>(s_ml + 4 * min(t + 64 * k, n_splits * 8 - 1)) = ml[k];
   }
   __syncthreads();
-  float M = kNegInf;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, s_m[s]);
+  // weights, all 64 threads: head t % 16 over the splits s = t / 16 (mod 4)
+  const int wh = t & 15, wq = t >> 4;
+  float mp = kNegInf;
+  for (int s = wq; s < n_splits; s += 4) mp = fmaxf(mp, s_ml[s * 32 + wh]);
+  s_red[wq * kHeadBlock + wh] = mp;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[wh], s_red[kHeadBlock + wh]),
+                        fmaxf(s_red[2 * kHeadBlock + wh], s_red[3 * kHeadBlock + wh]));
+  float lp = 0.f;
+  for (int s = wq; s < n_splits; s += 4) {
+    const float m = s_ml[s * 32 + wh];
+    const float w = m == kNegInf ? 0.f : fast_exp2(m - M) * s_ml[s * 32 + kHeadBlock + wh];
+    s_w[s * kHeadBlock + wh] = w;
+    lp += w;
+  }
+  s_red[(4 + wq) * kHeadBlock + wh] = lp;
+  __syncthreads();
+  if (t < kHeadBlock) {
+    const float L = (s_red[4 * kHeadBlock + t] + s_red[5 * kHeadBlock + t]) +
+                    (s_red[6 * kHeadBlock + t] + s_red[7 * kHeadBlock + t]);
+    s_red[8 * kHeadBlock + t] = L > 0.f ? 1.f / L : 0.f;
+    const int hg = hb * kHeadBlock + t;
+    if (cb == 0 && hg < heads)
+      lse[static_cast<int64_t>(b) * heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+  }
+  __syncthreads();
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
   auto add = [&](int s, const u32x4& x) {
-    const float w = s_m[s] == kNegInf ? 0.f : fast_exp2(s_m[s] - M) * s_l[s];
-    L += w;
-    const half8 h = __builtin_bit_cast(half8, x);
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(s_w + s * kHeadBlock + h0);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(s_w + s * kHeadBlock + h0 + 4);
+    const half8 hv = __builtin_bit_cast(half8, x);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, static_cast<float>(h[e]), acc[e]);
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = fmaf(w0[e], static_cast<float>(hv[e]), acc[e]);
+      acc[4 + e] = fmaf(w1[e], static_cast<float>(hv[4 + e]), acc[4 + e]);
+    }
   };
 #pragma unroll
   for (int s = 0; s < kEarly; ++s)
     if (s < n_splits) add(s, v[s]);
 #pragma unroll 8
   for (int s = kEarly; s < n_splits; ++s) add(s, ldg<u32x4>(row + static_cast<int64_t>(s) * kPartBytes));
-  const float il = L > 0.f ? 1.f / L : 0.f;
-  float* dst = out + (static_cast<int64_t>(b) * heads + hg) * kLatentDim + c;
-  *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0] * il, acc[1] * il, acc[2] * il, acc[3] * il};
-  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4] * il, acc[5] * il, acc[6] * il, acc[7] * il};
-  if (t == 0) lse[static_cast<int64_t>(b) * heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int hg = hb * kHeadBlock + h0 + e;
+    if (hg < heads)
+      out[(static_cast<int64_t>(b) * heads + hg) * kLatentDim + c] = acc[e] * s_red[8 * kHeadBlock + h0 + e];
+  }
 }
 
 }  // namespace
