@@ -978,11 +978,12 @@ __device__ void dense_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], co
 // Packed workgroup `ps` of n_ps: packed tiles split evenly, each wave a
 // contiguous run; per wave a ring of kSlots LDS slots filled by direct loads.
 // Software-pipelined rounds, two barriers each:
-//   A: output MFMAs of round r-1 (P' and every wave's slot (r-1) % 3) and the
+//   A: the direct loads of tile r+1 into slot (r+1) % 3 = (r-2) % 3 (free:
+//      every wave finished round r-1's phase A), then the output MFMAs of
+//      round r-1 (P' and every wave's slot (r-1) % 3) together with the
 //      scores of this wave's tile r (slot r % 3)
-//   B: the direct loads of tile r+2 into slot (r+2) % 3 = (r-1) % 3 (free:
-//      all waves are past A), the common running max, P' of round r, the
-//      rescale of the output accumulators
+//   B: the common running max, P' of round r, the rescale of the output
+//      accumulators
 template <int BITS>
 __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], const DecodeParams& p, uint8_t* smem,
                           const SeqRanges& sr, const WgCtx& cx, int ps, int n_ps) {
@@ -1059,12 +1060,16 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   float m_run = kNegInf;
   RopeOps ro;
   int ro_page = -1;
+  int id_next = -1;
   for (int r = 0; r < rounds; ++r) {
     // A: output of round r - 1 (P' is zero before round 0) and scores of
     // tile r, their LDS reads under one wait so that the two sets of MFMAs
     // and unpacks can interleave
     const int it = my0 + r;
     bool has = it < my_end;
+    // tile r+1 goes into slot (r+1) % 3, which every wave's output MFMAs of
+    // round r-2 have left (round r-1's first barrier)
+    if (r > 0 && it + 1 < my_end) issue(it + 1, uniform(id_next), (r + 1) % kSlots);
     if (has) wait_tiles_after<BITS>(r > 0 && it + 1 < my_end ? 1 : 0);  // tile r+1's loads may still fly
     const uint8_t* const slot = slot_ptr(r % kSlots, wave);
     const int pidx = ((t_lo + it) * kTile) >> p.log2P;
@@ -1089,8 +1094,8 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
 
-    // B: next loads, softmax of round r
-    if (it + 2 < my_end) issue(it + 2, uniform(id_2), (r + 2) % kSlots);
+    // B: softmax of round r (tile r+2 is issued at the top of the next round)
+    id_next = id_2;
     float ah[4];
     bool raised;
     const float alpha = raise_max(m_run, m_o, ah, raised, smax, n16, gq);
@@ -1189,8 +1194,15 @@ template <int BITS>
 __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   WgCtx cx;
-  cx.split = blockIdx.x % p.n_splits;
-  cx.grp = blockIdx.x / p.n_splits;  // b * n_hb + hb
+  // Workgroups are dealt to the 8 XCDs of the chip in turn (block i on XCD
+  // i mod 8); order the work so that each XCD's blocks take consecutive
+  // (sequence, head block, split) items, which keeps the splits of a sequence
+  // on one XCD, sharing its L2 for the query rows and block-table window.
+  // (Any dispatch order gives the same results; this only places the work.)
+  const int n_blocks = gridDim.x, xcd = blockIdx.x & 7, per_xcd = n_blocks >> 3, extra = n_blocks & 7;
+  const int item = xcd * per_xcd + min(xcd, extra) + (blockIdx.x >> 3);
+  cx.split = item % p.n_splits;
+  cx.grp = item / p.n_splits;  // b * n_hb + hb
   cx.hb = cx.grp % p.n_hb;
   cx.b = cx.grp / p.n_hb;
   cx.lane = threadIdx.x & 63;
