@@ -237,23 +237,30 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, xl, xr, lane);
   }
 
-  // k_R of a page that becomes full: per channel over its P tokens.  The
-  // page's P rows (tail buffer for tokens of earlier calls, input rows for
-  // new ones) are first staged in LDS with 16-byte loads, all in flight at
-  // once, then reduced per channel from LDS.
+  // k_R rows of a page that becomes full in this call (tail buffer for tokens
+  // of earlier calls, input rows for new ones) go straight from global memory
+  // into LDS, all at once (16 bytes per lane and load); the barrier before
+  // their reduction waits for them.
   __shared__ uint4 s_rows[256 * kRopeDim / 8];  // P x 64 bf16
-  __shared__ float s_min[kWaves][kRopeDim], s_max[kWaves][kRopeDim];
-  __shared__ float s_minf[kRopeDim], s_sf[kRopeDim];
-  __shared__ uint8_t s_code[256 * kRopeDim];
   const bool completes = (pg + 1) * P <= end;
   if (completes) {
-    for (int i = threadIdx.x; i < P * (kRopeDim / 8); i += kThreads) {
+    for (int k = 0; k < P * (kRopeDim / 8) / kThreads; ++k) {  // P * 8 is a multiple of 256 (P >= 32)
+      const int i = static_cast<int>(threadIdx.x) + k * kThreads;
       const int slot = i >> 3, q = i & 7;
       const int t = pg * P + slot;
       const uint4* src = t < sb ? reinterpret_cast<const uint4*>(tail + static_cast<int64_t>(slot) * kRopeDim) + q
                                 : reinterpret_cast<const uint4*>(p.k_r + (r0 + (t - sb)) * static_cast<int64_t>(kRopeDim)) + q;
-      s_rows[i] = *src;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(s_rows + k * kThreads + 64 * wave),
+                                       16, 0, 0);
     }
+  }
+
+  // k_R of a page that becomes full: per channel over its P tokens, reduced
+  // from the rows staged in LDS.
+  __shared__ float s_min[kWaves][kRopeDim], s_max[kWaves][kRopeDim];
+  __shared__ float s_minf[kRopeDim], s_sf[kRopeDim];
+  __shared__ uint8_t s_code[256 * kRopeDim];
+  if (completes) {
     __syncthreads();
     const uint16_t* rows = reinterpret_cast<const uint16_t*>(s_rows);
     const int c = threadIdx.x & 63, part = threadIdx.x >> 6;
