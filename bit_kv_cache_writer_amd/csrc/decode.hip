@@ -234,8 +234,8 @@ struct QueryOps {
 
 // Query staging.  Wave w fetches latent group w of the 16 heads of a head
 // block straight into the operand layout (lane (h, gq): channels
-// 128 w + 32 gq .. + 31 of head h) and wave 0 also the q_rope rows (lane:
-// head lane / 4, 16 channels).  Heads past the last one read a copy of the
+// 128 w + 32 gq .. + 31 of head h) and the q_rope rows (lane: head lane / 4,
+// 16 channels).  Heads past the last one read a copy of the
 // last head.
 struct QueryRows {
   u32x4 lat[4], rope[2];
@@ -248,13 +248,42 @@ __device__ inline void fetch_query(QueryRows& qr, const DecodeParams& p, int b, 
   const uint16_t* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + hc) * kLatentDim + 128 * wave + 32 * gq;
 #pragma unroll
   for (int u = 0; u < 4; ++u) qr.lat[u] = ldg<u32x4>(ql + 8 * u);
-  if (wave == 0) {
-    const int hr = hb * kHeadBlock + (lane >> 2);
-    const int hrc = hr < p.heads ? hr : p.heads - 1;
-    const uint16_t* qp = p.q_rope + (static_cast<int64_t>(b) * p.heads + hrc) * kRopeDim + 16 * (lane & 3);
-    qr.rope[0] = ldg<u32x4>(qp);
-    qr.rope[1] = ldg<u32x4>(qp + 8);
+  // every wave loads them (no branch, so that the loads' waits stay counted
+  // in order); only wave 0 stores them
+  const int hr = hb * kHeadBlock + (lane >> 2);
+  const int hrc = hr < p.heads ? hr : p.heads - 1;
+  const uint16_t* qp = p.q_rope + (static_cast<int64_t>(b) * p.heads + hrc) * kRopeDim + 16 * (lane & 3);
+  qr.rope[0] = ldg<u32x4>(qp);
+  qr.rope[1] = ldg<u32x4>(qp + 8);
+}
+
+// 16 bytes from global memory straight into LDS at lds_base + 16 * lane.
+__device__ inline void load_to_lds(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+// 4 bytes per lane: lds_base + 4 * lane.
+__device__ inline void load4_to_lds(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// Query rows of a packed workgroup by direct loads: wave w brings latent
+// group w of the 16 heads into qraw ([group][head][128 channels] bf16, four
+// loads) and the q_rope rows of heads 8 (w % 2) .. + 7 into qr_lds
+// ([head][64] bf16; waves w and w + 2 write the same bytes).  Heads past the
+// last one read a copy of the last head.
+__device__ inline void dma_query(const DecodeParams& p, int b, int hb, uint8_t* qraw, uint8_t* qr_lds, int wave,
+                                 int lane) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int h = hb * kHeadBlock + 4 * c + (lane >> 4);
+    const int hc = h < p.heads ? h : p.heads - 1;
+    const uint16_t* src = p.q_lat + (static_cast<int64_t>(b) * p.heads + hc) * kLatentDim + 128 * wave + 8 * (lane & 15);
+    load_to_lds(src, qraw + wave * 4096 + 1024 * c);
   }
+  const int h = hb * kHeadBlock + 8 * (wave & 1) + (lane >> 3);
+  const int hc = h < p.heads ? h : p.heads - 1;
+  load_to_lds(p.q_rope + (static_cast<int64_t>(b) * p.heads + hc) * kRopeDim + 8 * (lane & 7),
+              qr_lds + 1024 * (wave & 1));
 }
 
 // LDS image of the converted query: [group][chunk][lane] fp16 x 8 operands,
@@ -266,7 +295,7 @@ constexpr int kQopsBytes = kQopsSums + kHeadBlock * 4 * 4;
 // (divided by the slot's sigma for the masking unpack when kSigma) and Q_w =
 // sum of the group's 128 channels, both into the LDS image; wave 0 also
 // stores the q_rope rows as [head][128 B].
-template <int BITS, bool kSigma>
+template <int BITS, bool kSigma, bool kRope = true>
 __device__ inline void publish_query(const QueryRows& qr, uint8_t* qops, uint8_t* qr_lds, int wave, int lane) {
   const int n16 = lane & 15, gq = lane >> 4;
   float v[32];
@@ -292,7 +321,7 @@ __device__ inline void publish_query(const QueryRows& qr, uint8_t* qops, uint8_t
     lds_st<half8>(qops + ((wave * 4 + d) * 64 + lane) * 16, x);
   }
   if (gq == 0) lds_st<float>(qops + kQopsSums + (n16 * 4 + wave) * 4, qsum);
-  if (wave == 0) {
+  if (kRope && wave == 0) {
     lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * (lane & 3), qr.rope[0]);
     lds_st<u32x4>(qr_lds + (lane >> 2) * 128 + 32 * (lane & 3) + 16, qr.rope[1]);
   }
@@ -392,10 +421,6 @@ __device__ inline int lat_unit(int row, int u) {
   else return row * 128 + ((u ^ (row & 7)) << 4);
 }
 
-// 16 bytes from global memory straight into LDS at lds_base + 16 * lane.
-__device__ inline void load_to_lds(const void* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
 
 // Source offset (inside the tile's latent rows) of the 16 bytes lane `lane`
 // moves with direct load c: the lane writes slot unit 64 c + lane, which
@@ -418,18 +443,22 @@ template <int BITS>
 __device__ inline void dma_tile(uint8_t* slot, const uint8_t* page, int slot0, const uint32_t (&src)[4], int lane,
                                 const DecodeParams& p) {
   using G = TileGeom<BITS>;
-  if (page) {
-    const uint8_t* lat = page + slot0 * G::kLatRow;
+  // a page missing from the block table loads 16 bytes of the query instead
+  // (the tile is skipped); selected rather than branched, so that later waits
+  // can count these loads
+  const bool ok = page != nullptr;
+  const uint8_t* const base = ok ? page : reinterpret_cast<const uint8_t*>(p.q_lat);
+  const int64_t lat = ok ? slot0 * G::kLatRow : 0;
 #pragma unroll
-    for (int c = 0; c < G::kLatLoads; ++c) load_to_lds(lat + src[c], slot + 1024 * c);
-    const uint8_t* s = lane < 32 ? page + p.rope_codes_off + slot0 * kRopeRowBytes + 16 * lane
-                       : lane < 48 ? page + p.latent_meta_off + slot0 * 16 + 16 * (lane - 32)
-                                   : page + p.rope_meta_off + 16 * (lane - 48);
-    load_to_lds(s, slot + G::kOffRope);
-  } else {  // page missing from the block table: the tile is skipped
-#pragma unroll
-    for (int c = 0; c < G::kLoads; ++c) load_to_lds(p.q_lat, slot + 1024 * c);
-  }
+  for (int c = 0; c < G::kLatLoads; ++c) load_to_lds(base + (ok ? lat + src[c] : 0), slot + 1024 * c);
+  // lanes 0-31: k_R codes, 32-47: latent metadata, 48-63: the page's k_R
+  // metadata (arithmetic selects, no divergent branch)
+  const int64_t s_rope = p.rope_codes_off + slot0 * kRopeRowBytes + 16 * lane;
+  const int64_t s_meta = p.latent_meta_off + slot0 * 16 + 16 * (lane - 32);
+  const int64_t s_rmeta = p.rope_meta_off + 16 * (lane - 48);
+  int64_t s = lane < 48 ? s_meta : s_rmeta;
+  s = lane < 32 ? s_rope : s;
+  load_to_lds(base + (ok ? s : 0), slot + G::kOffRope);
 }
 
 // Waits until at most `after` tiles' direct loads are still in flight (the
@@ -1004,11 +1033,14 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   const int k0 = min(T, ps * per), k1 = min(T, k0 + per);
   const int rounds = (k1 - k0 + kWaves - 1) / kWaves;
   const int my0 = k0 + wave * rounds, my1 = min(k1, my0 + rounds);
-  int id0 = -1;  // page id of this wave's first tile
-  if (my0 < my1)
-    id0 = uniform(p.block_table[static_cast<int64_t>(cx.b) * p.max_pages + (((t_lo + my0) * kTile) >> p.log2P)]);
-  QueryRows qrows;
-  fetch_query(qrows, p, cx.b, cx.hb, wave, lane);
+  // The opening loads carry no branch (clamped indices; a block table that
+  // may be absent is replaced by the seqlens array), so the compiler's waits
+  // for the query and page ids leave the first tile's loads in flight.
+  const int32_t* const bt_seq =
+      p.max_pages > 0 ? p.block_table + static_cast<int64_t>(cx.b) * p.max_pages : p.seqlens;
+  const int last_pg = max(p.max_pages - 1, 0);
+  // page id of this wave's first tile (a wave without tiles loads one anyway)
+  const int id0 = uniform(bt_seq[min(((t_lo + my0) * kTile) >> p.log2P, last_pg)]);
 
   // page ids of this workgroup's tiles (the launch sizes splits so that they
   // fit the window); loaded together with the query rows
@@ -1017,39 +1049,48 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     pg_first = ((t_lo + k0) * kTile) >> p.log2P;
     n_pg = min((((t_lo + k1 - 1) * kTile) >> p.log2P) - pg_first + 1, kPageWin);
   }
-  const int32_t* bt_row = p.block_table + static_cast<int64_t>(cx.b) * p.max_pages + pg_first;
-  constexpr int kPidPerThread = kPageWin / kThreads;
-  int pid[kPidPerThread];
+  // The page-id window and the query rows come by direct loads (entries past
+  // n_pg repeat an in-range one and are never used): with only direct loads
+  // in flight, the counted wait below leaves the first tile's loads flying
+  // while the query is converted.
+  constexpr int kPidPerWave = kPageWin / kWaves;
+  static_assert(kPidPerWave % 64 == 0, "whole 4-byte direct loads per wave");
 #pragma unroll
-  for (int i = 0; i < kPidPerThread; ++i) {
-    const int k = threadIdx.x + i * kThreads;
-    pid[i] = k < n_pg ? bt_row[k] : -1;
+  for (int i = 0; i < kPidPerWave / 64; ++i) {
+    const int k = wave * kPidPerWave + 64 * i + lane;
+    load4_to_lds(bt_seq + min(pg_first + min(k, max(n_pg - 1, 0)), last_pg),
+                 reinterpret_cast<uint8_t*>(s_pid) + 4 * (wave * kPidPerWave + 64 * i));
   }
+  uint8_t* const qraw = smem + kPkOffStage + 1 * kWaves * kSlotBytes;  // slot 1 of every wave
+  static_assert(kWaves * 4096 <= kWaves * kSlotBytes, "the raw query rows fit one slot row");
+  dma_query(p, cx.b, cx.hb, qraw, smem + kPkOffQr, wave, lane);
   uint32_t src[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) src[c] = lat_src<BITS>(c, lane);
   // the first tile goes out as soon as its page id is in; only it joins the
   // opening burst (every workgroup starts at once), the second follows round
   // 0's scores
-  if (my0 < my1)
-    dma_tile<BITS>(slot_ptr(0, wave), page_of_id(p, id0), ((t_lo + my0) * kTile) & (p.P - 1), src, lane, p);
   // this sequence's packed tiles end at my_end (the sequence may be shorter
   // than the longest one)
-  const int t_end = sr.hi_p > sr.lo_p ? (sr.hi_p + kTile - 1) / kTile - t_lo : 0;
+  const int t_end = max((sr.hi_p + kTile - 1) / kTile - t_lo, 0) * (sr.hi_p > sr.lo_p);
   const int my_end = min(my1, t_end);
-#pragma unroll
-  for (int i = 0; i < kPidPerThread; ++i) {
-    const int k = threadIdx.x + i * kThreads;
-    if (k < n_pg) s_pid[k] = pid[i];
-  }
+  dma_tile<BITS>(slot_ptr(0, wave), page_of_id(p, id0), ((t_lo + my0) * kTile) & (p.P - 1), src, lane, p);
+  wait_tiles_after<BITS>(1);  // this wave's page ids and query rows are in
+  lds_barrier();              // every wave's are
   // staged page id of tile it (not yet wave-uniform: read early, used later)
   auto pid_at = [&](int it) { return s_pid[min(max((((t_lo + it) * kTile) >> p.log2P) - pg_first, 0), kPageWin - 1)]; };
   auto issue = [&](int it, int id, int s) {
     dma_tile<BITS>(slot_ptr(s, wave), page_of_id(p, id), ((t_lo + it) * kTile) & (p.P - 1), src, lane, p);
   };
-  // the query is converted while the first tiles are in flight; slot 2,
-  // which holds it, is first filled after the round-0 barrier
-  publish_query<BITS, true>(qrows, qops, smem + kPkOffQr, wave, lane);
+  // the query is converted while the first tile is in flight; slot 2, which
+  // holds it, is first filled after the round-0 barrier
+  {
+    QueryRows qrows;
+    const int n16 = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qrows.lat[u] = lds_ld<u32x4>(qraw + wave * 4096 + n16 * 256 + 64 * gq + 16 * u);
+    publish_query<BITS, true, false>(qrows, qops, nullptr, wave, lane);
+  }
   // zero weights for round 0's output MFMAs (no previous round)
   for (int off = 16 * threadIdx.x; off < kPkPBytes; off += 16 * kThreads)
     lds_st<u32x4>(smem + kPkOffP + off, u32x4{0, 0, 0, 0});

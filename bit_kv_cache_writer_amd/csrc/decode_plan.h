@@ -17,7 +17,7 @@ constexpr int kPartBytes = kPartRowBytes + 2 * kHeadBlock * 4;
 constexpr int kTargetGroups = 512;  // two workgroups per CU of an MI355X
 constexpr int kDenseTilesPerWg = 8;  // BF16-path tiles per workgroup (two rounds)
 constexpr int kMaxSplits = 128;     // workgroups per (sequence, head block)
-constexpr int kPageWin = 2048;      // page ids a packed workgroup stages in LDS
+constexpr int kPageWin = 512;       // page ids a packed workgroup stages in LDS
 
 // Every (sequence, head block) gets n_dense BF16-path workgroups (sink,
 // recent window and unfinished-page tokens, bounded by sink + local + P - 1)
