@@ -1006,13 +1006,14 @@ __device__ void dense_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], co
 
 // Packed workgroup `ps` of n_ps: packed tiles split evenly, each wave a
 // contiguous run; per wave a ring of kSlots LDS slots filled by direct loads.
-// Software-pipelined rounds, two barriers each:
-//   A: the direct loads of tile r+1 into slot (r+1) % 3 = (r-2) % 3 (free:
-//      every wave finished round r-1's phase A), then the output MFMAs of
-//      round r-1 (P' and every wave's slot (r-1) % 3) together with the
-//      scores of this wave's tile r (slot r % 3)
-//   B: the common running max, P' of round r, the rescale of the output
-//      accumulators
+// Rounds of three phases and two barriers:
+//   A: the scores of this wave's tile r (slot r % 3)
+//   B: the direct loads of tile r+2 into slot (r+2) % 3 = (r-1) % 3 (free:
+//      every wave's round r-1 output MFMAs ran before this round's first
+//      barrier), the common running max, P' of round r, the rescale of the
+//      output accumulators
+//   C: the output MFMAs of round r (P' and every wave's slot r % 3)
+// so each slot is busy for one round and two tiles are in flight.
 template <int BITS>
 __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], const DecodeParams& p, uint8_t* smem,
                           const SeqRanges& sr, const WgCtx& cx, int ps, int n_ps) {
@@ -1091,27 +1092,19 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     for (int u = 0; u < 4; ++u) qrows.lat[u] = lds_ld<u32x4>(qraw + wave * 4096 + n16 * 256 + 64 * gq + 16 * u);
     publish_query<BITS, true, false>(qrows, qops, nullptr, wave, lane);
   }
-  // zero weights for round 0's output MFMAs (no previous round)
-  for (int off = 16 * threadIdx.x; off < kPkPBytes; off += 16 * kThreads)
-    lds_st<u32x4>(smem + kPkOffP + off, u32x4{0, 0, 0, 0});
-  lds_barrier();  // page ids staged, query converted, P' zeroed
+  lds_barrier();  // query converted
   QueryOps<BITS> q;
   load_query<BITS>(q, qops, lane);
 
   float m_run = kNegInf;
   RopeOps ro;
   int ro_page = -1;
-  int id_next = -1;
   for (int r = 0; r < rounds; ++r) {
-    // A: output of round r - 1 (P' is zero before round 0) and scores of
-    // tile r, their LDS reads under one wait so that the two sets of MFMAs
-    // and unpacks can interleave
+    // A: scores of tile r (tile r+1, and after round 0 tile r+2, may still
+    // be in flight)
     const int it = my0 + r;
     bool has = it < my_end;
-    // tile r+1 goes into slot (r+1) % 3, which every wave's output MFMAs of
-    // round r-2 have left (round r-1's first barrier)
-    if (r > 0 && it + 1 < my_end) issue(it + 1, uniform(id_next), (r + 1) % kSlots);
-    if (has) wait_tiles_after<BITS>(r > 0 && it + 1 < my_end ? 1 : 0);  // tile r+1's loads may still fly
+    if (has) wait_tiles_after<BITS>(r > 0 && it + 1 < my_end ? 1 : 0);
     const uint8_t* const slot = slot_ptr(r % kSlots, wave);
     const int pidx = ((t_lo + it) * kTile) >> p.log2P;
     if (has && pidx != ro_page) {  // (a page missing from the block table only spoils its own tiles)
@@ -1123,7 +1116,6 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     const int id_cur = pid_at(it), id_1 = pid_at(it + 1), id_2 = pid_at(it + 2);
     ScoreIn<BITS> si;
     load_score_in<BITS>(si, slot, n16, gq);
-    packed_pv<BITS>(o, smem, (r + kSlots - 1) % kSlots, wave, n16, gq);
     has = has && page_of_id(p, uniform(id_cur)) != nullptr;
     f32x4 acc[6];
     score_mfma<BITS>(acc, si, q, ro);
@@ -1135,8 +1127,10 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
 
-    // B: softmax of round r (tile r+2 is issued at the top of the next round)
-    id_next = id_2;
+    // B: tile r+2 into slot (r+2) % 3 = (r-1) % 3, which every wave's output
+    // MFMAs of round r-1 have left (they ran before this round's barrier);
+    // the common running max and P' of round r
+    if (it + 2 < my_end) issue(it + 2, uniform(id_2), (r + 2) % kSlots);
     float ah[4];
     bool raised;
     const float alpha = raise_max(m_run, m_o, ah, raised, smax, n16, gq);
@@ -1154,8 +1148,10 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     }
     rescale_out(o, ah, raised);
     lds_barrier();
+
+    // C: output MFMAs of round r (P' and every wave's slot r % 3)
+    packed_pv<BITS>(o, smem, r % kSlots, wave, n16, gq);
   }
-  if (rounds > 0) packed_pv<BITS>(o, smem, (rounds + kSlots - 1) % kSlots, wave, n16, gq);  // the last round's output
   // no direct load outlives the workgroup, and every wave's last reads of P'
   // and of the slots are done before finish reuses that LDS
   __syncthreads();
