@@ -1008,12 +1008,13 @@ __device__ void dense_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], co
 // contiguous run; per wave a ring of kSlots LDS slots filled by direct loads.
 // Rounds of three phases and two barriers:
 //   A: the scores of this wave's tile r (slot r % 3)
-//   B: the direct loads of tile r+2 into slot (r+2) % 3 = (r-1) % 3 (free:
+//   B: the common running max, P' of round r, the rescale of the output
+//      accumulators
+//   C: the output MFMAs of round r (P' and every wave's slot r % 3), then
+//      the direct loads of tile r+2 into slot (r+2) % 3 = (r-1) % 3 (free:
 //      every wave's round r-1 output MFMAs ran before this round's first
-//      barrier), the common running max, P' of round r, the rescale of the
-//      output accumulators
-//   C: the output MFMAs of round r (P' and every wave's slot r % 3)
-// so each slot is busy for one round and two tiles are in flight.
+//      barrier)
+// so each slot is busy for one round and the next tiles stay in flight.
 template <int BITS>
 __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], const DecodeParams& p, uint8_t* smem,
                           const SeqRanges& sr, const WgCtx& cx, int ps, int n_ps) {
@@ -1127,10 +1128,7 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
 
-    // B: tile r+2 into slot (r+2) % 3 = (r-1) % 3, which every wave's output
-    // MFMAs of round r-1 have left (they ran before this round's barrier);
-    // the common running max and P' of round r
-    if (it + 2 < my_end) issue(it + 2, uniform(id_2), (r + 2) % kSlots);
+    // B: the common running max and P' of round r
     float ah[4];
     bool raised;
     const float alpha = raise_max(m_run, m_o, ah, raised, smax, n16, gq);
@@ -1149,8 +1147,11 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     rescale_out(o, ah, raised);
     lds_barrier();
 
-    // C: output MFMAs of round r (P' and every wave's slot r % 3)
+    // C: output MFMAs of round r (P' and every wave's slot r % 3), then tile
+    // r+2 into slot (r+2) % 3 = (r-1) % 3, which every wave's output MFMAs of
+    // round r-1 have left (they ran before this round's first barrier)
     packed_pv<BITS>(o, smem, r % kSlots, wave, n16, gq);
+    if (it + 2 < my_end) issue(it + 2, uniform(id_2), (r + 2) % kSlots);
   }
   // no direct load outlives the workgroup, and every wave's last reads of P'
   // and of the slots are done before finish reuses that LDS
