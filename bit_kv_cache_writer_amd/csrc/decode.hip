@@ -117,6 +117,8 @@ struct DecodeParams {
   const uint16_t* sink;
   const uint16_t* ring;
   const uint16_t* tail;
+  const uint8_t* fallback;  // load source for a tile without a page (see dma_tile)
+  uint32_t off_mask;        // ~0, or 0 when there is no page pool (max_seqlen = 0)
   uint8_t* parts;
   float* out;
   float* lse;
@@ -436,29 +438,54 @@ __device__ inline uint32_t lat_src(int c, int lane) {
   }
 }
 
+// Per-lane byte offsets of a tile's direct loads: the latent-code loads
+// relative to the tile's first code row, and the side load (lanes 0-31: k_R
+// codes, 32-47: latent metadata, 48-63: the page's k_R metadata) relative to
+// the page as side_a + slot0 * side_k.  All fit 32 bits (a page is < 64 KB),
+// so every load takes a wave-uniform 64-bit base plus a 32-bit lane offset and
+// the per-tile address work is one multiply-add.
+struct TileSrc {
+  uint32_t lat[4];
+  uint32_t side_a, side_k;
+};
+
+template <int BITS>
+__device__ inline TileSrc tile_src(const DecodeParams& p, int lane) {
+  TileSrc t;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) t.lat[c] = lat_src<BITS>(c, lane) & p.off_mask;
+  uint32_t a = static_cast<uint32_t>(p.rope_meta_off) + 16u * static_cast<uint32_t>(lane - 48), k = 0;
+  if (lane < 48) {
+    a = static_cast<uint32_t>(p.latent_meta_off) + 16u * static_cast<uint32_t>(lane - 32);
+    k = 16;
+  }
+  if (lane < 32) {
+    a = static_cast<uint32_t>(p.rope_codes_off) + 16u * static_cast<uint32_t>(lane);
+    k = kRopeRowBytes;
+  }
+  t.side_a = a & p.off_mask;
+  t.side_k = k & p.off_mask;
+  return t;
+}
+
 // Issues the direct loads of one 16-token tile (first slot slot0 of a
 // wave-uniform page) into an LDS slot: always TileGeom<BITS>::kLoads
 // vector-memory instructions, so the waits below can count them.
 template <int BITS>
-__device__ inline void dma_tile(uint8_t* slot, const uint8_t* page, int slot0, const uint32_t (&src)[4], int lane,
+__device__ inline void dma_tile(uint8_t* slot, const uint8_t* page, int slot0, const TileSrc& ts,
                                 const DecodeParams& p) {
   using G = TileGeom<BITS>;
-  // a page missing from the block table loads 16 bytes of the query instead
-  // (the tile is skipped); selected rather than branched, so that later waits
-  // can count these loads
+  // a page missing from the block table loads from the fallback buffer instead
+  // (page 0 of the pool, or the query when there is no pool and the offsets are
+  // all zero; the tile is skipped); selected rather than branched, so that later
+  // waits can count these loads
   const bool ok = page != nullptr;
-  const uint8_t* const base = ok ? page : reinterpret_cast<const uint8_t*>(p.q_lat);
-  const int64_t lat = ok ? slot0 * G::kLatRow : 0;
+  const uint8_t* const lat_base = ok ? page + slot0 * G::kLatRow : p.fallback;
+  const uint8_t* const side_base = ok ? page : p.fallback;
+  const uint32_t s0 = ok ? static_cast<uint32_t>(slot0) : 0u;
 #pragma unroll
-  for (int c = 0; c < G::kLatLoads; ++c) load_to_lds(base + (ok ? lat + src[c] : 0), slot + 1024 * c);
-  // lanes 0-31: k_R codes, 32-47: latent metadata, 48-63: the page's k_R
-  // metadata (arithmetic selects, no divergent branch)
-  const int64_t s_rope = p.rope_codes_off + slot0 * kRopeRowBytes + 16 * lane;
-  const int64_t s_meta = p.latent_meta_off + slot0 * 16 + 16 * (lane - 32);
-  const int64_t s_rmeta = p.rope_meta_off + 16 * (lane - 48);
-  int64_t s = lane < 48 ? s_meta : s_rmeta;
-  s = lane < 32 ? s_rope : s;
-  load_to_lds(base + (ok ? s : 0), slot + G::kOffRope);
+  for (int c = 0; c < G::kLatLoads; ++c) load_to_lds(lat_base + ts.lat[c], slot + 1024 * c);
+  load_to_lds(side_base + (ts.side_a + s0 * ts.side_k), slot + G::kOffRope);
 }
 
 // Waits until at most `after` tiles' direct loads are still in flight (the
@@ -1033,7 +1060,17 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   const int t_lo = p.t_lo, T = p.t_count;
   const int per = (T + n_ps - 1) / n_ps;
   const int k0 = min(T, ps * per), k1 = min(T, k0 + per);
-  const int rounds = (k1 - k0 + kWaves - 1) / kWaves;
+  int rounds = (k1 - k0 + kWaves - 1) / kWaves;
+  {
+    // Long runs are rounded up to whole pages per wave, when that costs at
+    // most 1/16 more rounds: then every wave changes page in the same round
+    // and the positional-key operands are rebuilt in one round of every P/16,
+    // instead of some wave rebuilding (and holding the barriers) in most
+    // rounds.
+    const int tpp = p.P / kTile;
+    const int r_al = (rounds + tpp - 1) / tpp * tpp;
+    if ((r_al - rounds) * 16 <= rounds) rounds = r_al;
+  }
   const int my0 = k0 + wave * rounds, my1 = min(k1, my0 + rounds);
   // The opening loads carry no branch (clamped indices; a block table that
   // may be absent is replaced by the seqlens array), so the compiler's waits
@@ -1066,9 +1103,7 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   uint8_t* const qraw = smem + kPkOffStage + 1 * kWaves * kSlotBytes;  // slot 1 of every wave
   static_assert(kWaves * 4096 <= kWaves * kSlotBytes, "the raw query rows fit one slot row");
   dma_query(p, cx.b, cx.hb, qraw, smem + kPkOffQr, wave, lane);
-  uint32_t src[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) src[c] = lat_src<BITS>(c, lane);
+  const TileSrc src = tile_src<BITS>(p, lane);
   // the first tile goes out as soon as its page id is in; only it joins the
   // opening burst (every workgroup starts at once), the second follows round
   // 0's scores
@@ -1076,13 +1111,13 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   // than the longest one)
   const int t_end = max((sr.hi_p + kTile - 1) / kTile - t_lo, 0) * (sr.hi_p > sr.lo_p);
   const int my_end = min(my1, t_end);
-  dma_tile<BITS>(slot_ptr(0, wave), page_of_id(p, id0), ((t_lo + my0) * kTile) & (p.P - 1), src, lane, p);
+  dma_tile<BITS>(slot_ptr(0, wave), page_of_id(p, id0), ((t_lo + my0) * kTile) & (p.P - 1), src, p);
   wait_tiles_after<BITS>(1);  // this wave's page ids and query rows are in
   lds_barrier();              // every wave's are
   // staged page id of tile it (not yet wave-uniform: read early, used later)
   auto pid_at = [&](int it) { return s_pid[min(max((((t_lo + it) * kTile) >> p.log2P) - pg_first, 0), kPageWin - 1)]; };
   auto issue = [&](int it, int id, int s) {
-    dma_tile<BITS>(slot_ptr(s, wave), page_of_id(p, id), ((t_lo + it) * kTile) & (p.P - 1), src, lane, p);
+    dma_tile<BITS>(slot_ptr(s, wave), page_of_id(p, id), ((t_lo + it) * kTile) & (p.P - 1), src, p);
   };
   // the query is converted while the first tile is in flight; slot 2, which
   // holds it, is first filled after the round-0 barrier
@@ -1390,6 +1425,11 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   p.q_lat = static_cast<const uint16_t*>(q_lat);
   p.q_rope = static_cast<const uint16_t*>(q_rope);
   p.pool = static_cast<const uint8_t*>(page_pool);
+  {
+    const bool pool_ok = page_pool != nullptr && num_pool_pages > 0;
+    p.fallback = pool_ok ? p.pool : static_cast<const uint8_t*>(q_lat);
+    p.off_mask = pool_ok ? ~0u : 0u;
+  }
   p.block_table = block_table;
   p.seqlens = seqlens;
   p.sink = static_cast<const uint16_t*>(sink_buf);
