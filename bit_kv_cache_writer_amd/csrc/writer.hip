@@ -219,28 +219,15 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   if (static_cast<int64_t>(pg) * P >= end) return;
   const int last_page = (end - 1) / P;
   if (last_page >= p.max_pages) return;  // positions beyond the block table
-  const int page_id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pg];
-  if (page_id < 0 || page_id >= p.num_pool_pages) return;
-  uint8_t* page = p.pool + static_cast<int64_t>(page_id) * p.page_bytes;
   const int tb = max(sb, pg * P), te = min(end, (pg + 1) * P);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint16_t* tail = p.tail + static_cast<int64_t>(b) * P * kRopeDim;
 
-  // Latent codes + metadata, BF16 sink / ring copies.
-  for (int t = tb + wave; t < te; t += kWaves) {
-    const int64_t row = r0 + (t - sb);
-    const uint16_t* xl = p.c_kv + row * kLatentDim;
-    const uint16_t* xr = p.k_r + row * kRopeDim;
-    write_latent_token(p, xl, page, t - pg * P, lane);
-    if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, xl, xr, lane);
-    if (p.local > 0 && t >= end - p.local)
-      copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, xl, xr, lane);
-  }
-
   // k_R rows of a page that becomes full in this call (tail buffer for tokens
   // of earlier calls, input rows for new ones) go straight from global memory
-  // into LDS, all at once (16 bytes per lane and load); the barrier before
-  // their reduction waits for them.
+  // into LDS, all at once (16 bytes per lane and load), before the page id is
+  // looked up: they do not depend on it.  The barrier before their reduction
+  // waits for them.
   __shared__ uint4 s_rows[256 * kRopeDim / 8];  // P x 64 bf16
   const bool completes = (pg + 1) * P <= end;
   if (completes) {
@@ -254,36 +241,78 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
                                        16, 0, 0);
     }
   }
+  const int page_id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pg];
+  if (page_id < 0 || page_id >= p.num_pool_pages) {
+    __syncthreads();  // no direct load outlives the workgroup
+    return;
+  }
+  uint8_t* page = p.pool + static_cast<int64_t>(page_id) * p.page_bytes;
 
-  // k_R of a page that becomes full: per channel over its P tokens, reduced
-  // from the rows staged in LDS.
+  // Latent codes + metadata, BF16 sink / ring copies.
+  for (int t = tb + wave; t < te; t += kWaves) {
+    const int64_t row = r0 + (t - sb);
+    const uint16_t* xl = p.c_kv + row * kLatentDim;
+    const uint16_t* xr = p.k_r + row * kRopeDim;
+    write_latent_token(p, xl, page, t - pg * P, lane);
+    if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, xl, xr, lane);
+    if (p.local > 0 && t >= end - p.local)
+      copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, xl, xr, lane);
+  }
+
+  // k_R of a page that becomes full: per channel over its P tokens.  Thread
+  // (part, octet q) takes channels 8q .. 8q + 7 of rows part, part + 32, ...
+  // (16-byte LDS reads); the 8 parts of a wave meet by lane swaps, the four
+  // waves in LDS.
   __shared__ float s_min[kWaves][kRopeDim], s_max[kWaves][kRopeDim];
   __shared__ float s_minf[kRopeDim], s_sf[kRopeDim];
-  __shared__ uint8_t s_code[256 * kRopeDim];
   if (completes) {
     __syncthreads();
-    const uint16_t* rows = reinterpret_cast<const uint16_t*>(s_rows);
-    const int c = threadIdx.x & 63, part = threadIdx.x >> 6;
-    float mn = 3.0e38f, mx = -3.0e38f;
-    for (int s = part; s < P; s += kWaves) {
-      const float v = canon_zero(bf16_to_f32(rows[s * kRopeDim + c]));
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
-    }
-    s_min[part][c] = mn;
-    s_max[part][c] = mx;
-    __syncthreads();
-    if (part == 0) {
+    const int q = threadIdx.x & 7, part = threadIdx.x >> 3;
+    float mn[8], mx[8];
 #pragma unroll
-      for (int q = 1; q < kWaves; ++q) {
-        mn = fminf(mn, s_min[q][c]);
-        mx = fmaxf(mx, s_max[q][c]);
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = 3.0e38f;
+      mx[e] = -3.0e38f;
+    }
+    for (int s = part; s < P; s += kThreads / 8) {
+      const uint4 w = s_rows[s * (kRopeDim / 8) + q];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = canon_zero(bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu));
+        mn[e] = fminf(mn[e], v);
+        mx[e] = fmaxf(mx[e], v);
       }
-      const uint16_t mh = f16_round_down(mn);
+    }
+#pragma unroll
+    for (int m = 8; m < 64; m <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mn[e] = fminf(mn[e], __shfl_xor(mn[e], m, 64));
+        mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], m, 64));
+      }
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s_min[wave][8 * q + e] = mn[e];
+        s_max[wave][8 * q + e] = mx[e];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < kRopeDim) {
+      const int c = threadIdx.x;
+      float cmn = s_min[0][c], cmx = s_max[0][c];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        cmn = fminf(cmn, s_min[w][c]);
+        cmx = fmaxf(cmx, s_max[w][c]);
+      }
+      const uint16_t mh = f16_round_down(cmn);
       const float minf = f16_to_f32(mh);
-      const float span = mx - minf;
-      const float s = span / 15.0f;
-      const uint16_t sh = f16_round_up(s);
+      const float span = cmx - minf;
+      const float sc = span / 15.0f;
+      const uint16_t sh = f16_round_up(sc);
       s_minf[c] = minf;
       s_sf[c] = f16_to_f32(sh);
       uint16_t* meta = reinterpret_cast<uint16_t*>(page + p.rope_meta_off);
@@ -291,26 +320,30 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       meta[kRopeDim + c] = mh;
     }
     __syncthreads();
-    const float minf = s_minf[c], sf = s_sf[c];
-    for (int s = part; s < P; s += kWaves) {
-      uint32_t code = 0;
-      if (sf > 0.0f) {
-        const float t = (canon_zero(bf16_to_f32(rows[s * kRopeDim + c])) - minf) / sf;
-        float r = rintf(t);
-        r = fminf(fmaxf(r, 0.0f), 15.0f);
-        code = static_cast<uint32_t>(r);
-      }
-      s_code[s * kRopeDim + c] = static_cast<uint8_t>(code);
-    }
-    __syncthreads();
-    // pack: 8 channels per dword, P rows x 8 dwords
-    uint32_t* rc = reinterpret_cast<uint32_t*>(page + p.rope_codes_off);
-    for (int i = threadIdx.x; i < P * 8; i += kThreads) {
-      const uint8_t* cs = s_code + (i >> 3) * kRopeDim + (i & 7) * 8;
-      uint32_t w = 0;
+    // codes, packed as they are made: dword i = row i / 8, channels 8 (i % 8) .. + 7
+    float minf[8], sf[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) w |= static_cast<uint32_t>(cs[k]) << (4 * k);
-      rc[i] = w;
+    for (int e = 0; e < 8; ++e) {
+      minf[e] = s_minf[8 * q + e];
+      sf[e] = s_sf[8 * q + e];
+    }
+    uint32_t* rc = reinterpret_cast<uint32_t*>(page + p.rope_codes_off);
+    for (int s = part; s < P; s += kThreads / 8) {
+      const uint4 w = s_rows[s * (kRopeDim / 8) + q];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t code = 0;
+        if (sf[e] > 0.0f) {
+          const float t = (canon_zero(bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu)) - minf[e]) / sf[e];
+          float r = rintf(t);
+          r = fminf(fmaxf(r, 0.0f), 15.0f);
+          code = static_cast<uint32_t>(r);
+        }
+        packed |= code << (4 * e);
+      }
+      rc[s * (kRopeDim / 8) + q] = packed;
     }
   }
 
