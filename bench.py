@@ -33,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
+FLOPS_PER_TOKEN_HEAD = 2 * 576 + 2 * 512  # QK over 576 channels + PV over 512
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "bit_kv_cache_writer_amd", "csrc", "decode.hip")
 
@@ -246,6 +248,21 @@ def main() -> int:
     dec_bytes = alg["total"] * w.batch
     achieved = dec_bytes / (dec_us * 1e-6) / 1e9
     packed_gbs = alg["cache"] * w.batch / (dec_us * 1e-6) / 1e9
+    # the binding roofline: HBM time of the algorithmic bytes vs matrix-core
+    # time of the useful flops (every cached token, every head)
+    dec_flops = FLOPS_PER_TOKEN_HEAD * n * w.heads * w.batch
+    tflops = dec_flops / (dec_us * 1e-6) / 1e12
+    hbm_bound = dec_bytes / (HBM_PEAK_GBS * 1e9) >= dec_flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    hbm_roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    mfma_roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+    roof = dict(hbm_roof if hbm_bound else mfma_roof)
+    roof.update({"traffic": measured_traffic(w.name),
+                 "kernel": "mla_lowbit_decode = decode_kernel + combine_kernel (one call per layer)",
+                 "bytes_per_launch": dec_bytes, "flops_per_launch": dec_flops,
+                 "other": mfma_roof if hbm_bound else hbm_roof})
+    write_us = us_layer - dec_us
 
     cpu = None
     if not args.no_cpu:
@@ -271,15 +288,14 @@ def main() -> int:
                    "step": "per layer: append 1 token per sequence (completes a page) + decode over N",
                    "value": "decode (attention + split merge) us per layer"},
         "decode_us": round(dec_us, 3),
-        "write_us": round(us_layer - dec_us, 3),
+        "write_us": round(write_us, 3),
+        "writer_tokens_per_s": round(w.batch / (write_us * 1e-6), 1),
         "step_us_per_layer": round(us_layer, 3),
         "packed_cache_gbs": round(packed_gbs, 1),
+        "packed_cache_frac_of_hbm": round(packed_gbs / HBM_PEAK_GBS, 4),
         "writer_bulk_fill_gbs": round(fill_bytes / (np.median(fill_ms) * 1e-3) / 1e9, 1),
         "wall_s": round(wall, 3),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "mla_lowbit_decode = decode_kernel + combine_kernel (one call per layer)",
-                     "bytes_per_launch": dec_bytes},
+        "roofline": roof,
         "cpu_baseline": cpu,
         "context_h20": {"raq_mla_us_per_layer": 12.6, "flashmla_us_per_layer": 17.4,
                         "tpot_ms": [5.97, 6.56]},
