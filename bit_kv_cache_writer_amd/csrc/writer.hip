@@ -120,9 +120,7 @@ __device__ inline uint32_t wave_kth_smallest(const uint32_t (&a)[8], int k) {
 }
 
 // Quantizes one latent token (one wave; lane l holds channels 8l..8l+7).
-__device__ void write_latent_token(const WriterParams& p, const uint16_t* src, uint8_t* page,
-                                   int slot, int lane) {
-  const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * lane);
+__device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8_t* page, int slot, int lane) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   float x[8];
 #pragma unroll
@@ -197,10 +195,22 @@ __device__ void write_latent_token(const WriterParams& p, const uint16_t* src, u
   }
 }
 
-// Copies one token's BF16 row [c_KV 512 | k_R 64] (1152 B) with one wave.
-__device__ inline void copy_row(uint16_t* dst, const uint16_t* ckv, const uint16_t* kr, int lane) {
-  reinterpret_cast<uint4*>(dst)[lane] = reinterpret_cast<const uint4*>(ckv)[lane];
-  if (lane < 8) reinterpret_cast<uint4*>(dst + kLatentDim)[lane] = reinterpret_cast<const uint4*>(kr)[lane];
+// Stores one token's BF16 row [c_KV 512 | k_R 64] (1152 B) with one wave:
+// lane l holds c_KV bytes 16 l .. 16 l + 15 and (l < 8) k_R bytes 16 l ...
+__device__ inline void copy_row(uint16_t* dst, const uint4 ckv, const uint4 kr, int lane) {
+  reinterpret_cast<uint4*>(dst)[lane] = ckv;
+  if (lane < 8) reinterpret_cast<uint4*>(dst + kLatentDim)[lane] = kr;
+}
+
+// One token's rows as a wave holds them (see copy_row).
+struct TokenRows {
+  uint4 ckv, kr;
+};
+__device__ inline TokenRows load_token(const WriterParams& p, int64_t row, int lane) {
+  TokenRows r;
+  r.ckv = reinterpret_cast<const uint4*>(p.c_kv + row * kLatentDim)[lane];
+  r.kr = reinterpret_cast<const uint4*>(p.k_r + row * kRopeDim)[lane & 7];
+  return r;
 }
 
 __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
@@ -241,6 +251,9 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
                                        16, 0, 0);
     }
   }
+  // this wave's first token goes out with them (its row index is clamped
+  // into the input: a wave without a token reads a row it does not use)
+  TokenRows cur = load_token(p, r0 + (min(tb + wave, te - 1) - sb), lane);
   const int page_id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pg];
   if (page_id < 0 || page_id >= p.num_pool_pages) {
     __syncthreads();  // no direct load outlives the workgroup
@@ -250,13 +263,12 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
 
   // Latent codes + metadata, BF16 sink / ring copies.
   for (int t = tb + wave; t < te; t += kWaves) {
-    const int64_t row = r0 + (t - sb);
-    const uint16_t* xl = p.c_kv + row * kLatentDim;
-    const uint16_t* xr = p.k_r + row * kRopeDim;
-    write_latent_token(p, xl, page, t - pg * P, lane);
-    if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, xl, xr, lane);
+    const TokenRows x = cur;
+    if (t + kWaves < te) cur = load_token(p, r0 + (t + kWaves - sb), lane);
+    write_latent_token(p, x.ckv, page, t - pg * P, lane);
+    if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, x.ckv, x.kr, lane);
     if (p.local > 0 && t >= end - p.local)
-      copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, xl, xr, lane);
+      copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, x.ckv, x.kr, lane);
   }
 
   // k_R of a page that becomes full: per channel over its P tokens.  Thread
