@@ -83,20 +83,48 @@ __device__ inline uint16_t f16_round_up(float x) {
   return h;
 }
 
+// Min / max over each 16-lane row by DPP lane moves (VALU, no LDS round
+// trip): swap neighbours, swap pairs, then rotate the row by 4 and by 8.
+template <int kCtrl>
+__device__ inline float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
 __device__ inline float wave_min16(float v) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v = fminf(v, __shfl_xor(v, m, 64));
-  return v;
+  v = fminf(v, dpp_move<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fminf(v, dpp_move<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fminf(v, dpp_move<0x124>(v));  // row_ror:4
+  return fminf(v, dpp_move<0x128>(v));  // row_ror:8
 }
 __device__ inline float wave_max16(float v) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  v = fmaxf(v, dpp_move<0xB1>(v));
+  v = fmaxf(v, dpp_move<0x4E>(v));
+  v = fmaxf(v, dpp_move<0x124>(v));
+  return fmaxf(v, dpp_move<0x128>(v));
 }
-__device__ inline int wave_sum(int v) {
+// Min / max over lanes l, l ^ 8, l ^ 16, ... (the 8 lanes of equal l % 8):
+// a DPP row rotation by 8, then the row-swap permutes across 16 and 32 lanes.
+__device__ inline float lanes_min_mod8(float v) {
+  v = fminf(v, dpp_move<0x128>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ inline float lanes_max_mod8(float v) {
+  v = fmaxf(v, dpp_move<0x128>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// Number of the wave's 8 x 64 values a[i] with a[i] <= t (wave-uniform), by
+// ballots: one compare and one popcount per register, no cross-lane round trip.
+__device__ inline int wave_count_le(const uint32_t (&a)[8], uint32_t t) {
+  int c = 0;
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  for (int i = 0; i < 8; ++i) c += __popcll(__ballot(a[i] <= t));
+  return c;
 }
 __device__ inline uint32_t wave_min_u32(uint32_t v) {
 #pragma unroll
@@ -110,11 +138,7 @@ __device__ inline uint32_t wave_kth_smallest(const uint32_t (&a)[8], int k) {
   uint32_t prefix = 0;
   for (int b = 14; b >= 0; --b) {
     const uint32_t t = prefix | ((1u << b) - 1u);
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c += a[i] <= t ? 1 : 0;
-    c = wave_sum(c);
-    if (c < k + 1) prefix |= 1u << b;
+    if (wave_count_le(a, t) < k + 1) prefix |= 1u << b;
   }
   return prefix;
 }
@@ -133,14 +157,11 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = (__float_as_uint(x[i]) >> 16) & 0x7FFFu;
     const uint32_t lo = wave_kth_smallest(a, p.clip_lo);
-    int c_le = 0;
+    const int c_le = wave_count_le(a, lo);
     uint32_t above = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      c_le += a[i] <= lo ? 1 : 0;
+    for (int i = 0; i < 8; ++i)
       if (a[i] > lo) above = min(above, a[i]);
-    }
-    c_le = wave_sum(c_le);
     above = wave_min_u32(above);
     const uint32_t hi = (c_le >= p.clip_hi + 1) ? lo : above;
     const float flo = bf16_to_f32(lo), fhi = bf16_to_f32(hi);
@@ -273,7 +294,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
 
   // k_R of a page that becomes full: per channel over its P tokens.  Thread
   // (part, octet q) takes channels 8q .. 8q + 7 of rows part, part + 32, ...
-  // (16-byte LDS reads); the 8 parts of a wave meet by lane swaps, the four
+  // (16-byte LDS reads); the 8 parts of a wave meet by lane moves, the four
   // waves in LDS.
   __shared__ float s_min[kWaves][kRopeDim], s_max[kWaves][kRopeDim];
   __shared__ float s_minf[kRopeDim], s_sf[kRopeDim];
@@ -297,12 +318,9 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       }
     }
 #pragma unroll
-    for (int m = 8; m < 64; m <<= 1) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        mn[e] = fminf(mn[e], __shfl_xor(mn[e], m, 64));
-        mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], m, 64));
-      }
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = lanes_min_mod8(mn[e]);
+      mx[e] = lanes_max_mod8(mx[e]);
     }
     if (lane < 8) {
 #pragma unroll
