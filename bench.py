@@ -161,6 +161,81 @@ def cpu_baseline(w, n_seq_sample: int, budget_s: float = 12.0) -> dict:
             "append_us_per_layer": t_app * scale1 * 1e6, "sample_seconds": round(t_app + t_dec + wall, 3)}
 
 
+def sweep(steps: int) -> int:
+    """Context sweep (timing only; parity is covered by the tests): C4R4
+    decode, 16 heads, page 128, sink 4 + local 128, batch 1 and 8, N = 1K to
+    1M cached tokens.  Inputs are drawn on the GPU from a seeded generator
+    (N(0,1) latent and queries, k_R N(0,1) with channels 7, 23, 39, 55 x20,
+    rounded to bf16); each configuration uses enough layer caches for >= 1 GB
+    of packed pages.  One JSON line per configuration."""
+    import torch
+
+    from bit_kv_cache_writer_amd import mla
+
+    mla.lib()
+    lay = mla.Layout(128, 4, 0.0, 4, 128)
+    page_bytes = mla.mla_lowbit_layout_query(lay)["page_bytes"]
+    heads, scale = 16, 1.0 / math.sqrt(192.0)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    outl = torch.ones(64, device="cuda")
+    outl[[7, 23, 39, 55]] = 20.0
+
+    def bf16_rows(n, width, mult=None):
+        x = torch.randn((n, width), generator=gen, device="cuda", dtype=torch.float32)
+        if mult is not None:
+            x *= mult
+        return x.to(torch.bfloat16).view(torch.int16)
+
+    class W:  # the shape algorithmic_decode_bytes reads
+        latent_bits, page_size, sink, local = 4, 128, 4, 128
+
+    for B in (1, 8):
+        for N in (1024, 4096, 16384, 65536, 262144, 1048576):
+            W.heads = heads
+            max_pages = (N + 127) // 128
+            rng = np.random.default_rng(np.random.SeedSequence([7, B, N]))
+            n_pool = int(math.ceil(B * max_pages * 1.25))
+            bt = rng.permutation(n_pool)[: B * max_pages].astype(np.int32).reshape(B, max_pages)
+            layers = min(64, max(2, math.ceil(1.0e9 / (B * max_pages * page_bytes))))
+            caches = []
+            for _ in range(layers):
+                c = mla.DeviceCache(lay, B, max_pages, bt, n_pool)
+                done = 0
+                while done < N:
+                    t = min(65536, N - done)
+                    c.append(bf16_rows(B * t, 512), bf16_rows(B * t, 64, outl), [t] * B)
+                    done += t
+                caches.append(c)
+            q_lat = bf16_rows(B * heads, 512).view(B, heads, 512).contiguous()
+            q_rope = bf16_rows(B * heads, 64).view(B, heads, 64).contiguous()
+            stream = torch.cuda.current_stream()
+            for c in caches:
+                c.decode(q_lat, q_rope, scale, stream=stream)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps * layers)]
+            for st in range(steps):
+                for li, c in enumerate(caches):
+                    e = evs[st * layers + li]
+                    e[0].record(stream)
+                    c.decode(q_lat, q_rope, scale, stream=stream)
+                    e[1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1000.0)
+            alg = algorithmic_decode_bytes(W, N)
+            byts = alg["total"] * B
+            gbs = byts / (us * 1e-6) / 1e9
+            print(json.dumps({"sweep": "C4R4 decode, 16 heads, page 128, sink 4 + local 128",
+                              "batch": B, "cached_tokens": N, "layers": layers, "decode_us": round(us, 3),
+                              "algorithmic_bytes": byts, "hbm_gbs": round(gbs, 1),
+                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                              "workspace_bytes": mla.mla_lowbit_decode_workspace(lay, B, heads, N)}), flush=True)
+            del caches
+            torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +245,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0, help="0: enough layers for >= 1 GB of packed cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true", help="time a plain 1 GiB copy and exit")
+    ap.add_argument("--sweep", action="store_true", help="context sweep 1K..1M at batch 1 and 8 (JSON lines)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -186,6 +262,8 @@ def main() -> int:
         return 2
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.sweep:
+        return sweep(max(1, min(args.steps, 5)))
     mla.lib()
     w = wl.WORKLOADS[args.workload]
     lay = mla.Layout(w.page_size, w.latent_bits, w.clip_q, w.sink, w.local)

@@ -1302,74 +1302,102 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   }
 }
 
-// Merge of the split partials of one (sequence, head block): grid =
-// (sequence, head block) x 16 blocks of 32 channels, 64 threads; thread t takes
-// channel 32 block + t / 2, heads 8 (t % 2) .. + 7 (16 bytes of the
-// channel-major partial rows).  A partial holds the split's normalized output
-// O_s / l_s (fp16) and (m_s, l_s); the merge weights split s by
-// 2^(m_s - M) l_s / sum over splits, M = max_s m_s, per head (the weights are
-// formed by all 64 threads: head t % 16, every fourth split).
-__global__ void __launch_bounds__(64) combine_kernel(const uint8_t* __restrict__ parts, float* __restrict__ out,
-                                                     float* __restrict__ lse, int heads, int n_hb, int n_splits) {
-  __shared__ __attribute__((aligned(16))) float s_ml[kMaxSplits * 2 * kHeadBlock];  // [split][m 16, l 16]
-  __shared__ __attribute__((aligned(16))) float s_w[kMaxSplits * kHeadBlock];  // [split][head] weights
-  __shared__ __attribute__((aligned(16))) float s_red[9 * kHeadBlock];  // partial max, partial sums, 1 / sum
-  const int grp = blockIdx.x >> 4, cb = blockIdx.x & 15;
+// Merge of the split partials of one (sequence, head block).  A workgroup
+// takes CB channels: its 2 CB columns are (channel, heads 8 (col % 2) .. + 7),
+// 16 bytes of the channel-major partial rows each, and its SG split groups
+// take the splits g, g + SG, ... of every column with up to 16 row loads in
+// flight per thread; the split groups' sums meet in LDS at the end.  Grid =
+// (sequence, head block) x 512 / CB.  A partial holds the split's normalized
+// output O_s / l_s (fp16) and (m_s, l_s); the merge weights split s by
+// 2^(m_s - M) l_s / sum over splits, M = max_s m_s, per head (formed by all
+// threads: head t % 16, splits t / 16 (mod threads / 16)).
+template <int CB, int SG>
+struct Cmb {
+  static constexpr int kThreads = 2 * CB * SG;
+  static constexpr int kQ = kThreads / kHeadBlock;  // split groups of the weights
+  static constexpr int kBlocks = kLatentDim / CB;   // workgroups per (sequence, head block)
+  static constexpr int kMaxS = SG == 1 ? 32 : kMaxSplits;  // splits it is launched for
+};
+
+// Dynamic LDS of combine_kernel<CB, SG> for n splits: s_ml [split][m 16, l 16],
+// s_w [split][head], s_red [2][kQ][head] + [head], s_acc [thread][8].
+template <int CB, int SG>
+constexpr size_t combine_lds_bytes(int n_splits) {
+  return static_cast<size_t>(n_splits) * 3 * kHeadBlock * 4 + (2 * Cmb<CB, SG>::kQ + 1) * kHeadBlock * 4 +
+         (SG > 1 ? Cmb<CB, SG>::kThreads * 8 * 4 : 0);
+}
+
+template <int CB, int SG>
+__global__ void __launch_bounds__((Cmb<CB, SG>::kThreads)) combine_kernel(const uint8_t* __restrict__ parts,
+                                                                       float* __restrict__ out, float* __restrict__ lse,
+                                                                       int heads, int n_hb, int n_splits) {
+  using C = Cmb<CB, SG>;
+  extern __shared__ __attribute__((aligned(16))) float cmb_lds[];
+  float* const s_ml = cmb_lds;
+  float* const s_w = s_ml + n_splits * 2 * kHeadBlock;
+  float* const s_red = s_w + n_splits * kHeadBlock;
+  float* const s_acc = s_red + (2 * C::kQ + 1) * kHeadBlock;
+  const int grp = blockIdx.x / C::kBlocks, cb = blockIdx.x % C::kBlocks;
   const int b = grp / n_hb, hb = grp % n_hb;
   const uint8_t* const base = parts + static_cast<int64_t>(grp) * n_splits * kPartBytes;
-  const int t = threadIdx.x, c = 32 * cb + (t >> 1), h0 = 8 * (t & 1);
+  const int t = threadIdx.x, col = t % (2 * CB), sg = t / (2 * CB);
+  const int c = CB * cb + (col >> 1), h0 = 8 * (col & 1);
   const uint8_t* const row = base + 2 * (c * kHeadBlock + h0);
   // every split's (max, sum) block (8 x 16 bytes) goes out first, all at once,
-  // then the first splits' rows; the weights are formed while the rows fly
-  // (addresses are clamped to the last split rather than branched around, so
-  // that every load is in flight before the first wait)
-  const int n_ml = (n_splits * 8 + 63) / 64;  // pieces per thread
-  constexpr int kMlPieces = kMaxSplits * 8 / 64;
+  // then this split group's first rows; the weights are formed while the rows
+  // fly (the (max, sum) addresses are clamped to the last split rather than
+  // branched around, so that every load is in flight before the wait)
+  const int n_ml = (n_splits * 8 + C::kThreads - 1) / C::kThreads;  // pieces per thread
+  constexpr int kMlPieces = C::kMaxS * 8 / C::kThreads;
   u32x4 ml[kMlPieces];
 #pragma unroll
   for (int k = 0; k < kMlPieces; ++k) {
-    const int i = min(t + 64 * k, n_splits * 8 - 1);  // piece i: split i / 8, floats 4 (i % 8) .. + 3
+    const int i = min(t + C::kThreads * k, n_splits * 8 - 1);  // piece i: split i / 8, floats 4 (i % 8) .. + 3
     if (k < n_ml) ml[k] = ldg<u32x4>(base + static_cast<int64_t>(i >> 3) * kPartBytes + kPartRowBytes + 16 * (i & 7));
   }
   constexpr int kEarly = 16;
   u32x4 v[kEarly];
 #pragma unroll
-  for (int s = 0; s < kEarly; ++s) v[s] = ldg<u32x4>(row + static_cast<int64_t>(min(s, n_splits - 1)) * kPartBytes);
+  for (int j = 0; j < kEarly; ++j) {
+    const int sp = sg + SG * j;
+    if (sp < n_splits) v[j] = ldg<u32x4>(row + static_cast<int64_t>(sp) * kPartBytes);
+  }
 #pragma unroll
   for (int k = 0; k < kMlPieces; ++k) {
-    if (k < n_ml) *reinterpret_cast<u32x4*>(s_ml + 4 * min(t + 64 * k, n_splits * 8 - 1)) = ml[k];
+    if (k < n_ml) *reinterpret_cast<u32x4*>(s_ml + 4 * min(t + C::kThreads * k, n_splits * 8 - 1)) = ml[k];
   }
   __syncthreads();
-  // weights, all 64 threads: head t % 16 over the splits s = t / 16 (mod 4)
   const int wh = t & 15, wq = t >> 4;
   float mp = kNegInf;
-  for (int s = wq; s < n_splits; s += 4) mp = fmaxf(mp, s_ml[s * 32 + wh]);
+  for (int sp = wq; sp < n_splits; sp += C::kQ) mp = fmaxf(mp, s_ml[sp * 32 + wh]);
   s_red[wq * kHeadBlock + wh] = mp;
   __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[wh], s_red[kHeadBlock + wh]),
-                        fmaxf(s_red[2 * kHeadBlock + wh], s_red[3 * kHeadBlock + wh]));
+  float M = kNegInf;
+#pragma unroll
+  for (int q = 0; q < C::kQ; ++q) M = fmaxf(M, s_red[q * kHeadBlock + wh]);
   float lp = 0.f;
-  for (int s = wq; s < n_splits; s += 4) {
-    const float m = s_ml[s * 32 + wh];
-    const float w = m == kNegInf ? 0.f : fast_exp2(m - M) * s_ml[s * 32 + kHeadBlock + wh];
-    s_w[s * kHeadBlock + wh] = w;
+  for (int sp = wq; sp < n_splits; sp += C::kQ) {
+    const float m = s_ml[sp * 32 + wh];
+    const float w = m == kNegInf ? 0.f : fast_exp2(m - M) * s_ml[sp * 32 + kHeadBlock + wh];
+    s_w[sp * kHeadBlock + wh] = w;
     lp += w;
   }
-  s_red[(4 + wq) * kHeadBlock + wh] = lp;
+  s_red[(C::kQ + wq) * kHeadBlock + wh] = lp;
   __syncthreads();
   if (t < kHeadBlock) {
-    const float L = (s_red[4 * kHeadBlock + t] + s_red[5 * kHeadBlock + t]) +
-                    (s_red[6 * kHeadBlock + t] + s_red[7 * kHeadBlock + t]);
-    s_red[8 * kHeadBlock + t] = L > 0.f ? 1.f / L : 0.f;
+    float L = 0.f;
+#pragma unroll
+    for (int q = 0; q < C::kQ; ++q) L += s_red[(C::kQ + q) * kHeadBlock + t];
+    s_red[2 * C::kQ * kHeadBlock + t] = L > 0.f ? 1.f / L : 0.f;
     const int hg = hb * kHeadBlock + t;
     if (cb == 0 && hg < heads)
       lse[static_cast<int64_t>(b) * heads + hg] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
   }
   __syncthreads();
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto add = [&](int s, const u32x4& x) {
-    const f32x4 w0 = *reinterpret_cast<const f32x4*>(s_w + s * kHeadBlock + h0);
-    const f32x4 w1 = *reinterpret_cast<const f32x4*>(s_w + s * kHeadBlock + h0 + 4);
+  auto add = [&](int sp, const u32x4& x) {
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(s_w + sp * kHeadBlock + h0);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(s_w + sp * kHeadBlock + h0 + 4);
     const half8 hv = __builtin_bit_cast(half8, x);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1378,16 +1406,53 @@ __global__ void __launch_bounds__(64) combine_kernel(const uint8_t* __restrict__
     }
   };
 #pragma unroll
-  for (int s = 0; s < kEarly; ++s)
-    if (s < n_splits) add(s, v[s]);
-#pragma unroll 8
-  for (int s = kEarly; s < n_splits; ++s) add(s, ldg<u32x4>(row + static_cast<int64_t>(s) * kPartBytes));
+  for (int j = 0; j < kEarly; ++j) {
+    const int sp = sg + SG * j;
+    if (sp < n_splits) add(sp, v[j]);
+  }
+#pragma unroll 16
+  for (int sp = sg + SG * kEarly; sp < n_splits; sp += SG) add(sp, ldg<u32x4>(row + static_cast<int64_t>(sp) * kPartBytes));
+  if constexpr (SG > 1) {
+    float* const mine = s_acc + t * 8;
+    *reinterpret_cast<f32x4*>(mine) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(mine + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    __syncthreads();
+    if (sg != 0) return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float sum = 0.f;
+#pragma unroll
+      for (int g = 0; g < SG; ++g) sum += s_acc[(g * 2 * CB + col) * 8 + e];
+      acc[e] = sum;
+    }
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int hg = hb * kHeadBlock + h0 + e;
     if (hg < heads)
-      out[(static_cast<int64_t>(b) * heads + hg) * kLatentDim + c] = acc[e] * s_red[8 * kHeadBlock + h0 + e];
+      out[(static_cast<int64_t>(b) * heads + hg) * kLatentDim + c] = acc[e] * s_red[2 * C::kQ * kHeadBlock + h0 + e];
   }
+}
+
+// Launches the merge in the shape that suits the split count: one wave per 32
+// channels when the splits are few, four split groups when they are many, and
+// 8-channel blocks (more workgroups) when they are many and the sequences few.
+template <int CB, int SG>
+int launch_combine(const DecodeParams& p, int64_t groups, int heads, int n_hb, int n_splits, hipStream_t stream) {
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&combine_kernel<CB, SG>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(combine_lds_bytes<CB, SG>(Cmb<CB, SG>::kMaxS))) != hipSuccess)
+      return MLA_LOWBIT_ERR_HIP;
+    attr = true;
+  }
+  using C = Cmb<CB, SG>;
+  const dim3 grid(static_cast<uint32_t>(groups * C::kBlocks)), block(C::kThreads);
+  const size_t lds = combine_lds_bytes<CB, SG>(n_splits);
+  hipLaunchKernelGGL((combine_kernel<CB, SG>), grid, block, lds, stream, p.parts, p.out, p.lse, heads, n_hb,
+                     n_splits);
+  return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
 }
 
 }  // namespace
@@ -1465,7 +1530,7 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   }
   const int64_t groups = static_cast<int64_t>(batch) * plan.n_hb;
   const int64_t blocks = groups * plan.n_splits;
-  if (blocks > 0x7FFFFFFF || groups * 32 > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
+  if (blocks > 0x7FFFFFFF || groups * 64 > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<4>),
@@ -1483,9 +1548,13 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
                        stream, p);
   if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
   if (plan.n_splits > 1) {
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(groups * 16)), dim3(64), 0, stream, p.parts, out,
-                       lse, heads, plan.n_hb, plan.n_splits);
-    if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
+    if (plan.n_splits <= 32)
+      rc = launch_combine<32, 1>(p, groups, heads, plan.n_hb, plan.n_splits, stream);
+    else if (groups >= 16)
+      rc = launch_combine<32, 4>(p, groups, heads, plan.n_hb, plan.n_splits, stream);
+    else
+      rc = launch_combine<8, 16>(p, groups, heads, plan.n_hb, plan.n_splits, stream);
+    if (rc) return rc;
   }
   return MLA_LOWBIT_OK;
 }

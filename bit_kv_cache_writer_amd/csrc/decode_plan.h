@@ -16,7 +16,7 @@ constexpr int kDecodeWaves = 4;    // waves per workgroup (one per SIMD)
 constexpr int kPartRowBytes = kHeadBlock * kLatentDim * 2;
 constexpr int kPartBytes = kPartRowBytes + 2 * kHeadBlock * 4;
 constexpr int kTargetGroups = 512;  // two workgroups per CU of an MI355X
-constexpr int kMaxSplits = 128;     // workgroups per (sequence, head block)
+constexpr int kMaxSplits = 512;     // workgroups per (sequence, head block)
 constexpr int kPageWin = 512;       // page ids a packed workgroup stages in LDS
 
 // Every (sequence, head block) gets n_dense BF16-path workgroups (sink,

@@ -67,6 +67,9 @@ CASES = [
     ("c4r4_p32_noprot_h7", 32, 4, 0.0, 0, 0, [64, 95, 200], 7),
     ("c2r4_p256_allprot", 256, 2, 0.94, 8, 512, [300, 40], 16),
     ("c4r4_p64_local8", 64, 4, 0.0, 2, 8, [150, 64, 63], 33),
+    # one long sequence: over 128 splits, so the merge loads the splits'
+    # (max, sum) blocks in several rounds
+    ("c4r4_p128_b1_long", 128, 4, 0.0, 4, 128, [40000], 16),
 ]
 
 
