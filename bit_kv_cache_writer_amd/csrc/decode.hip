@@ -1358,10 +1358,8 @@ __global__ void __launch_bounds__((Cmb<CB, SG>::kThreads)) combine_kernel(const 
   constexpr int kEarly = 16;
   u32x4 v[kEarly];
 #pragma unroll
-  for (int j = 0; j < kEarly; ++j) {
-    const int sp = sg + SG * j;
-    if (sp < n_splits) v[j] = ldg<u32x4>(row + static_cast<int64_t>(sp) * kPartBytes);
-  }
+  for (int j = 0; j < kEarly; ++j)  // clamped, not branched: all 16 go out back to back
+    v[j] = ldg<u32x4>(row + static_cast<int64_t>(min(sg + SG * j, n_splits - 1)) * kPartBytes);
 #pragma unroll
   for (int k = 0; k < kMlPieces; ++k) {
     if (k < n_ml) *reinterpret_cast<u32x4*>(s_ml + 4 * min(t + C::kThreads * k, n_splits * 8 - 1)) = ml[k];
