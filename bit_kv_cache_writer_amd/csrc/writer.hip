@@ -51,7 +51,9 @@ struct WriterParams {
 
 __device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-__device__ inline float canon_zero(float x) { return x == 0.0f ? 0.0f : x; }
+// -0 -> +0, every other value unchanged: -0 + +0 is +0 under round to
+// nearest, x + 0 = x otherwise (one add; contraction is off in this file).
+__device__ inline float canon_zero(float x) { return x + 0.0f; }
 
 __device__ inline uint16_t f16_bits_rn(float x) {
   _Float16 h = static_cast<_Float16>(x);  // v_cvt_f16_f32, round to nearest even
@@ -81,6 +83,18 @@ __device__ inline uint16_t f16_round_up(float x) {
     if (h == 0x8000u) h = 0;
   }
   return h;
+}
+
+// rint of the correctly rounded quotient d / s (d >= 0, s > 0, the quotient
+// below 32 in every use).  d times the hardware reciprocal is within 2 ulp of
+// the correctly rounded quotient; more than 1e-5 (over 4 ulp below 32) from a
+// half-integer, both round to the same integer; otherwise (rare) the IEEE
+// division decides.  Bit-identical to rintf(d / s).
+__device__ inline float rint_div(float d, float s, float rcp_s) {
+  const float qa = d * rcp_s;
+  float r = rintf(qa);
+  if (__builtin_expect(fabsf(qa - floorf(qa) - 0.5f) <= 1e-5f, 0)) r = rintf(d / s);
+  return r;
 }
 
 // Min / max over each 16-lane row by DPP lane moves (VALU, no LDS round
@@ -191,13 +205,13 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
   const float s = span / static_cast<float>(levels);
   const uint16_t sh = f16_round_up(s);
   const float sf = f16_to_f32(sh);
+  const float rs = __builtin_amdgcn_rcpf(sf);
   uint32_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t code = 0;
     if (sf > 0.0f) {
-      const float t = (x[i] - minf) / sf;
-      float r = rintf(t);
+      float r = rint_div(x[i] - minf, sf, rs);
       r = fminf(fmaxf(r, 0.0f), static_cast<float>(levels));
       code = static_cast<uint32_t>(r);
     }
@@ -351,11 +365,12 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
     }
     __syncthreads();
     // codes, packed as they are made: dword i = row i / 8, channels 8 (i % 8) .. + 7
-    float minf[8], sf[8];
+    float minf[8], sf[8], rsf[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       minf[e] = s_minf[8 * q + e];
       sf[e] = s_sf[8 * q + e];
+      rsf[e] = __builtin_amdgcn_rcpf(sf[e]);
     }
     uint32_t* rc = reinterpret_cast<uint32_t*>(page + p.rope_codes_off);
     for (int s = part; s < P; s += kThreads / 8) {
@@ -366,8 +381,8 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       for (int e = 0; e < 8; ++e) {
         uint32_t code = 0;
         if (sf[e] > 0.0f) {
-          const float t = (canon_zero(bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu)) - minf[e]) / sf[e];
-          float r = rintf(t);
+          float r = rint_div(canon_zero(bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu)) - minf[e],
+                             sf[e], rsf[e]);
           r = fminf(fmaxf(r, 0.0f), 15.0f);
           code = static_cast<uint32_t>(r);
         }
