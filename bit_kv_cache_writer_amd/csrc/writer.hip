@@ -4,7 +4,7 @@
 // 0.94-quantile |x| clipping for the 2-bit latent, per-(channel, page) 4-bit
 // k_R with FP16 scale/min).
 //
-// One workgroup (4 waves) per (sequence, cache page touched by the call):
+// One workgroup (8 waves) per (sequence, cache page touched by the call):
 //   * each wave quantizes whole latent tokens: lane l owns channels 8l..8l+7,
 //     so a 128-channel group is 16 lanes and its min/max is a 16-lane
 //     butterfly; codes are packed in registers and stored as one dword
@@ -29,7 +29,7 @@
 namespace mla {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
 struct WriterParams {
@@ -276,8 +276,9 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   __shared__ uint4 s_rows[256 * kRopeDim / 8];  // P x 64 bf16
   const bool completes = (pg + 1) * P <= end;
   if (completes) {
-    for (int k = 0; k < P * (kRopeDim / 8) / kThreads; ++k) {  // P * 8 is a multiple of 256 (P >= 32)
+    for (int k = 0; k * kThreads < P * (kRopeDim / 8); ++k) {
       const int i = static_cast<int>(threadIdx.x) + k * kThreads;
+      if (k * kThreads + 64 * wave >= P * (kRopeDim / 8)) break;  // whole waves (P * 8 is a multiple of 256)
       const int slot = i >> 3, q = i & 7;
       const int t = pg * P + slot;
       const uint4* src = t < sb ? reinterpret_cast<const uint4*>(tail + static_cast<int64_t>(slot) * kRopeDim) + q
