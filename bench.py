@@ -246,6 +246,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true", help="time a plain 1 GiB copy and exit")
     ap.add_argument("--sweep", action="store_true", help="context sweep 1K..1M at batch 1 and 8 (JSON lines)")
+    ap.add_argument("--bf16-baseline", action="store_true",
+                    help="the same workload with every token protected (sink 0, window = N <= 4096): the decode "
+                         "reads a BF16 cache through the same split-KV skeleton")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -266,6 +269,13 @@ def main() -> int:
         return sweep(max(1, min(args.steps, 5)))
     mla.lib()
     w = wl.WORKLOADS[args.workload]
+    if args.bf16_baseline:
+        import dataclasses
+        if w.seqlen > 4096:
+            print("--bf16-baseline needs N <= 4096 (the longest recent window a layout allows)", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, name=w.name + "_bf16", sink=0, local=w.seqlen,
+                                description=w.description + "; every token from BF16 (sink 0, window N)")
     lay = mla.Layout(w.page_size, w.latent_bits, w.clip_q, w.sink, w.local)
     n = w.seqlen
     max_pages = w.pages_per_seq()
