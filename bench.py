@@ -236,6 +236,105 @@ def sweep(steps: int) -> int:
     return 0
 
 
+def ragged(steps: int) -> int:
+    """Ragged decode and chunked prefill (timing only; parity of both is
+    covered by the tests): (1) C4R4 decode, 16 heads, page 128, sink 4 + local
+    128, 32 sequences with seeded lengths uniform in [1024, 8192]; (2) the
+    writer appending four 128K-token prompts in 8K-token chunks.  Inputs drawn
+    on the GPU from a seeded generator.  One JSON line each."""
+    import torch
+
+    from bit_kv_cache_writer_amd import mla
+
+    mla.lib()
+    lay = mla.Layout(128, 4, 0.0, 4, 128)
+    page_bytes = mla.mla_lowbit_layout_query(lay)["page_bytes"]
+    heads, scale = 16, 1.0 / math.sqrt(192.0)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    outl = torch.ones(64, device="cuda")
+    outl[[7, 23, 39, 55]] = 20.0
+
+    def bf16_rows(n, width, mult=None):
+        x = torch.randn((n, width), generator=gen, device="cuda", dtype=torch.float32)
+        if mult is not None:
+            x *= mult
+        return x.to(torch.bfloat16).view(torch.int16)
+
+    class W:  # the shape algorithmic_decode_bytes reads
+        latent_bits, page_size, sink, local, heads = 4, 128, 4, 128, 16
+
+    # (1) ragged decode
+    B = 32
+    rng = np.random.default_rng(np.random.SeedSequence([11, B]))
+    lengths = [int(x) for x in rng.integers(1024, 8193, size=B)]
+    max_pages = (max(lengths) + 127) // 128
+    n_pool = int(math.ceil(B * max_pages * 1.25))
+    bt = rng.permutation(n_pool)[: B * max_pages].astype(np.int32).reshape(B, max_pages)
+    layers = max(2, math.ceil(1.0e9 / (sum((L + 127) // 128 for L in lengths) * page_bytes)))
+    caches = []
+    for _ in range(layers):
+        c = mla.DeviceCache(lay, B, max_pages, bt, n_pool)
+        n_tok = sum(lengths)
+        c.append(bf16_rows(n_tok, 512), bf16_rows(n_tok, 64, outl), lengths)
+        caches.append(c)
+    q_lat = bf16_rows(B * heads, 512).view(B, heads, 512).contiguous()
+    q_rope = bf16_rows(B * heads, 64).view(B, heads, 64).contiguous()
+    stream = torch.cuda.current_stream()
+    for c in caches:
+        c.decode(q_lat, q_rope, scale, stream=stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps * layers)]
+    for st in range(steps):
+        for li, c in enumerate(caches):
+            e = evs[st * layers + li]
+            e[0].record(stream)
+            c.decode(q_lat, q_rope, scale, stream=stream)
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1000.0)
+    byts = sum(algorithmic_decode_bytes(W, L)["total"] for L in lengths)
+    gbs = byts / (us * 1e-6) / 1e9
+    print(json.dumps({"ragged": "C4R4 decode, 16 heads, page 128, sink 4 + local 128, 32 sequences, "
+                                "lengths uniform in [1024, 8192]",
+                      "mean_tokens": round(float(np.mean(lengths)), 1), "max_tokens": max(lengths),
+                      "layers": layers, "decode_us": round(us, 3), "algorithmic_bytes": byts,
+                      "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+    del caches
+    torch.cuda.empty_cache()
+
+    # (2) chunked prefill: 4 prompts of 131072 tokens in chunks of 8192
+    B, N, chunk = 4, 131072, 8192
+    max_pages = N // 128
+    n_pool = B * max_pages
+    bt = np.arange(n_pool, dtype=np.int32).reshape(B, max_pages)
+    c = mla.DeviceCache(lay, B, max_pages, bt, n_pool)
+    ckv = bf16_rows(B * chunk, 512)
+    kr = bf16_rows(B * chunk, 64, outl)
+    # the entry point itself, every argument already on the device (the
+    # DeviceCache helper would also time its small host-to-device copies)
+    cu_new = torch.arange(0, (B + 1) * chunk, chunk, dtype=torch.int32, device="cuda")
+    before = [torch.full((B,), k * chunk, dtype=torch.int32, device="cuda") for k in range(N // chunk)]
+    torch.cuda.synchronize()
+    evs = []
+    for k in range(N // chunk):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        mla.mla_lowbit_write(lay, ckv, kr, cu_new, before[k], B, B * chunk, chunk, c.block_table, max_pages, n_pool,
+                             c.pool, c.sink, c.ring, c.tail, stream)
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs[1:]]
+    per_tok = 1152 + 304  # read bf16 row, write codes + metadata (C4R4)
+    gbs = B * chunk * per_tok / (float(np.median(ms)) * 1e-3) / 1e9
+    print(json.dumps({"chunked_prefill": "writer, C4R4 page 128, 4 prompts of 131072 tokens in chunks of 8192",
+                      "chunk_us_median": round(float(np.median(ms)) * 1000.0, 2),
+                      "tokens_per_s": round(B * chunk / (float(np.median(ms)) * 1e-3), 1),
+                      "algorithmic_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +345,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true", help="time a plain 1 GiB copy and exit")
     ap.add_argument("--sweep", action="store_true", help="context sweep 1K..1M at batch 1 and 8 (JSON lines)")
+    ap.add_argument("--ragged", action="store_true", help="ragged-batch decode and chunked-prefill writer (JSON lines)")
     ap.add_argument("--bf16-baseline", action="store_true",
                     help="the same workload with every token protected (sink 0, window = N <= 4096): the decode "
                          "reads a BF16 cache through the same split-KV skeleton")
@@ -267,6 +367,8 @@ def main() -> int:
         return calibrate_copy()
     if args.sweep:
         return sweep(max(1, min(args.steps, 5)))
+    if args.ragged:
+        return ragged(max(1, min(args.steps, 5)))
     mla.lib()
     w = wl.WORKLOADS[args.workload]
     if args.bf16_baseline:
