@@ -1433,8 +1433,9 @@ __global__ void __launch_bounds__((Cmb<CB, SG>::kThreads)) combine_kernel(const 
 }
 
 // Launches the merge in the shape that suits the split count: one wave per 32
-// channels when the splits are few, four split groups when they are many, and
-// 8-channel blocks (more workgroups) when they are many and the sequences few.
+// channels when the splits are few (up to 32), else 8-channel blocks of 16
+// split groups (four times the workgroups, 16 times the loads in flight per
+// column), which a handful of sequences with hundreds of splits needs.
 template <int CB, int SG>
 int launch_combine(const DecodeParams& p, int64_t groups, int heads, int n_hb, int n_splits, hipStream_t stream) {
   static bool attr = false;
@@ -1548,8 +1549,6 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   if (plan.n_splits > 1) {
     if (plan.n_splits <= 32)
       rc = launch_combine<32, 1>(p, groups, heads, plan.n_hb, plan.n_splits, stream);
-    else if (groups >= 16)
-      rc = launch_combine<32, 4>(p, groups, heads, plan.n_hb, plan.n_splits, stream);
     else
       rc = launch_combine<8, 16>(p, groups, heads, plan.n_hb, plan.n_splits, stream);
     if (rc) return rc;
