@@ -65,6 +65,31 @@ def test_workspace_query_and_errors():
         assert e.value.code == -2
 
 
+# The work split the decode chooses, seen through the workspace it needs
+# (groups x splits x one partial).  Two workgroups per CU (512), at most 512
+# splits, the BF16-path count minimizing the longer of the two kinds of
+# workgroup: the headline batch keeps 16 splits (3 BF16-path + 13 packed, five
+# rounds of packed tiles), one long sequence fills the chip with 512, 128 heads
+# need 3 per (sequence, head block) (1 BF16-path + 2 packed, a 512-page window
+# each).
+SPLITS = [
+    # (P, bits, batch, heads, max_seqlen, splits per (sequence, head block))
+    (128, 4, 32, 16, 4096, 16),
+    (128, 4, 8, 16, 4096, 35),
+    (128, 4, 1, 16, 1 << 20, 512),
+    (64, 4, 64, 128, 32768, 3),
+    (64, 2, 4, 64, 131072, 32),
+]
+
+
+@pytest.mark.parametrize("P,bits,batch,heads,L,splits", SPLITS)
+def test_decode_split_plan(P, bits, batch, heads, L, splits):
+    lay = mla.Layout(P, bits, 0.94 if bits == 2 else 0.0, 4, 128)
+    part = 16 * 512 * 2 + 32 * 4
+    groups = batch * ((heads + 15) // 16)
+    assert mla.mla_lowbit_decode_workspace(lay, batch, heads, L) == groups * splits * part
+
+
 def _write(lay, **kw):
     a = dict(c_kv=16, k_r=16, cu_new=16, seqlens_before=16, batch=1, total_new=1, max_new_per_seq=1,
              block_table=16, max_pages=1, num_pool_pages=1, page_pool=16, sink_buf=16, ring_buf=16,
