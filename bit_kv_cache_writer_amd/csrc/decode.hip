@@ -1269,15 +1269,18 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   WgCtx cx;
   // Workgroups are dealt to the 8 XCDs of the chip in turn (block i on XCD
   // i mod 8); order the work so that each XCD's blocks take consecutive
-  // (sequence, head block, split) items, which keeps the splits of a sequence
-  // on one XCD, sharing its L2 for the query rows and block-table window.
+  // items, which keeps the splits of a sequence on one XCD, sharing its L2 for
+  // the query rows, block-table window and (with several head blocks) pages.
   // (Any dispatch order gives the same results; this only places the work.)
   const int n_blocks = gridDim.x, xcd = blockIdx.x & 7, per_xcd = n_blocks >> 3, extra = n_blocks & 7;
   const int item = xcd * per_xcd + min(xcd, extra) + (blockIdx.x >> 3);
-  cx.split = item % p.n_splits;
-  cx.grp = item / p.n_splits;  // b * n_hb + hb
-  cx.hb = cx.grp % p.n_hb;
-  cx.b = cx.grp / p.n_hb;
+  // items are ordered (sequence, split, head block): the head blocks of one
+  // (sequence, split) read the same pages, and as consecutive items they run
+  // on one XCD at the same time, so the XCD's L2 serves the repeats
+  cx.hb = item % p.n_hb;
+  cx.split = (item / p.n_hb) % p.n_splits;
+  cx.b = item / (p.n_hb * p.n_splits);
+  cx.grp = cx.b * p.n_hb + cx.hb;
   cx.lane = threadIdx.x & 63;
   cx.wave = uniform(threadIdx.x >> 6);
   cx.n16 = cx.lane & 15;
