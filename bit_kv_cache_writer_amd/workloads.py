@@ -142,3 +142,13 @@ def block_table(w: Workload, max_pages: int, stream: int = 2_000_003):
 def cu_from_counts(counts) -> np.ndarray:
     counts = np.asarray(counts, dtype=np.int64)
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def random_orthogonal_bf16(seed: int, dim: int = 512) -> np.ndarray:
+    """A seeded random orthogonal matrix (QR of a Gaussian one, signs fixed by
+    R's diagonal), rounded to bf16 bits: a stand-in for a fitted latent
+    transform, which needs training data."""
+    g = _rng(seed, 3_000_017).standard_normal((dim, dim))
+    q, r = np.linalg.qr(g)
+    q = q * np.sign(np.diag(r))[None, :]
+    return f32_to_bf16_bits(q.astype(np.float32))

@@ -101,6 +101,8 @@ def lib():
         L.oracle_read_token.restype = i32
         L.oracle_read_token.argtypes = [P, P, P, P, P, P, i32, i32, i32, P]
         L.oracle_decode.argtypes = [P, P, P, i32, i32, f64, P, P, i32, P, P, P, P, P, P]
+        L.oracle_transform.argtypes = [P, P, i64, i32, P]
+        L.oracle_transform.restype = None
         _lib = L
     return _lib
 
@@ -184,6 +186,17 @@ def write(layout: Layout, c_kv, k_r, cu_new, seqlens_before, block_table, pool, 
                             _p(pool), _p(sink_buf), _p(ring_buf), _p(tail_buf))
     if rc != 0:
         raise ValueError("oracle_write: position beyond the block table")
+
+
+def transform(a_c, x) -> np.ndarray:
+    """bf16(A_c x) per token row of x (see oracle_transform); uint16 views."""
+    a_c = np.ascontiguousarray(a_c, dtype=np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    dim = a_c.shape[0]
+    assert a_c.shape == (dim, dim) and x.shape[-1] == dim
+    y = np.zeros_like(x)
+    lib().oracle_transform(_p(a_c), _p(x), x.size // dim, dim, _p(y))
+    return y
 
 
 def read_token(layout: Layout, pool, block_table, sink_buf, ring_buf, tail_buf, b: int,

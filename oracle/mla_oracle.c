@@ -518,3 +518,35 @@ void oracle_f16_round_down_n(const float* x, int64_t n, uint16_t* out) {
 void oracle_f16_round_up_n(const float* x, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_round_up(x[i]);
 }
+
+/* ------------------------------------------------------------------ */
+/* Latent transform before the cache write (RAQ-MLA, Figure 4 caption: A_c
+ * acts on the latent before it is quantized; appendix Table 9: applied inside
+ * the write kernel).  Reading taken: y = A_c x with A_c stored row-major
+ * [out][in] in bf16; each output is an fp32 fused multiply-add chain over the
+ * inputs in ascending order, rounded once to bf16 (nearest, ties to even),
+ * and the writer then caches y exactly as it caches an untransformed row.
+ * The pages do not fix the transform's precision, so the decision is taken
+ * in the GPU writer's: single-precision fma in input order. */
+
+static uint16_t f32_to_bf16_rne(float f) {
+  /* keep the top 16 bits of the fp32 pattern, rounding the 16 dropped bits
+   * to nearest with ties to the even kept pattern (finite inputs) */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  const uint32_t dropped = u & 0xFFFFu, kept = u >> 16;
+  if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) return (uint16_t)(kept + 1u);
+  return (uint16_t)kept;
+}
+
+/* y[t][c] = bf16(fma chain over k of A[c][k] * x[t][k]) for t < n_tokens. */
+void oracle_transform(const uint16_t* a_c, const uint16_t* x, int64_t n_tokens, int32_t dim, uint16_t* y) {
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    for (int32_t c = 0; c < dim; ++c) {
+      float acc = 0.0f;
+      for (int32_t k = 0; k < dim; ++k)
+        acc = fmaf(bf16_to_f32(a_c[(int64_t)c * dim + k]), bf16_to_f32(x[t * dim + k]), acc);
+      y[t * dim + c] = f32_to_bf16_rne(acc);
+    }
+  }
+}

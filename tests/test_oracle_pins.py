@@ -396,3 +396,99 @@ def test_chunked_appends_equal_one_bulk_append(orc):
     np.testing.assert_array_equal(inc.ring, bulk.ring)
     np.testing.assert_array_equal(inc.sink, bulk.sink)
     np.testing.assert_array_equal(inc.tail[:, : L % P], bulk.tail[:, : L % P])
+
+
+# ----------------------------------------------------------------------------
+# Latent transform y = bf16(fp32 fma chain of A_c x), ascending input order
+
+def _bf16(v):
+    return wl.f32_to_bf16_bits(np.asarray(v, dtype=np.float32))
+
+
+def _eye_bf16(dim, scale=1.0):
+    a = np.zeros((dim, dim), dtype=np.float32)
+    np.fill_diagonal(a, scale)
+    return _bf16(a)
+
+
+def _x_rows(seed, n, dim=512):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, dim)).astype(np.float32) * rng.choice([1e-3, 1.0, 30.0], (n, dim))
+    x[:, ::97] = 0.0
+    x[0, 5] = -0.0
+    return _bf16(x)
+
+
+def test_transform_identity_and_permutation(orc):
+    """A_c = I returns x (a -0 input becomes +0: 0 + -0 = +0 to nearest);
+    a permutation matrix permutes; 2 I doubles exactly."""
+    import oracle as orc_mod
+    x = _x_rows(1, 6)
+    canon = np.where(x == 0x8000, np.uint16(0), x)
+    assert np.array_equal(orc_mod.transform(_eye_bf16(512), x), canon)
+    perm = np.random.default_rng(2).permutation(512)
+    a = np.zeros((512, 512), dtype=np.float32)
+    a[np.arange(512), perm] = 1.0
+    assert np.array_equal(orc_mod.transform(_bf16(a), x), canon[:, perm])
+    xf = wl.bf16_bits_to_f32(canon)
+    assert np.array_equal(orc_mod.transform(_eye_bf16(512, 2.0), x), _bf16(2.0 * xf))
+
+
+def test_transform_bf16_round_to_nearest_even(orc):
+    """Three-term sums that land on, above and below bf16 midpoints (bf16 keeps
+    7 fraction bits: its step at 1 is 2^-7)."""
+    import oracle as orc_mod
+    dim = 512
+    a = np.zeros((dim, dim), dtype=np.float32)
+    a[:, :3] = 1.0
+    cases = [  # (x0, x1, x2, expected sum after rounding)
+        (1.0, 2.0**-8, 0.0, 1.0),                              # tie, even below
+        (1.0 + 2.0**-7, 2.0**-8, 0.0, 1.0 + 2.0**-6),         # tie, even above
+        (1.0, 2.0**-8, 2.0**-16, 1.0 + 2.0**-7),              # just above the tie
+        (1.0, 2.0**-8, -(2.0**-17), 1.0),                     # just below the tie
+        (-1.0, -(2.0**-8), 0.0, -1.0),                        # negative tie
+        (3.0, 2.0**-7, 0.0, 3.0),                             # tie: the step in [2, 4) is 2^-6
+    ]
+    x = np.zeros((len(cases), dim), dtype=np.float32)
+    for i, c in enumerate(cases):
+        x[i, :3] = c[:3]
+    xb = _bf16(x)
+    assert np.array_equal(wl.bf16_bits_to_f32(xb)[:, :3], x[:, :3])  # inputs exact in bf16
+    y = wl.bf16_bits_to_f32(orc_mod.transform(_bf16(a), xb))
+    assert np.array_equal(y[:, 0], np.array([c[3] for c in cases], dtype=np.float32))
+
+
+def test_transform_single_precision_input_order(orc):
+    """The sum runs in fp32 in ascending input order: after 2^24 every +1
+    lands on a tie and rounds back to 2^24 (even), so 2^24, 510 ones and
+    -2^24 sum to 0; in any exact or reordered sum they give 510."""
+    import oracle as orc_mod
+    dim = 512
+    a = _bf16(np.ones((dim, dim), dtype=np.float32))
+    x = np.ones((1, dim), dtype=np.float32)
+    x[0, 0], x[0, -1] = 2.0**24, -(2.0**24)
+    y = wl.bf16_bits_to_f32(orc_mod.transform(a, _bf16(x)))
+    assert np.all(y == 0.0)
+    x2 = x.copy()
+    x2[0, 0], x2[0, 1] = -(2.0**24), 2.0**24   # cancellation first: the ones add up
+    x2[0, -1] = 1.0
+    y2 = wl.bf16_bits_to_f32(orc_mod.transform(a, _bf16(x2)))
+    assert np.all(y2 == 510.0)
+
+
+def test_transform_within_fp32_bound_of_exact(orc):
+    """Against the exact product (float64: every bf16 x bf16 product is exact
+    and the 512-term sum's error is far below the bound): |y - Ax| is at most
+    half a bf16 step of y plus the fp32 chain's bound 512 u sum |a x|."""
+    import oracle as orc_mod
+    a = wl.random_orthogonal_bf16(11)
+    x = _x_rows(3, 8)
+    af = wl.bf16_bits_to_f32(a).astype(np.float64)
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    exact = xf @ af.T
+    absum = np.abs(xf) @ np.abs(af).T
+    y = wl.bf16_bits_to_f32(orc_mod.transform(a, x)).astype(np.float64)
+    step = np.abs(y) * 2.0**-7 + 2.0**-133
+    assert np.all(np.abs(y - exact) <= 0.5 * step + 512 * 2.0**-24 * absum)
+    # the transform is (nearly) orthogonal: row norms are kept to bf16 accuracy
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(xf, axis=1), rtol=2e-2)
