@@ -33,6 +33,7 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
 struct WriterParams {
+  const uint16_t* a_c;  // latent transform, bf16 [512][512] row-major (transforming writer only)
   const uint16_t* c_kv;
   const uint16_t* k_r;
   const int32_t* cu_new;
@@ -50,6 +51,11 @@ struct WriterParams {
 };
 
 __device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+// fp32 -> bf16 bits, nearest with ties to even (finite values)
+__device__ inline uint32_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 // -0 -> +0, every other value unchanged: -0 + +0 is +0 under round to
 // nearest, x + 0 = x otherwise (one add; contraction is off in this file).
@@ -248,6 +254,7 @@ __device__ inline TokenRows load_token(const WriterParams& p, int64_t row, int l
   return r;
 }
 
+template <bool kTransform>
 __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   const int b = blockIdx.x / p.pages_per_seq_grid;
   const int pi = blockIdx.x % p.pages_per_seq_grid;
@@ -289,7 +296,8 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   }
   // this wave's first token goes out with them (its row index is clamped
   // into the input: a wave without a token reads a row it does not use)
-  TokenRows cur = load_token(p, r0 + (min(tb + wave, te - 1) - sb), lane);
+  TokenRows cur{};
+  if constexpr (!kTransform) cur = load_token(p, r0 + (min(tb + wave, te - 1) - sb), lane);
   const int page_id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pg];
   if (page_id < 0 || page_id >= p.num_pool_pages) {
     __syncthreads();  // no direct load outlives the workgroup
@@ -297,14 +305,84 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   }
   uint8_t* page = p.pool + static_cast<int64_t>(page_id) * p.page_bytes;
 
-  // Latent codes + metadata, BF16 sink / ring copies.
-  for (int t = tb + wave; t < te; t += kWaves) {
-    const TokenRows x = cur;
-    if (t + kWaves < te) cur = load_token(p, r0 + (t + kWaves - sb), lane);
-    write_latent_token(p, x.ckv, page, t - pg * P, lane);
-    if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, x.ckv, x.kr, lane);
-    if (p.local > 0 && t >= end - p.local)
-      copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, x.ckv, x.kr, lane);
+  if constexpr (kTransform) {
+    // The latent transform (RAQ-MLA Figure 4 caption; appendix Table 9, the
+    // fused variant): y = A_c x per token, for up to kWaves tokens at a time.
+    // Thread c forms output channel c of each token as an fp32 fma chain over
+    // the 512 inputs in ascending order (the inputs broadcast from LDS, A_c's
+    // row c read 16 bytes at a time), rounded once to bf16; wave w then
+    // caches token t0 + w from that bf16 row exactly as it caches an
+    // untransformed one (codes, metadata, sink and ring copies).
+    __shared__ __attribute__((aligned(16))) float s_x[kWaves][kLatentDim];
+    __shared__ uint4 s_y[kWaves][kLatentDim / 8];
+    const int c = static_cast<int>(threadIdx.x);
+    const uint4* const arow = reinterpret_cast<const uint4*>(p.a_c + static_cast<int64_t>(c) * kLatentDim);
+    for (int t0 = tb; t0 < te; t0 += kWaves) {
+      const int n = min(kWaves, te - t0);
+      if (wave < n) {
+        const uint4 raw =
+            reinterpret_cast<const uint4*>(p.c_kv + (r0 + (t0 + wave - sb)) * static_cast<int64_t>(kLatentDim))[lane];
+        const float4 lo = {bf16_to_f32(raw.x & 0xFFFFu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xFFFFu),
+                           bf16_to_f32(raw.y >> 16)};
+        const float4 hi = {bf16_to_f32(raw.z & 0xFFFFu), bf16_to_f32(raw.z >> 16), bf16_to_f32(raw.w & 0xFFFFu),
+                           bf16_to_f32(raw.w >> 16)};
+        *reinterpret_cast<float4*>(&s_x[wave][8 * lane]) = lo;
+        *reinterpret_cast<float4*>(&s_x[wave][8 * lane + 4]) = hi;
+      }
+      __syncthreads();
+      float acc[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) acc[w] = 0.0f;
+#pragma unroll 4
+      for (int kb = 0; kb < kLatentDim / 8; ++kb) {
+        const uint4 a8 = arow[kb];
+        const float a[8] = {bf16_to_f32(a8.x & 0xFFFFu), bf16_to_f32(a8.x >> 16), bf16_to_f32(a8.y & 0xFFFFu),
+                            bf16_to_f32(a8.y >> 16),     bf16_to_f32(a8.z & 0xFFFFu), bf16_to_f32(a8.z >> 16),
+                            bf16_to_f32(a8.w & 0xFFFFu), bf16_to_f32(a8.w >> 16)};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          if (w < n) {
+            const float4 x0 = *reinterpret_cast<const float4*>(&s_x[w][8 * kb]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&s_x[w][8 * kb + 4]);
+            float s = acc[w];
+            s = fmaf(a[0], x0.x, s);
+            s = fmaf(a[1], x0.y, s);
+            s = fmaf(a[2], x0.z, s);
+            s = fmaf(a[3], x0.w, s);
+            s = fmaf(a[4], x1.x, s);
+            s = fmaf(a[5], x1.y, s);
+            s = fmaf(a[6], x1.z, s);
+            s = fmaf(a[7], x1.w, s);
+            acc[w] = s;
+          }
+        }
+      }
+      uint16_t* const ys = reinterpret_cast<uint16_t*>(&s_y[0][0]);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (w < n) ys[w * kLatentDim + c] = static_cast<uint16_t>(f32_to_bf16_rne(acc[w]));
+      __syncthreads();
+      if (wave < n) {
+        const int t = t0 + wave;
+        const uint4 y = s_y[wave][lane];
+        const uint4 kr = reinterpret_cast<const uint4*>(p.k_r + (r0 + (t - sb)) * static_cast<int64_t>(kRopeDim))[lane & 7];
+        write_latent_token(p, y, page, t - pg * P, lane);
+        if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, y, kr, lane);
+        if (p.local > 0 && t >= end - p.local)
+          copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, y, kr, lane);
+      }
+      __syncthreads();  // s_x and s_y are refilled for the next tokens
+    }
+  } else {
+    // Latent codes + metadata, BF16 sink / ring copies.
+    for (int t = tb + wave; t < te; t += kWaves) {
+      const TokenRows x = cur;
+      if (t + kWaves < te) cur = load_token(p, r0 + (t + kWaves - sb), lane);
+      write_latent_token(p, x.ckv, page, t - pg * P, lane);
+      if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, x.ckv, x.kr, lane);
+      if (p.local > 0 && t >= end - p.local)
+        copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, x.ckv, x.kr, lane);
+    }
   }
 
   // k_R of a page that becomes full: per channel over its P tokens.  Thread
@@ -409,13 +487,15 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
 }  // namespace
 }  // namespace mla
 
-extern "C" int mla_lowbit_write(const mla_lowbit_layout* layout, const void* c_kv, const void* k_r,
+namespace mla {
+namespace {
+
+int write_impl(const mla_lowbit_layout* layout, const void* a_c, const void* c_kv, const void* k_r,
                                 const int32_t* cu_new, const int32_t* seqlens_before, int32_t batch,
                                 int32_t total_new, int32_t max_new_per_seq,
                                 const int32_t* block_table, int32_t max_pages,
                                 int32_t num_pool_pages, void* page_pool, void* sink_buf,
                                 void* ring_buf, void* rope_tail, hipStream_t stream) {
-  using namespace mla;
   Geometry g;
   int rc = make_geometry(layout, &g);
   if (rc) return rc;
@@ -430,7 +510,9 @@ extern "C" int mla_lowbit_write(const mla_lowbit_layout* layout, const void* c_k
       (sink_buf && !aligned16(sink_buf)) || (ring_buf && !aligned16(ring_buf)))
     return MLA_LOWBIT_ERR_ARG;
   if (max_pages == 0 || num_pool_pages == 0) return MLA_LOWBIT_ERR_ARG;
+  if (a_c && !aligned16(a_c)) return MLA_LOWBIT_ERR_ARG;
   WriterParams p{};
+  p.a_c = static_cast<const uint16_t*>(a_c);
   p.c_kv = static_cast<const uint16_t*>(c_kv);
   p.k_r = static_cast<const uint16_t*>(k_r);
   p.cu_new = cu_new;
@@ -461,6 +543,34 @@ extern "C" int mla_lowbit_write(const mla_lowbit_layout* layout, const void* c_k
   p.pages_per_seq_grid = (max_new_per_seq - 1) / g.page_size + 2;
   const int64_t blocks = static_cast<int64_t>(batch) * p.pages_per_seq_grid;
   if (blocks > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(writer_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  if (a_c)
+    hipLaunchKernelGGL(writer_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(writer_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace mla
+
+extern "C" int mla_lowbit_write(const mla_lowbit_layout* layout, const void* c_kv, const void* k_r,
+                                const int32_t* cu_new, const int32_t* seqlens_before, int32_t batch,
+                                int32_t total_new, int32_t max_new_per_seq,
+                                const int32_t* block_table, int32_t max_pages,
+                                int32_t num_pool_pages, void* page_pool, void* sink_buf,
+                                void* ring_buf, void* rope_tail, hipStream_t stream) {
+  return mla::write_impl(layout, nullptr, c_kv, k_r, cu_new, seqlens_before, batch, total_new, max_new_per_seq,
+                         block_table, max_pages, num_pool_pages, page_pool, sink_buf, ring_buf, rope_tail, stream);
+}
+
+extern "C" int mla_lowbit_write_transformed(const mla_lowbit_layout* layout, const void* a_c, const void* c_kv,
+                                            const void* k_r, const int32_t* cu_new,
+                                            const int32_t* seqlens_before, int32_t batch, int32_t total_new,
+                                            int32_t max_new_per_seq, const int32_t* block_table,
+                                            int32_t max_pages, int32_t num_pool_pages, void* page_pool,
+                                            void* sink_buf, void* ring_buf, void* rope_tail,
+                                            hipStream_t stream) {
+  if (!a_c) return MLA_LOWBIT_ERR_ARG;
+  return mla::write_impl(layout, a_c, c_kv, k_r, cu_new, seqlens_before, batch, total_new, max_new_per_seq,
+                         block_table, max_pages, num_pool_pages, page_pool, sink_buf, ring_buf, rope_tail, stream);
 }

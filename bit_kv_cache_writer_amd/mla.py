@@ -19,7 +19,8 @@ ERRORS = {
     0: "ok", -1: "MLA_LOWBIT_ERR_LAYOUT", -2: "MLA_LOWBIT_ERR_ARG", -3: "MLA_LOWBIT_ERR_UNSUPPORTED",
     -4: "MLA_LOWBIT_ERR_WORKSPACE", -5: "MLA_LOWBIT_ERR_HIP",
 }
-EXPORTS = ("mla_lowbit_layout_query", "mla_lowbit_write", "mla_lowbit_decode_workspace",
+EXPORTS = ("mla_lowbit_layout_query", "mla_lowbit_write", "mla_lowbit_write_transformed",
+           "mla_lowbit_decode_workspace",
            "mla_lowbit_decode", "mla_lowbit_strerror")
 
 
@@ -79,6 +80,8 @@ def lib():
         L.mla_lowbit_layout_query.argtypes = [P, P]
         L.mla_lowbit_write.restype = ctypes.c_int
         L.mla_lowbit_write.argtypes = [P, P, P, P, P, i32, i32, i32, P, i32, i32, P, P, P, P, P]
+        L.mla_lowbit_write_transformed.restype = ctypes.c_int
+        L.mla_lowbit_write_transformed.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, i32, i32, P, P, P, P, P]
         L.mla_lowbit_decode_workspace.restype = ctypes.c_int
         L.mla_lowbit_decode_workspace.argtypes = [P, i32, i32, i32, P]
         L.mla_lowbit_decode.restype = ctypes.c_int
@@ -135,6 +138,17 @@ def mla_lowbit_write(layout: Layout, c_kv, k_r, cu_new, seqlens_before, batch: i
     _check(rc, "mla_lowbit_write")
 
 
+def mla_lowbit_write_transformed(layout: Layout, a_c, c_kv, k_r, cu_new, seqlens_before, batch: int,
+                                 total_new: int, max_new_per_seq: int, block_table, max_pages: int,
+                                 num_pool_pages: int, page_pool, sink_buf, ring_buf, rope_tail,
+                                 stream=None) -> None:
+    rc = lib().mla_lowbit_write_transformed(
+        ctypes.byref(layout.c()), _ptr(a_c), _ptr(c_kv), _ptr(k_r), _ptr(cu_new), _ptr(seqlens_before),
+        batch, total_new, max_new_per_seq, _ptr(block_table), max_pages, num_pool_pages, _ptr(page_pool),
+        _ptr(sink_buf), _ptr(ring_buf), _ptr(rope_tail), _stream(stream))
+    _check(rc, "mla_lowbit_write_transformed")
+
+
 def mla_lowbit_decode_workspace(layout: Layout, batch: int, heads: int, max_seqlen: int) -> int:
     n = ctypes.c_size_t()
     _check(lib().mla_lowbit_decode_workspace(ctypes.byref(layout.c()), batch, heads, max_seqlen,
@@ -179,8 +193,9 @@ class DeviceCache:
     def capacity(self) -> int:
         return self.max_pages * self.layout.page_size
 
-    def append(self, c_kv, k_r, counts, stream=None) -> None:
-        """Append counts[b] new tokens per sequence (rows of c_kv / k_r in order)."""
+    def append(self, c_kv, k_r, counts, stream=None, a_c=None) -> None:
+        """Append counts[b] new tokens per sequence (rows of c_kv / k_r in order);
+        with a_c (bf16 [512][512]) the latent rows are transformed in the writer."""
         import torch
         counts = [int(c) for c in counts]
         if len(counts) != self.batch or min(counts) < 0:
@@ -192,9 +207,14 @@ class DeviceCache:
             cu.append(cu[-1] + c)
         dev = self.pool.device
         cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
-        mla_lowbit_write(self.layout, c_kv, k_r, cu_t, self.lengths, self.batch, cu[-1], max(counts),
-                         self.block_table, self.max_pages, self.num_pool_pages, self.pool, self.sink,
-                         self.ring, self.tail, stream)
+        if a_c is None:
+            mla_lowbit_write(self.layout, c_kv, k_r, cu_t, self.lengths, self.batch, cu[-1], max(counts),
+                             self.block_table, self.max_pages, self.num_pool_pages, self.pool, self.sink,
+                             self.ring, self.tail, stream)
+        else:
+            mla_lowbit_write_transformed(self.layout, a_c, c_kv, k_r, cu_t, self.lengths, self.batch, cu[-1],
+                                         max(counts), self.block_table, self.max_pages, self.num_pool_pages,
+                                         self.pool, self.sink, self.ring, self.tail, stream)
         self.lengths += torch.tensor(counts, dtype=torch.int32, device=dev)
         self.host_lengths = [a + c for a, c in zip(self.host_lengths, counts)]
 

@@ -129,6 +129,29 @@ int mla_lowbit_write(const mla_lowbit_layout* layout, const void* c_kv, const vo
                      int32_t max_pages, int32_t num_pool_pages, void* page_pool, void* sink_buf,
                      void* ring_buf, void* rope_tail, hipStream_t stream);
 
+/*
+ * The same writer with the latent transform applied inside it (RAQ-MLA
+ * Figure 4 caption: A_c acts on the latent before quantization, its inverse
+ * is folded into the read-side weights; appendix Table 9: the transform
+ * fused into the write kernel).  Every token's latent is replaced by
+ *   y[c] = bf16( sum over k = 0..511 of A_c[c][k] * c_kv[k] )
+ * with the sum an fp32 fused multiply-add chain in ascending k, rounded once
+ * to the nearest bf16 (ties to even); y is then cached exactly as
+ * mla_lowbit_write caches a latent row (codes, metadata, sink and ring
+ * copies).  k_R is not transformed.  The result equals mla_lowbit_write on
+ * the rows y, bit for bit.
+ *
+ *   a_c            bf16 [512][512] row-major ([output][input]), 16-B aligned,
+ *                  read only; required (NULL is an argument error)
+ *   other arguments, errors and ownership as mla_lowbit_write.
+ */
+int mla_lowbit_write_transformed(const mla_lowbit_layout* layout, const void* a_c, const void* c_kv,
+                                 const void* k_r, const int32_t* cu_new, const int32_t* seqlens_before,
+                                 int32_t batch, int32_t total_new, int32_t max_new_per_seq,
+                                 const int32_t* block_table, int32_t max_pages, int32_t num_pool_pages,
+                                 void* page_pool, void* sink_buf, void* ring_buf, void* rope_tail,
+                                 hipStream_t stream);
+
 /* Bytes of device workspace mla_lowbit_decode needs for this shape. Host only. */
 int mla_lowbit_decode_workspace(const mla_lowbit_layout* layout, int32_t batch, int32_t heads,
                                 int32_t max_seqlen, size_t* bytes);

@@ -29,7 +29,7 @@ def _to_dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
 
 
-def _build(torch, name, P, bits, clip, sink, local, lengths, seed, chunks=None):
+def _build(torch, name, P, bits, clip, sink, local, lengths, seed, chunks=None, a_c=None):
     from bit_kv_cache_writer_amd import mla
     glay, olay = layouts(P, bits, clip, sink, local)
     B = len(lengths)
@@ -40,8 +40,12 @@ def _build(torch, name, P, bits, clip, sink, local, lengths, seed, chunks=None):
     gpu = mla.DeviceCache(glay, B, max_pages, bt, n_pool)
     ref = OracleCache(olay, B, max_pages, bt, n_pool)
     # oracle: one bulk append
-    ref.append(np.concatenate([t[0][:L] for t, L in zip(toks, lengths)]),
-               np.concatenate([t[1][:L] for t, L in zip(toks, lengths)]), lengths)
+    ref_ckv = np.concatenate([t[0][:L] for t, L in zip(toks, lengths)])
+    if a_c is not None:  # the oracle caches bf16(A_c x) in place of x
+        import oracle
+        ref_ckv = oracle.transform(a_c, ref_ckv)
+    ref.append(ref_ckv, np.concatenate([t[1][:L] for t, L in zip(toks, lengths)]), lengths)
+    a_dev = None if a_c is None else _to_dev(torch, a_c)
     # GPU: bulk, or the given chunk schedule (list of per-sequence count lists)
     chunks = chunks or [lengths]
     pos = [0] * B
@@ -49,7 +53,7 @@ def _build(torch, name, P, bits, clip, sink, local, lengths, seed, chunks=None):
         ckv = np.concatenate([toks[b][0][pos[b]:pos[b] + c] for b, c in enumerate(counts)])
         kr = np.concatenate([toks[b][1][pos[b]:pos[b] + c] for b, c in enumerate(counts)])
         say(name, "GPU append", counts[:8])
-        gpu.append(_to_dev(torch, ckv), _to_dev(torch, kr), counts)
+        gpu.append(_to_dev(torch, ckv), _to_dev(torch, kr), counts, a_c=a_dev)
         pos = [p + c for p, c in zip(pos, counts)]
     torch.cuda.synchronize()
     assert pos == list(lengths)
@@ -103,6 +107,66 @@ def test_chunked_appends_equal_bulk(torch_cuda):
     gpu2, ref2 = _build(torch, "chunked_c4r4", 32, 4, 0.0, 4, 8, lengths, seed=92,
                         chunks=[[1, 1, 1]] * 7 + [[L - 7 for L in lengths]])
     compare_cache(gpu2, ref2)
+
+
+TRANSFORM_CASES = [
+    # name, P, bits, clip, sink, local, lengths, chunk schedule (None = one bulk append)
+    ("xf_c4r4_p64_steps", 64, 4, 0.0, 4, 32, [3, 70, 130, 9],
+     [[1, 1, 1, 1]] * 3 + [[0, 67, 127, 6]]),
+    ("xf_c2r4_p128_bulk", 128, 2, 0.94, 4, 128, [300, 5, 129], None),
+    ("xf_c4r4_p32_noprot", 32, 4, 0.0, 0, 0, [64, 33], [[1, 1], [20, 0], [43, 32]]),
+]
+
+
+@pytest.mark.parametrize("case", TRANSFORM_CASES, ids=[c[0] for c in TRANSFORM_CASES])
+def test_transformed_writer_parity(torch_cuda, case):
+    """The writer with the latent transform A_c inside it (a seeded random
+    orthogonal matrix) caches, bit for bit, what the oracle caches for the
+    rows bf16(A_c x); decode over that cache matches the oracle's."""
+    torch = torch_cuda
+    name, P, bits, clip, sink, local, lengths, chunks = case
+    a_c = wl.random_orthogonal_bf16(len(name))
+    gpu, ref = _build(torch, name, P, bits, clip, sink, local, lengths, seed=len(name) + 500,
+                      chunks=chunks, a_c=a_c)
+    say(name, "compare cache bytes")
+    compare_cache(gpu, ref)
+    ql, qr = random_queries(31, len(lengths), 16)
+    scale = 1.0 / math.sqrt(192.0)
+    say(name, "GPU decode")
+    out, lse = gpu.decode(_to_dev(torch, ql), _to_dev(torch, qr), scale)
+    torch.cuda.synchronize()
+    r_out, r_lse = ref.decode(ql, qr, scale)
+    worst = compare_decode(out.cpu().numpy(), lse.cpu().numpy(), r_out, r_lse)
+    say(name, f"worst row rel err {worst:.2e}")
+
+
+def test_transformed_writer_identity_equals_plain(torch_cuda):
+    """A_c = I through the transforming writer gives the plain writer's bytes
+    (the inputs hold no -0, which the fma chain would turn into +0)."""
+    torch = torch_cuda
+    lengths = [150, 64, 1]
+    eye = np.zeros((512, 512), np.float32)
+    np.fill_diagonal(eye, 1.0)
+    a_c = wl.f32_to_bf16_bits(eye)
+    gpu_t, ref = _build(torch, "xf_identity", 64, 4, 0.0, 4, 32, lengths, seed=77, a_c=a_c)
+    gpu_p, _ = _build(torch, "xf_identity_plain", 64, 4, 0.0, 4, 32, lengths, seed=77)
+    compare_cache(gpu_t, ref)
+    for a, b in ((gpu_t.pool, gpu_p.pool), (gpu_t.sink, gpu_p.sink), (gpu_t.ring, gpu_p.ring),
+                 (gpu_t.tail, gpu_p.tail)):
+        assert torch.equal(a, b)
+
+
+def test_transformed_writer_rejects_null_matrix(torch_cuda):
+    from bit_kv_cache_writer_amd import mla
+    torch = torch_cuda
+    glay, _ = layouts(64, 4, 0.0, 4, 32)
+    c = mla.DeviceCache(glay, 1, 1, [[0]], 1)
+    x = torch.zeros((1, 512), dtype=torch.int16, device="cuda")
+    k = torch.zeros((1, 64), dtype=torch.int16, device="cuda")
+    cu = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    with pytest.raises(mla.MlaError):
+        mla.mla_lowbit_write_transformed(glay, None, x, k, cu, c.lengths, 1, 1, 1, c.block_table, 1, 1,
+                                         c.pool, c.sink, c.ring, c.tail)
 
 
 def test_decode_edge_inputs(torch_cuda):
