@@ -335,6 +335,103 @@ def ragged(steps: int) -> int:
     return 0
 
 
+def transform_cost(steps: int) -> int:
+    """Per-layer cost of the latent transform A_c (RAQ-MLA appendix Table 9:
+    one GLM-shaped MLA layer, 2K cached tokens, decode batch 1..64): the
+    writer with A_c fused in against the plain writer, and a standalone bf16
+    GEMM (the library's, x A_c^T) that a separate transform would run before
+    the plain writer.  C4R4, page 64, sink 4 + local 128, 20 heads; one new
+    token per sequence at position 2053 (a step that completes no page).
+    A_c is a seeded random orthogonal matrix.  Times are GPU times per call
+    from events, with the calls queued behind a sleep kernel so that the host
+    does not pace them.  One JSON line per batch."""
+    import torch
+
+    from bit_kv_cache_writer_amd import mla
+    from bit_kv_cache_writer_amd import workloads as wl
+
+    mla.lib()
+    lay = mla.Layout(64, 4, 0.0, 4, 128)
+    heads, scale, pos = 20, 1.0 / math.sqrt(192.0), 2053
+    a_c = torch.from_numpy(wl.random_orthogonal_bf16(5).view(np.int16)).cuda()
+    a_t = a_c.view(torch.bfloat16).t().contiguous()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(17)
+    stream = torch.cuda.current_stream()
+    reps = max(20, steps * 20)
+
+    def bf16_rows(n, width):
+        return torch.randn((n, width), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        try:
+            torch.cuda._sleep(50_000_000)  # the queue fills while this runs
+        except (AttributeError, RuntimeError):
+            pass
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]) * 1000.0)
+
+    for B in (1, 2, 4, 8, 64):
+        max_pages = (pos + 1 + 63) // 64
+        n_pool = B * max_pages
+        bt = np.arange(n_pool, dtype=np.int32).reshape(B, max_pages)
+        caches = []
+        for _ in range(2):
+            c = mla.DeviceCache(lay, B, max_pages, bt, n_pool)
+            c.append(bf16_rows(B * pos, 512), bf16_rows(B * pos, 64), [pos] * B)
+            caches.append(c)
+        plain, fused = caches
+        x = bf16_rows(B, 512)
+        kr = bf16_rows(B, 64)
+        cu_new = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+        before = torch.full((B,), pos, dtype=torch.int32, device="cuda")
+        seqlens = torch.full((B,), pos + 1, dtype=torch.int32, device="cuda")
+        ws_bytes = mla.mla_lowbit_decode_workspace(lay, B, heads, pos + 1)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        out = torch.empty((B, heads, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, heads), dtype=torch.float32, device="cuda")
+        q_lat = bf16_rows(B * heads, 512)
+        q_rope = bf16_rows(B * heads, 64)
+        y = torch.empty((B, 512), dtype=torch.bfloat16, device="cuda")
+
+        def w_plain():
+            mla.mla_lowbit_write(lay, x, kr, cu_new, before, B, B, 1, plain.block_table, max_pages, n_pool,
+                                 plain.pool, plain.sink, plain.ring, plain.tail, stream)
+
+        def w_fused():
+            mla.mla_lowbit_write_transformed(lay, a_c, x, kr, cu_new, before, B, B, 1, fused.block_table,
+                                             max_pages, n_pool, fused.pool, fused.sink, fused.ring, fused.tail,
+                                             stream)
+
+        def gemm():
+            torch.matmul(x.view(torch.bfloat16), a_t, out=y)
+
+        def dec():
+            mla.mla_lowbit_decode(lay, q_lat, q_rope, B, heads, scale, plain.pool, n_pool, plain.block_table,
+                                  max_pages, seqlens, pos + 1, plain.sink, plain.ring, plain.tail, out, lse, ws,
+                                  ws_bytes, stream)
+
+        t_plain, t_fused, t_gemm, t_dec = timed(w_plain), timed(w_fused), timed(gemm), timed(dec)
+        cost = t_fused - t_plain
+        print(json.dumps({"transform": "latent transform A_c (512 x 512) per new token, C4R4 page 64, "
+                                       "2054 cached tokens, 20 heads",
+                          "batch": B, "plain_write_us": round(t_plain, 2), "fused_write_us": round(t_fused, 2),
+                          "fused_cost_us": round(cost, 2), "standalone_gemm_us": round(t_gemm, 2),
+                          "decode_us": round(t_dec, 2),
+                          "fused_share": round(cost / (t_plain + t_dec), 4)}), flush=True)
+        del caches, plain, fused
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +443,8 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true", help="time a plain 1 GiB copy and exit")
     ap.add_argument("--sweep", action="store_true", help="context sweep 1K..1M at batch 1 and 8 (JSON lines)")
     ap.add_argument("--ragged", action="store_true", help="ragged-batch decode and chunked-prefill writer (JSON lines)")
+    ap.add_argument("--transform", action="store_true",
+                    help="cost of the latent transform fused into the writer vs a standalone GEMM (JSON lines)")
     ap.add_argument("--bf16-baseline", action="store_true",
                     help="the same workload with every token protected (sink 0, window = N <= 4096): the decode "
                          "reads a BF16 cache through the same split-KV skeleton")
@@ -369,6 +468,8 @@ def main() -> int:
         return sweep(max(1, min(args.steps, 5)))
     if args.ragged:
         return ragged(max(1, min(args.steps, 5)))
+    if args.transform:
+        return transform_cost(max(1, min(args.steps, 5)))
     mla.lib()
     w = wl.WORKLOADS[args.workload]
     if args.bf16_baseline:

@@ -254,6 +254,39 @@ __device__ inline TokenRows load_token(const WriterParams& p, int64_t row, int l
   return r;
 }
 
+// Columns k0 .. k0 + 63 of the latent transform for N tokens: acc[w] of
+// token w continues its fp32 fma chain over A_c row `arow` (64 staged bf16
+// values) times the token's inputs xs[w][k0 ..] (fp32, broadcast from LDS),
+// in ascending order.  N is a compile-time count so that the pass has no
+// branches and its LDS reads can all be issued ahead of the chain.
+template <int N>
+__device__ inline void transform_pass(float (&acc)[kWaves], const uint8_t* arow, const float (*xs)[kLatentDim],
+                                      int k0) {
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    const uint4 a8 = *reinterpret_cast<const uint4*>(arow + 16 * kb);
+    const float a[8] = {bf16_to_f32(a8.x & 0xFFFFu), bf16_to_f32(a8.x >> 16), bf16_to_f32(a8.y & 0xFFFFu),
+                        bf16_to_f32(a8.y >> 16),     bf16_to_f32(a8.z & 0xFFFFu), bf16_to_f32(a8.z >> 16),
+                        bf16_to_f32(a8.w & 0xFFFFu), bf16_to_f32(a8.w >> 16)};
+    const int k = k0 + 8 * kb;
+#pragma unroll
+    for (int w = 0; w < N; ++w) {
+      const float4 x0 = *reinterpret_cast<const float4*>(&xs[w][k]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&xs[w][k + 4]);
+      float s = acc[w];
+      s = fmaf(a[0], x0.x, s);
+      s = fmaf(a[1], x0.y, s);
+      s = fmaf(a[2], x0.z, s);
+      s = fmaf(a[3], x0.w, s);
+      s = fmaf(a[4], x1.x, s);
+      s = fmaf(a[5], x1.y, s);
+      s = fmaf(a[6], x1.z, s);
+      s = fmaf(a[7], x1.w, s);
+      acc[w] = s;
+    }
+  }
+}
+
 template <bool kTransform>
 __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   const int b = blockIdx.x / p.pages_per_seq_grid;
@@ -309,14 +342,20 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
     // The latent transform (RAQ-MLA Figure 4 caption; appendix Table 9, the
     // fused variant): y = A_c x per token, for up to kWaves tokens at a time.
     // Thread c forms output channel c of each token as an fp32 fma chain over
-    // the 512 inputs in ascending order (the inputs broadcast from LDS, A_c's
-    // row c read 16 bytes at a time), rounded once to bf16; wave w then
+    // the 512 inputs in ascending order, rounded once to bf16; wave w then
     // caches token t0 + w from that bf16 row exactly as it caches an
-    // untransformed one (codes, metadata, sink and ring copies).
+    // untransformed one (codes, metadata, sink and ring copies).  A_c passes
+    // through LDS 64 input columns at a time, read as whole 128-byte row
+    // segments (coalesced) and stored with a padded row pitch so that each
+    // thread's reads of its own row do not collide; the inputs are broadcast
+    // from LDS.
+    constexpr int kAChunk = 64;                // input columns per LDS pass
+    constexpr int kAPitch = 2 * kAChunk + 16;  // bytes per staged row
+    __shared__ __attribute__((aligned(16))) uint8_t s_a[kLatentDim * kAPitch];
     __shared__ __attribute__((aligned(16))) float s_x[kWaves][kLatentDim];
     __shared__ uint4 s_y[kWaves][kLatentDim / 8];
     const int c = static_cast<int>(threadIdx.x);
-    const uint4* const arow = reinterpret_cast<const uint4*>(p.a_c + static_cast<int64_t>(c) * kLatentDim);
+    const int st_row = c >> 3, st_part = c & 7;  // staging: 16 bytes of row st_row + 64 j
     for (int t0 = tb; t0 < te; t0 += kWaves) {
       const int n = min(kWaves, te - t0);
       if (wave < n) {
@@ -329,32 +368,53 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
         *reinterpret_cast<float4*>(&s_x[wave][8 * lane]) = lo;
         *reinterpret_cast<float4*>(&s_x[wave][8 * lane + 4]) = hi;
       }
-      __syncthreads();
       float acc[kWaves];
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) acc[w] = 0.0f;
-#pragma unroll 4
-      for (int kb = 0; kb < kLatentDim / 8; ++kb) {
-        const uint4 a8 = arow[kb];
-        const float a[8] = {bf16_to_f32(a8.x & 0xFFFFu), bf16_to_f32(a8.x >> 16), bf16_to_f32(a8.y & 0xFFFFu),
-                            bf16_to_f32(a8.y >> 16),     bf16_to_f32(a8.z & 0xFFFFu), bf16_to_f32(a8.z >> 16),
-                            bf16_to_f32(a8.w & 0xFFFFu), bf16_to_f32(a8.w >> 16)};
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          if (w < n) {
-            const float4 x0 = *reinterpret_cast<const float4*>(&s_x[w][8 * kb]);
-            const float4 x1 = *reinterpret_cast<const float4*>(&s_x[w][8 * kb + 4]);
-            float s = acc[w];
-            s = fmaf(a[0], x0.x, s);
-            s = fmaf(a[1], x0.y, s);
-            s = fmaf(a[2], x0.z, s);
-            s = fmaf(a[3], x0.w, s);
-            s = fmaf(a[4], x1.x, s);
-            s = fmaf(a[5], x1.y, s);
-            s = fmaf(a[6], x1.z, s);
-            s = fmaf(a[7], x1.w, s);
-            acc[w] = s;
-          }
+      // this thread's 16-byte pieces of the next pass's A_c columns, loaded
+      // one pass ahead so that they arrive while the current pass computes
+      auto a_piece = [&](int j, int k0) {
+        return reinterpret_cast<const uint4*>(p.a_c + static_cast<int64_t>(st_row + 64 * j) * kLatentDim + k0)[st_part];
+      };
+      uint4 nx0 = a_piece(0, 0), nx1 = a_piece(1, 0), nx2 = a_piece(2, 0), nx3 = a_piece(3, 0);
+      uint4 nx4 = a_piece(4, 0), nx5 = a_piece(5, 0), nx6 = a_piece(6, 0), nx7 = a_piece(7, 0);
+#pragma unroll 1
+      for (int k0 = 0; k0 < kLatentDim; k0 += kAChunk) {
+        __syncthreads();  // the previous pass's reads of s_a are done
+        {
+          uint8_t* const dst = s_a + st_row * kAPitch + 16 * st_part;
+          *reinterpret_cast<uint4*>(dst + 0 * 64 * kAPitch) = nx0;
+          *reinterpret_cast<uint4*>(dst + 1 * 64 * kAPitch) = nx1;
+          *reinterpret_cast<uint4*>(dst + 2 * 64 * kAPitch) = nx2;
+          *reinterpret_cast<uint4*>(dst + 3 * 64 * kAPitch) = nx3;
+          *reinterpret_cast<uint4*>(dst + 4 * 64 * kAPitch) = nx4;
+          *reinterpret_cast<uint4*>(dst + 5 * 64 * kAPitch) = nx5;
+          *reinterpret_cast<uint4*>(dst + 6 * 64 * kAPitch) = nx6;
+          *reinterpret_cast<uint4*>(dst + 7 * 64 * kAPitch) = nx7;
+        }
+        __syncthreads();  // s_a (and, on the first pass, s_x) filled
+        if (k0 + kAChunk < kLatentDim) {
+          const int k1 = k0 + kAChunk;
+          nx0 = a_piece(0, k1);
+          nx1 = a_piece(1, k1);
+          nx2 = a_piece(2, k1);
+          nx3 = a_piece(3, k1);
+          nx4 = a_piece(4, k1);
+          nx5 = a_piece(5, k1);
+          nx6 = a_piece(6, k1);
+          nx7 = a_piece(7, k1);
+        }
+        static_assert(kAChunk == 64, "transform_pass takes 64 columns");
+        const uint8_t* const arow = s_a + c * kAPitch;
+        switch (n) {
+          case 1: transform_pass<1>(acc, arow, s_x, k0); break;
+          case 2: transform_pass<2>(acc, arow, s_x, k0); break;
+          case 3: transform_pass<3>(acc, arow, s_x, k0); break;
+          case 4: transform_pass<4>(acc, arow, s_x, k0); break;
+          case 5: transform_pass<5>(acc, arow, s_x, k0); break;
+          case 6: transform_pass<6>(acc, arow, s_x, k0); break;
+          case 7: transform_pass<7>(acc, arow, s_x, k0); break;
+          default: transform_pass<8>(acc, arow, s_x, k0); break;
         }
       }
       uint16_t* const ys = reinterpret_cast<uint16_t*>(&s_y[0][0]);

@@ -29,6 +29,12 @@ MUTANTS = {
     "page_complete_wrong": ("int page_complete = (int64_t)(pidx + 1) * P <= Lb;",
                             "int page_complete = (int64_t)(pidx + 1) * P < Lb;"),
     "softmax_not_max_subtracted": ("s += exp(z[(int64_t)h * Lb + j] - m);", "s += exp(z[(int64_t)h * Lb + j] - m) * 1.0001;"),
+    "transform_ties_away": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))",
+                            "if (dropped >= 0x8000u)"),
+    "transform_matrix_transposed": ("acc = fmaf(bf16_to_f32(a_c[(int64_t)c * dim + k])",
+                                    "acc = fmaf(bf16_to_f32(a_c[(int64_t)k * dim + c])"),
+    "transform_double_accumulation": ("      float acc = 0.0f;\n      for (int32_t k = 0; k < dim; ++k)\n        acc = fmaf(",
+                                      "      double acc = 0.0;\n      for (int32_t k = 0; k < dim; ++k)\n        acc = fma("),
 }
 
 
