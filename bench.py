@@ -450,7 +450,7 @@ def main() -> int:
                          "reads a BF16 cache through the same split-KV skeleton")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         return 2
 

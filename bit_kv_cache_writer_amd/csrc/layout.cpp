@@ -80,7 +80,7 @@ extern "C" const char* mla_lowbit_strerror(int code) {
     case MLA_LOWBIT_OK: return "ok";
     case MLA_LOWBIT_ERR_LAYOUT: return "invalid or unsupported cache-layout descriptor";
     case MLA_LOWBIT_ERR_ARG: return "invalid argument (null or misaligned pointer, or bad size)";
-    case MLA_LOWBIT_ERR_UNSUPPORTED: return "request not supported by this build";
+    case MLA_LOWBIT_ERR_UNSUPPORTED: return "valid request the library does not run";
     case MLA_LOWBIT_ERR_WORKSPACE: return "workspace smaller than mla_lowbit_decode_workspace()";
     case MLA_LOWBIT_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown error code";

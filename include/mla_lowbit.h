@@ -44,7 +44,7 @@ extern "C" {
 #define MLA_LOWBIT_OK 0
 #define MLA_LOWBIT_ERR_LAYOUT (-1)      /* invalid or unsupported layout descriptor */
 #define MLA_LOWBIT_ERR_ARG (-2)         /* null / misaligned pointer, bad size */
-#define MLA_LOWBIT_ERR_UNSUPPORTED (-3) /* valid request this build does not run */
+#define MLA_LOWBIT_ERR_UNSUPPORTED (-3) /* valid request the library does not run */
 #define MLA_LOWBIT_ERR_WORKSPACE (-4)   /* workspace smaller than required */
 #define MLA_LOWBIT_ERR_HIP (-5)         /* a HIP launch failed */
 
