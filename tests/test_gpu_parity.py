@@ -74,6 +74,9 @@ CASES = [
     # one long sequence: over 128 splits, so the merge loads the splits'
     # (max, sum) blocks in several rounds
     ("c4r4_p128_b1_long", 128, 4, 0.0, 4, 128, [40000], 16),
+    # the layout's largest protection: sink 64 and a 4096-token window, one
+    # sequence past both and one inside them
+    ("c2r4_p64_maxwin", 64, 2, 0.94, 64, 4096, [4500, 3000], 16),
 ]
 
 
