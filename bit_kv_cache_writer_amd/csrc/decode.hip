@@ -785,14 +785,14 @@ __device__ void dense_scores(float (&sc)[4], const QueryOps<BITS>& q, const uint
     lds_st<u32x4>(rbuf + u * 1024 + 16 * lane, w);
   }
   // latent rows: lane handles channels 16 part .. 16 part + 15 of rows
-  // lane / 32 + 2 m, four rows per batch
+  // lane / 32 + 2 m, all eight of its rows requested before any is converted
   const int part = lane & 31;
-#pragma unroll 1
-  for (int m0 = 0; m0 < kTile / 2; m0 += 4) {
-    u32x4 ra[4], rc[4];
-    int kind[4];
+  {
+    constexpr int m0 = 0;
+    u32x4 ra[kTile / 2], rc[kTile / 2];
+    int kind[kTile / 2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kTile / 2; ++u) {
       const int t = 2 * (m0 + u) + (lane >> 5);
       const DenseSrc s = dense_src(p, b, sr, k0 + t);
       kind[u] = s.kind;
@@ -814,7 +814,7 @@ __device__ void dense_scores(float (&sc)[4], const QueryOps<BITS>& q, const uint
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kTile / 2; ++u) {
       const int t = 2 * (m0 + u) + (lane >> 5);
       float v[16];
       if (kind[u] == 2) {
