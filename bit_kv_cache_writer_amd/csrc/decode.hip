@@ -959,18 +959,34 @@ __device__ void dense_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], co
   const uint8_t* const qr_row = smem + kOffQr + n16 * 128;
   uint8_t* const qops = smem + kOffX;  // converted query, until round 0 writes x tiles
 
-  {
-    QueryRows qrows;
-    fetch_query(qrows, p, cx.b, cx.hb, wave, lane);
-    publish_query<BITS, false>(qrows, qops, smem + kOffQr, wave, lane);
-  }
-  static_assert(kQopsBytes <= kWaves * kXTile, "the converted query fits the x tiles");
   const int n_dense = sr.lo_p + (sr.L - sr.hi_p);
   const int D = (n_dense + kTile - 1) / kTile;
   const int per = (D + p.n_dense - 1) / p.n_dense;
   const int i0 = min(D, ds * per), i1 = min(D, i0 + per);
   const int rounds = (i1 - i0 + kWaves - 1) / kWaves;
   const int my0 = i0 + wave * rounds, my1 = min(i1, my0 + rounds);
+  // Round 0's BF16 rows (9 lines of 128 bytes each; lane: token lane / 4,
+  // lines lane % 4 + 4 j) are touched before the query is requested: loads
+  // complete in order, so the query's wait also covers them, and round 0
+  // then finds them in cache instead of waiting a second HBM round trip.
+  uint32_t touch = 0;
+  if (my0 < my1) {
+    const DenseSrc s = dense_src(p, cx.b, sr, my0 * kTile + (lane >> 2));
+    if (s.kind == 1) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int line = (lane & 3) + 4 * j;
+        if (line < kRowElems * 2 / 128) touch ^= ldg<uint32_t>(reinterpret_cast<const uint8_t*>(s.row) + 128 * line);
+      }
+    }
+  }
+  {
+    QueryRows qrows;
+    fetch_query(qrows, p, cx.b, cx.hb, wave, lane);
+    publish_query<BITS, false>(qrows, qops, smem + kOffQr, wave, lane);
+  }
+  static_assert(kQopsBytes <= kWaves * kXTile, "the converted query fits the x tiles");
+  asm volatile("" ::"v"(touch));  // keeps the touching loads
   lds_barrier();  // query converted
   QueryOps<BITS> q;
   load_query<BITS>(q, qops, lane);
