@@ -72,9 +72,27 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = kDecodeWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStatW = 5;      // per head: sum p, sum p m_g (4)
-constexpr float kPrescale = 1.0f / 256.0f;  // keeps q' and Q_g inside fp16 range
 constexpr float kCodeScale = 16777216.0f;   // 2^24: undoes the subnormal unpack
 constexpr float kNegInf = -INFINITY;
+
+// The power of two that brings magnitude x into the binade [2^(top-1), 2^top)
+// (1 for x = 0): fp16 operands are scaled by it so that they neither overflow
+// nor lose bits to the subnormal range, and the fp32 results are scaled back.
+__device__ inline float pow2_to_binade(float x, int top) {
+  if (!(x > 0.f)) return 1.f;
+  int k = top - __builtin_amdgcn_frexp_expf(x);  // x = f 2^e, f in [0.5, 1)
+  k = k < -100 ? -100 : (k > 100 ? 100 : k);
+  return __builtin_amdgcn_ldexpf(1.f, k);
+}
+
+// Largest |bf16| among the 8 halves of a 16-byte row piece (bf16 magnitudes
+// order like their bit patterns).
+__device__ inline uint32_t bf16_absmax8(u32x4 w) {
+  uint32_t a = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a = max(a, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+  return a;
+}
 
 // BF16-path workgroup LDS map (bytes).  x-tile row: 512 fp16 + 16 B pad (260
 // dwords: rows land 4 banks apart, so row writes and transposed reads are
@@ -231,7 +249,8 @@ __device__ inline float row_allmax(float v) {
 template <int BITS>
 struct QueryOps {
   half8 lat[4][4];  // [group][chunk], slot order of the unpack
-  half8 meta;       // (scale, min) slots of the metadata MFMA, prescaled
+  half8 meta;       // (scale, min) slots of the metadata MFMA, scaled by 1 / meta_mul
+  float meta_mul;   // per head (lane & 15): undoes the metadata operand's scale
 };
 
 // Query staging.  Wave w fetches latent group w of the 16 heads of a head
@@ -294,11 +313,13 @@ constexpr int kQopsSums = 4 * 4 * 64 * 16;
 constexpr int kQopsBytes = kQopsSums + kHeadBlock * 4 * 4;
 
 // Wave w converts its latent group: fp16 operands in the unpack's slot order
-// (divided by the slot's sigma for the masking unpack when kSigma) and Q_w =
-// sum of the group's 128 channels, both into the LDS image; wave 0 also
-// stores the q_rope rows as [head][128 B].
+// (times qscale, a power of two per head, and divided by the slot's sigma for
+// the masking unpack when kSigma) and Q_w = sum of the group's 128 channels
+// (unscaled), both into the LDS image; wave 0 also stores the q_rope rows as
+// [head][128 B].
 template <int BITS, bool kSigma, bool kRope = true>
-__device__ inline void publish_query(const QueryRows& qr, uint8_t* qops, uint8_t* qr_lds, int wave, int lane) {
+__device__ inline void publish_query(const QueryRows& qr, uint8_t* qops, uint8_t* qr_lds, int wave, int lane,
+                                     float qscale = 1.f) {
   const int n16 = lane & 15, gq = lane >> 4;
   float v[32];
 #pragma unroll
@@ -318,7 +339,7 @@ __device__ inline void publish_query(const QueryRows& qr, uint8_t* qops, uint8_t
     half8 x;
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl)
-      x[sl] = static_cast<_Float16>(kSigma ? v[chan_off<BITS>(d, sl)] * (1.f / slot_sigma<BITS>(d, sl))
+      x[sl] = static_cast<_Float16>(kSigma ? v[chan_off<BITS>(d, sl)] * (qscale / slot_sigma<BITS>(d, sl))
                                            : v[chan_off<BITS>(d, sl)]);
     lds_st<half8>(qops + ((wave * 4 + d) * 64 + lane) * 16, x);
   }
@@ -330,7 +351,8 @@ __device__ inline void publish_query(const QueryRows& qr, uint8_t* qops, uint8_t
 }
 
 // MFMA operands of the whole query from the LDS image; Q_g enters the
-// metadata operand (min slots; the scale slots stay zero).
+// metadata operand (min slots; the scale slots stay zero) as fp16 hi + lo,
+// scaled per head so that the largest |Q_g| lies in [2^13, 2^14).
 template <int BITS>
 __device__ inline void load_query(QueryOps<BITS>& q, const uint8_t* qops, int lane) {
   const int n16 = lane & 15, gq = lane >> 4;
@@ -340,9 +362,12 @@ __device__ inline void load_query(QueryOps<BITS>& q, const uint8_t* qops, int la
     for (int d = 0; d < 4; ++d) q.lat[i][d] = lds_ld<half8>(qops + ((i * 4 + d) * 64 + lane) * 16);
   }
   const f32x4 qg = lds_ld<f32x4>(qops + kQopsSums + n16 * 16);
+  const float mscale =
+      pow2_to_binade(fmaxf(fmaxf(fabsf(qg[0]), fabsf(qg[1])), fmaxf(fabsf(qg[2]), fabsf(qg[3]))), 14);
+  q.meta_mul = 1.f / mscale;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float c = qg[i] * kPrescale;
+    const float c = qg[i] * mscale;
     const _Float16 ch = static_cast<_Float16>(c);
     const _Float16 cl = static_cast<_Float16>(c - static_cast<float>(ch));
     const _Float16 z = static_cast<_Float16>(0.f);
@@ -352,12 +377,14 @@ __device__ inline void load_query(QueryOps<BITS>& q, const uint8_t* qops, int la
 }
 
 // Per-page positional-key operands for channels 16*gq + 8e + slot order
-// (masking unpack, as the latent codes): q' = q s / sigma, prescaled, as fp16
-// hi + lo (a bf16 times an fp16 needs more bits than one fp16 holds);
-// bias = sum_c q_c m_c over the lane row's 64 channels.
+// (masking unpack, as the latent codes): q' = q s r / sigma as fp16 hi + lo
+// (a bf16 times an fp16 needs more bits than one fp16 holds), r a power of two
+// per (head, page) that puts the largest |q s| of the head into [2^13, 2^14);
+// mul = 2^24 / r undoes it and the unpack; bias = sum_c q_c m_c over the lane
+// row's 64 channels.
 struct RopeOps {
   half8 hi[2], lo[2];
-  float bias;
+  float bias, mul;
 };
 
 __device__ inline void rope_ops(RopeOps& r, const uint8_t* qr_row, const uint8_t* rmeta, int gq) {
@@ -385,16 +412,22 @@ __device__ inline void rope_ops(RopeOps& r, const uint8_t* qr_row, const uint8_t
     qv[8 + 2 * k] = bf16f(q1[k] & 0xFFFFu);
     qv[8 + 2 * k + 1] = bf16f(q1[k] >> 16);
   }
-  float bias = 0.f;
+  float bias = 0.f, qs[16], big = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) bias = fmaf(qv[c], mn[c], bias);
+  for (int c = 0; c < 16; ++c) {
+    bias = fmaf(qv[c], mn[c], bias);
+    qs[c] = qv[c] * sc[c];
+    big = fmaxf(big, fabsf(qs[c]));
+  }
   r.bias = row_allsum(bias);
+  const float rs = pow2_to_binade(row_allmax(big), 14);
+  r.mul = kCodeScale / rs;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
       const int c = 8 * e + chan_off<4>(0, sl);
-      const float v = qv[c] * sc[c] * (kPrescale / slot_sigma<4>(0, sl));
+      const float v = qs[c] * (rs / slot_sigma<4>(0, sl));
       const _Float16 vh = static_cast<_Float16>(v);
       r.hi[e][sl] = vh;
       r.lo[e][sl] = static_cast<_Float16>(v - static_cast<float>(vh));
@@ -499,10 +532,17 @@ __device__ inline void wait_tiles_after(int after) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Score from the MFMA sums: latent 2^-24 sum_g s_g q_g.code_g (v), metadata
-// kPrescale sum_g m_g Q_g (meta), positional 2^-24 kPrescale q s.code (rope).
-__device__ inline float score_of(float v, float meta, float rope, float bias) {
-  return fmaf(fmaf(rope, 1.f / kPrescale, v), kCodeScale, fmaf(meta, 1.f / kPrescale, bias));
+// Per-head multipliers that undo the operand scalings of the score MFMAs:
+// latent (2^24 / the query's scale), metadata and positional key.
+struct ScoreMul {
+  float lat, meta, rope;
+};
+
+// Score from the MFMA sums: latent sum_g s_g q_g.code_g (v), metadata
+// sum_g m_g Q_g (meta), positional q s.code (rope), each scaled as its
+// operands were; bias = sum_c q_R,c m_R,c.
+__device__ inline float score_of(float v, float meta, float rope, float bias, const ScoreMul& k) {
+  return fmaf(rope, k.rope, fmaf(v, k.lat, fmaf(meta, k.meta, bias)));
 }
 
 // Score inputs of one packed tile from its LDS slot: lane (t, gq) gets the
@@ -534,9 +574,9 @@ __device__ inline void load_score_in(ScoreIn<BITS>& si, const uint8_t* slot, int
   si.ma = lds_ld<u32x4>(slot + G::kOffMeta + 16 * n16);
 }
 
-// Score MFMAs of one packed tile: acc[g] = 2^-24 q_g . code_g per latent
-// group g, acc[4] = kPrescale sum_g m_g Q_g (metadata), acc[5] = 2^-24
-// kPrescale q_R s . code_R (positional key).
+// Score MFMAs of one packed tile: acc[g] = q_g . code_g per latent group g,
+// acc[4] = sum_g m_g Q_g (metadata), acc[5] = q_R s . code_R (positional
+// key), each scaled as its operands are (ScoreMul undoes it).
 template <int BITS>
 __device__ inline void score_mfma(f32x4 (&acc)[6], const ScoreIn<BITS>& si, const QueryOps<BITS>& q,
                                   const RopeOps& ro) {
@@ -564,7 +604,8 @@ __device__ inline void score_mfma(f32x4 (&acc)[6], const ScoreIn<BITS>& si, cons
 // gets tokens 4 gq + r of head h.  md[r] = the metadata words of token 4 gq + r.
 template <int BITS>
 __device__ inline void score_finish(float (&sc)[4], u32x4 (&md)[4], const f32x4 (&acc)[6], const uint8_t* slot,
-                                    float bias, bool has, int j0, int vlo, int vhi, int gq, float c_log2) {
+                                    float bias, const ScoreMul& km, bool has, int j0, int vlo, int vhi, int gq,
+                                    float c_log2) {
   using G = TileGeom<BITS>;
 #pragma unroll
   for (int r = 0; r < 4; ++r) md[r] = lds_ld<u32x4>(slot + G::kOffMeta + 16 * (4 * gq + r));
@@ -576,13 +617,13 @@ __device__ inline void score_finish(float (&sc)[4], u32x4 (&md)[4], const f32x4 
   }
   if (has && j0 >= vlo && j0 + kTile <= vhi) {  // whole tile valid
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = score_of(v[r], acc[4][r], acc[5][r], bias) * c_log2;
+    for (int r = 0; r < 4; ++r) sc[r] = score_of(v[r], acc[4][r], acc[5][r], bias, km) * c_log2;
     return;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = j0 + 4 * gq + r;
-    const float z = score_of(v[r], acc[4][r], acc[5][r], bias);
+    const float z = score_of(v[r], acc[4][r], acc[5][r], bias, km);
     sc[r] = (has && t >= vlo && t < vhi) ? z * c_log2 : kNegInf;
   }
 }
@@ -591,31 +632,41 @@ __device__ inline void score_finish(float (&sc)[4], u32x4 (&md)[4], const f32x4 
 // tokens 8 gq .. 8 gq + 7 of the K block (tiles 2 kb, 2 kb + 1), fp16.
 __device__ inline int p_entry(int kb, int g, int gq, int h) { return (((kb * 4 + g) * 4 + gq) * kHeadBlock + h) * 16; }
 
-// Weights of this wave's packed tile: P'_g = fp16(fp16(fp16(p) / sigma) s_g) into
-// the P' entries its tokens fall in (tokens 4 gq + 2, 4 gq + 3 land in the
-// output unpack's sigma = 16 slots); adds this lane's sums of p and of p m_g
-// to st.
+// Headroom of this lane's four tokens of a packed tile (metadata words md):
+// k = E - 7, E the exponent with max_g s_g < 2^E over the tokens' latent
+// scales (fp16 bit patterns: field 0 gives E = -14, the subnormal bound).
+// The running max m of a packed workgroup is raised so that t + k <= m + 8
+// for every token (t its score), hence p = 2^(t - m) <= 2^(8 - k) and
+// p s_g < 2^15: the fp16 weights P'_g below never overflow, and the largest
+// of a tile sits near 2^14, far above the subnormal range, at any latent
+// magnitude.  k >= -21 bounds p by 2^29, which fp32 sums hold.
+__device__ inline float scale_headroom(const u32x4 (&md)[4]) {
+  uint32_t a = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) a = max(a, md[r][g] & 0x7FFFu);
+  }
+  return static_cast<float>(a >> 10) - 21.f;
+}
+
+// Weights of this wave's packed tile: P'_g = fp16(p s_g / sigma), one
+// rounding of the fp32 product, into the P' entries its tokens fall in
+// (tokens 4 gq + 2, 4 gq + 3 land in the output unpack's sigma = 16 slots);
+// adds this lane's sums of p and of p m_g (fp32) to st.
 __device__ inline void packed_weights(const float (&pr)[4], const u32x4 (&md)[4], uint8_t* pbase,
                                       float (&st)[kStatW], int wave, int n16, int gq) {
-  const half2 ph[2] = {half2{static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1])},
-                       half2{static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])}};
   st[0] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  const half2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-  const half2 pw[2] = {ph[0], ph[1] * sixteenth};
+  const float pw[4] = {pr[0], pr[1], pr[2] * 0.0625f, pr[3] * 0.0625f};
   const int at = 8 * (gq & 1);  // tokens 4 gq .. 4 gq + 3 of the tile
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     half4 pa;
     float ms = st[1 + g];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t w0 = md[2 * k][g], w1 = md[2 * k + 1][g];
-      const half2 s2 = {__builtin_bit_cast(half2, w0)[0], __builtin_bit_cast(half2, w1)[0]};
-      const half2 m2 = {__builtin_bit_cast(half2, w0)[1], __builtin_bit_cast(half2, w1)[1]};
-      const half2 ps = pw[k] * s2;
-      ms = __builtin_amdgcn_fdot2(ph[k], m2, ms, false);
-      pa[2 * k] = ps[0];
-      pa[2 * k + 1] = ps[1];
+    for (int r = 0; r < 4; ++r) {
+      pa[r] = static_cast<_Float16>(pw[r] * lo_f16(md[r][g]));
+      ms = fmaf(pr[r], hi_f16(md[r][g]), ms);
     }
     lds_st<half4>(pbase + p_entry(wave >> 1, g, 2 * (wave & 1) + (gq >> 1), n16) + at, pa);
     st[1 + g] = ms;
@@ -898,7 +949,9 @@ struct WgCtx {
 // layout) and m_o.  The reference max only moves when a tile max exceeds it
 // by more than kMaxSlack (log2 units): weights stay below 2^kMaxSlack, and
 // most rounds keep every factor at exactly 1 so that the rescale is skipped.
-// Both layouts apply the same rule to the same maxima, so they agree.
+// (Packed workgroups publish t + k, k the tiles' scale headroom, instead of
+// the score t: see scale_headroom.)  Both layouts apply the same rule to the
+// same maxima, so they agree.
 constexpr float kMaxSlack = 8.f;
 __device__ inline float lazy_max(float m, float tile_max) { return tile_max > m + kMaxSlack ? tile_max : m; }
 
@@ -1137,16 +1190,34 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   };
   // the query is converted while the first tile is in flight; slot 2, which
   // holds it, is first filled after the round-0 barrier
+  // The fp16 query operands carry q / sigma (sigma up to 16 for 4-bit and 256
+  // for 2-bit codes), so each head's query is first scaled by a power of two
+  // that puts its largest |q| into [2^14, 2^15): the operands then stay exact
+  // (no subnormals) for any query magnitude.  The waves' group maxima meet in
+  // the (still unused) tile-maxima area.
+  float qscale;
   {
     QueryRows qrows;
     const int n16 = lane & 15, gq = lane >> 4;
+    uint32_t big = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) qrows.lat[u] = lds_ld<u32x4>(qraw + wave * 4096 + n16 * 256 + 64 * gq + 16 * u);
-    publish_query<BITS, true, false>(qrows, qops, nullptr, wave, lane);
+    for (int u = 0; u < 4; ++u) {
+      qrows.lat[u] = lds_ld<u32x4>(qraw + wave * 4096 + n16 * 256 + 64 * gq + 16 * u);
+      big = max(big, bf16_absmax8(qrows.lat[u]));
+    }
+    const float gmax = row_allmax(bf16f(big));
+    if (gq == 0) smax[n16 * kWaves + wave] = gmax;
+    lds_barrier();  // every group's maximum is in
+    const f32x4 mv = lds_ld<f32x4>(reinterpret_cast<const uint8_t*>(smax + n16 * kWaves));
+    qscale = pow2_to_binade(fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])), 15);
+    publish_query<BITS, true, false>(qrows, qops, nullptr, wave, lane, qscale);
   }
   lds_barrier();  // query converted
   QueryOps<BITS> q;
   load_query<BITS>(q, qops, lane);
+  ScoreMul km;
+  km.lat = kCodeScale / qscale;
+  km.meta = q.meta_mul;
 
   float m_run = kNegInf;
   RopeOps ro;
@@ -1173,9 +1244,11 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     score_mfma<BITS>(acc, si, q, ro);
     float sc[4];
     u32x4 md[4];
-    score_finish<BITS>(sc, md, acc, slot, ro.bias, has, (t_lo + it) * kTile, sr.lo_p, sr.hi_p, gq, p.c_log2);
+    km.rope = ro.mul;
+    score_finish<BITS>(sc, md, acc, slot, ro.bias, km, has, (t_lo + it) * kTile, sr.lo_p, sr.hi_p, gq,
+                       p.c_log2);
     if (r == 0 && it + 1 < my_end) issue(it + 1, uniform(id_1), 1);
-    const float tmax = row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float tmax = row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) + scale_headroom(md));
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
 
@@ -1457,14 +1530,11 @@ __global__ void __launch_bounds__((Cmb<CB, SG>::kThreads)) combine_kernel(const 
 // column), which a handful of sequences with hundreds of splits needs.
 template <int CB, int SG>
 int launch_combine(const DecodeParams& p, int64_t groups, int heads, int n_hb, int n_splits, hipStream_t stream) {
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&combine_kernel<CB, SG>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(combine_lds_bytes<CB, SG>(Cmb<CB, SG>::kMaxS))) != hipSuccess)
-      return MLA_LOWBIT_ERR_HIP;
-    attr = true;
-  }
+  static const bool attr_ok =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&combine_kernel<CB, SG>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(combine_lds_bytes<CB, SG>(Cmb<CB, SG>::kMaxS))) == hipSuccess;
+  if (!attr_ok) return MLA_LOWBIT_ERR_HIP;
   using C = Cmb<CB, SG>;
   const dim3 grid(static_cast<uint32_t>(groups * C::kBlocks)), block(C::kThreads);
   const size_t lds = combine_lds_bytes<CB, SG>(n_splits);
@@ -1473,16 +1543,26 @@ int launch_combine(const DecodeParams& p, int64_t groups, int heads, int n_hb, i
   return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
 }
 
-}  // namespace
-}  // namespace mla
+// Sets the decode kernels' dynamic-LDS limits once per process (thread-safe
+// static initialization).
+int set_decode_attributes() {
+  static const int rc = [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<4>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) == hipSuccess &&
+                   hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<2>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) == hipSuccess
+               ? MLA_LOWBIT_OK
+               : MLA_LOWBIT_ERR_HIP;
+  }();
+  return rc;
+}
 
-extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_lat, const void* q_rope,
-                                 int32_t batch, int32_t heads, float softmax_scale, const void* page_pool,
-                                 int32_t num_pool_pages, const int32_t* block_table, int32_t max_pages,
-                                 const int32_t* seqlens, int32_t max_seqlen, const void* sink_buf,
-                                 const void* ring_buf, const void* rope_tail, float* out, float* lse,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  using namespace mla;
+// Validation, work split and launches of the decode entry point.
+int decode_impl(const mla_lowbit_layout* layout, const void* q_lat, const void* q_rope, int32_t batch,
+                int32_t heads, float softmax_scale, const void* page_pool, int32_t num_pool_pages,
+                const int32_t* block_table, int32_t max_pages, const int32_t* seqlens, int32_t max_seqlen,
+                const void* sink_buf, const void* ring_buf, const void* rope_tail, float* out, float* lse,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Geometry g;
   int rc = make_geometry(layout, &g);
   if (rc) return rc;
@@ -1549,15 +1629,7 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
   const int64_t groups = static_cast<int64_t>(batch) * plan.n_hb;
   const int64_t blocks = groups * plan.n_splits;
   if (blocks > 0x7FFFFFFF || groups * 64 > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<4>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<2>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
-      return MLA_LOWBIT_ERR_HIP;
-    attr_set = true;
-  }
+  if ((rc = set_decode_attributes()) != MLA_LOWBIT_OK) return rc;
   if (g.latent_bits == 4)
     hipLaunchKernelGGL(decode_kernel<4>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), kLdsBytes,
                        stream, p);
@@ -1573,4 +1645,18 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
     if (rc) return rc;
   }
   return MLA_LOWBIT_OK;
+}
+
+}  // namespace
+}  // namespace mla
+
+extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_lat, const void* q_rope,
+                                 int32_t batch, int32_t heads, float softmax_scale, const void* page_pool,
+                                 int32_t num_pool_pages, const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* seqlens, int32_t max_seqlen, const void* sink_buf,
+                                 const void* ring_buf, const void* rope_tail, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mla::decode_impl(layout, q_lat, q_rope, batch, heads, softmax_scale, page_pool, num_pool_pages,
+                          block_table, max_pages, seqlens, max_seqlen, sink_buf, ring_buf, rope_tail, out, lse,
+                          workspace, workspace_bytes, stream);
 }

@@ -70,17 +70,24 @@ __device__ inline float f16_to_f32(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-// Largest fp16 <= x: round to nearest, then step one ulp down if it went up.
+// An infinity (a finite input beyond the fp16 range) saturates to the largest
+// finite fp16 of its sign, so the metadata always stays finite.
+__device__ inline uint16_t f16_saturate(uint16_t h) {
+  return (h & 0x7FFFu) == 0x7C00u ? static_cast<uint16_t>((h & 0x8000u) | 0x7BFFu) : h;
+}
+
+// Largest fp16 <= x (-65504 for x below it): round to nearest, then step one
+// ulp down if it went up.
 __device__ inline uint16_t f16_round_down(float x) {
   uint16_t h = f16_bits_rn(x);
   if (f16_to_f32(h) > x) {
     if ((h & 0x7FFFu) == 0) h = 0x8001u;  // zero -> smallest negative subnormal
     else h = (h & 0x8000u) ? h + 1 : h - 1;
   }
-  return h;
+  return f16_saturate(h);
 }
 
-// Smallest fp16 >= x (x >= 0 here; a zero result is +0).
+// Smallest fp16 >= x (x >= 0 here; a zero result is +0; 65504 for x above it).
 __device__ inline uint16_t f16_round_up(float x) {
   uint16_t h = f16_bits_rn(x);
   if (f16_to_f32(h) < x) {
@@ -88,7 +95,7 @@ __device__ inline uint16_t f16_round_up(float x) {
     else h = (h & 0x8000u) ? h - 1 : h + 1;
     if (h == 0x8000u) h = 0;
   }
-  return h;
+  return f16_saturate(h);
 }
 
 // rint of the correctly rounded quotient d / s (d >= 0, s > 0, the quotient

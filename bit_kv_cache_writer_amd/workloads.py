@@ -98,14 +98,17 @@ def _rng(seed: int, stream: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream])))
 
 
-def seq_tokens(w: Workload, b: int, n: int | None = None, start: int = 0):
-    """Tokens [start, start+n) of sequence b: (c_kv, k_r) as bf16 bit arrays."""
+def seq_tokens(w: Workload, b: int, n: int | None = None, start: int = 0, latent_mult: float = 1.0):
+    """Tokens [start, start+n) of sequence b: (c_kv, k_r) as bf16 bit arrays
+    (the latent drawn N(0, latent_mult^2) when latent_mult != 1)."""
     n = w.seqlen if n is None else n
     rng = _rng(w.seed, b)
     if start:
         rng.standard_normal((start, w.latent_dim + w.rope_dim), dtype=np.float32)
     x = rng.standard_normal((n, w.latent_dim + w.rope_dim), dtype=np.float32)
     ckv = x[:, : w.latent_dim]
+    if latent_mult != 1.0:
+        ckv = ckv * np.float32(latent_mult)
     kr = x[:, w.latent_dim:].copy()
     if w.outlier_channels:
         kr[:, list(w.outlier_channels)] *= np.float32(w.outlier_mult)

@@ -112,6 +112,9 @@ int mla_lowbit_layout_query(const mla_lowbit_layout* layout, mla_lowbit_sizes* s
  *     (FP16 scale/min per channel and page) and packed.
  * Codes, metadata and the BF16 copies equal, bit for bit, those of appending
  * the same tokens one at a time.  `seqlens_before` is not modified.
+ * Inputs must be finite bf16.  The FP16 minimum is rounded toward -inf and
+ * the scale toward +inf, each saturating at +-65504; mla_lowbit_decode
+ * further requires |x| <= 65280 (the largest bf16 below the fp16 limit).
  *
  *   c_kv           bf16 [total_new][512], 16-B aligned
  *   k_r            bf16 [total_new][64],  16-B aligned
@@ -180,8 +183,13 @@ int mla_lowbit_decode_workspace(const mla_lowbit_layout* layout, int32_t batch, 
  *                  and the merge kernel of one call; calls that share a
  *                  workspace must not run concurrently).  May be NULL when
  *                  the query returns 0 (one split per sequence).
- * Queries are converted to fp16 inside the kernel: |q| must be below 65504
- * (values under 2^-14 in magnitude keep an absolute accuracy of 2^-25).
+ * Value range.  Queries and cached values must be finite with |x| <= 65280
+ * (the largest bf16 below the fp16 limit): queries, BF16 rows and split
+ * partials are carried as fp16.  Within that range the packed tokens'
+ * scores and weights are exact-product MFMA sums scaled into fp16 range per
+ * head, per page and per tile (no overflow at any magnitude).  BF16-path
+ * values (sink, window) and queries of magnitude below 2^-14 keep an
+ * absolute accuracy of 2^-25 rather than a relative one.
  */
 int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_lat, const void* q_rope,
                       int32_t batch, int32_t heads, float softmax_scale, const void* page_pool,

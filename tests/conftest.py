@@ -25,3 +25,18 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Worst decode errors per parity case (relative row error against the
+    2e-3 bar, absolute lse difference), printed even with -q."""
+    try:
+        from harness import PARITY_LOG
+    except Exception:
+        return
+    if not PARITY_LOG:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "decode parity margins (bar: row rel err <= 2e-3, |d lse| <= 2e-3)")
+    for case, rel, dl, rows in PARITY_LOG:
+        tr.write_line(f"{case:<44s} rows {rows:6d}  worst rel {rel:.2e}  worst |d lse| {dl:.2e}")

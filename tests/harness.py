@@ -10,12 +10,30 @@ import numpy as np
 from bit_kv_cache_writer_amd import workloads as wl
 
 TOL_REL = 2e-3   # per (sequence, head) row: max |o - r| / max |r|
-TOL_LSE = 2e-3   # absolute, natural-log units
+TOL_LSE = 2e-3   # absolute, natural-log units, plus the fp32 slack below
+# An fp32 dot product of n terms carries rounding errors that scale with
+# u * sum_i |a_i b_i| (u = 2^-24; the classical bound is n u sum |a_i b_i|),
+# not with the size of the result, and the lse of a peaked softmax is the top
+# score itself.  So the lse bar adds 2^-17 = 128 u times the score's L1 size
+# S = scale * max_j sum_c |q_c x_jc| (x the oracle's dequantized tokens): at
+# unit-scale inputs this is ~2e-4, at latents scaled by 10^3 it is what any
+# fp32 score computation needs.  The output bar (TOL_REL) is unchanged.
+LSE_FP32_FRACTION = 2.0 ** -17
 
 
 def say(*a):
     print("[case]", *a, flush=True)
     sys.stdout.flush()
+
+
+# worst errors of every decode comparison of the session, printed in the
+# terminal summary (tests/conftest.py) so that the margin to the 2e-3 bar
+# shows even in a quiet run
+PARITY_LOG: list = []
+
+
+def record(case: str, worst_rel: float, worst_lse: float, rows: int) -> None:
+    PARITY_LOG.append((case, worst_rel, worst_lse, rows))
 
 
 def layouts(P, bits, clip, sink, local):
@@ -45,6 +63,20 @@ class OracleCache:
     def decode(self, ql, qr, scale):
         return self.orc.decode(self.lay, np.ascontiguousarray(ql), np.ascontiguousarray(qr), scale,
                                self.pool, self.bt, self.len.copy(), self.sink, self.ring, self.tail)
+
+    def lse_slack(self, ql, qr, scale, chunk=8192):
+        """LSE_FP32_FRACTION * scale * max_j sum_c |q_c x_jc| per (sequence, head),
+        x_j the oracle's dequantized tokens (as its decode reads them)."""
+        B, H, _ = ql.shape
+        q = np.abs(np.concatenate([wl.bf16_bits_to_f32(ql), wl.bf16_bits_to_f32(qr)], axis=2)).astype(np.float64)
+        S = np.zeros((B, H))
+        for b in range(B):
+            L = int(self.len[b])
+            for j0 in range(0, L, chunk):
+                X = np.stack([self.orc.read_token(self.lay, self.pool, self.bt, self.sink, self.ring, self.tail,
+                                                  b, L, j)[0] for j in range(j0, min(L, j0 + chunk))])
+                S[b] = np.maximum(S[b], (np.abs(X) @ q[b].T).max(axis=0))
+        return LSE_FP32_FRACTION * abs(scale) * S
 
 
 def compare_cache(gpu, ref: OracleCache, seqs=None):
@@ -86,10 +118,15 @@ def compare_cache(gpu, ref: OracleCache, seqs=None):
         np.testing.assert_array_equal(tail[b, :nt], ref.tail[b, :nt], err_msg=f"seq {b} k_R tail rows")
 
 
-def compare_decode(out, lse, ref_out, ref_lse, heads=None, seqs=None):
+def compare_decode(out, lse, ref_out, ref_lse, heads=None, seqs=None, case=None, lse_slack=None):
+    """Per (sequence, head) row: max |o - r| / max |r| <= TOL_REL and
+    |lse - lse_ref| <= TOL_LSE + lse_slack (OracleCache.lse_slack); outputs
+    must be finite.  Returns the worst row error; with `case`, the worst
+    errors are recorded for the summary."""
     out = np.asarray(out, np.float64)
     lse = np.asarray(lse, np.float64)
-    worst = 0.0
+    assert np.all(np.isfinite(out)), "non-finite decode output"
+    worst, worst_lse, rows = 0.0, 0.0, 0
     seqs = range(ref_out.shape[0]) if seqs is None else seqs
     for bi, b in enumerate(seqs):
         for hi in range(ref_out.shape[1]):
@@ -102,9 +139,14 @@ def compare_decode(out, lse, ref_out, ref_lse, heads=None, seqs=None):
                 continue
             err = np.abs(o - r).max() / denom
             worst = max(worst, err)
+            rows += 1
             assert err <= TOL_REL, f"seq {b} head {hi}: max rel err {err:.3e} > {TOL_REL}"
             d = abs(lse[bi, hi] - ref_lse[bi, hi])
-            assert d <= TOL_LSE, f"seq {b} head {hi}: lse diff {d:.3e}"
+            worst_lse = max(worst_lse, d)
+            bar = TOL_LSE + (0.0 if lse_slack is None else float(lse_slack[bi, hi]))
+            assert d <= bar, f"seq {b} head {hi}: lse diff {d:.3e} > {bar:.3e}"
+    if case is not None:
+        record(case, worst, worst_lse, rows)
     return worst
 
 

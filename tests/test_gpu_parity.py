@@ -93,7 +93,8 @@ def test_write_and_decode_parity(torch_cuda, case):
     out, lse = gpu.decode(_to_dev(torch, ql), _to_dev(torch, qr), scale)
     torch.cuda.synchronize()
     r_out, r_lse = ref.decode(ql, qr, scale)
-    worst = compare_decode(out.cpu().numpy(), lse.cpu().numpy(), r_out, r_lse)
+    worst = compare_decode(out.cpu().numpy(), lse.cpu().numpy(), r_out, r_lse, case=name,
+                           lse_slack=ref.lse_slack(ql, qr, scale))
     say(name, f"worst row rel err {worst:.2e}")
 
 
@@ -139,7 +140,8 @@ def test_transformed_writer_parity(torch_cuda, case):
     out, lse = gpu.decode(_to_dev(torch, ql), _to_dev(torch, qr), scale)
     torch.cuda.synchronize()
     r_out, r_lse = ref.decode(ql, qr, scale)
-    worst = compare_decode(out.cpu().numpy(), lse.cpu().numpy(), r_out, r_lse)
+    worst = compare_decode(out.cpu().numpy(), lse.cpu().numpy(), r_out, r_lse, case=name,
+                           lse_slack=ref.lse_slack(ql, qr, scale))
     say(name, f"worst row rel err {worst:.2e}")
 
 
@@ -198,24 +200,20 @@ def test_decode_edge_inputs(torch_cuda):
         out, lse = gpu.decode(_to_dev(torch, ql), _to_dev(torch, qr), 0.07)
         torch.cuda.synchronize()
         r_out, r_lse = ref.decode(ql, qr, 0.07)
-        compare_decode(out.cpu().numpy(), lse.cpu().numpy(), r_out, r_lse)
+        compare_decode(out.cpu().numpy(), lse.cpu().numpy(), r_out, r_lse, case=f"edge_inputs_c{bits}r4",
+                       lse_slack=ref.lse_slack(ql, qr, 0.07))
 
 
 # --------------------------------------------------------------------------
 # the configurations at their full sizes, in the launch configuration the
 # benchmark times; sampled sequences (and, for the many-head ones, a subset
-# of heads) are recomputed by the oracle one by one
-
-FULL = [("tiny_c4r4", [0], None), ("c4r4_h16_b8", [0, 7], None), ("c4r4_h16_b32", [5, 31], None),
-        ("c2r4_h20", [3], None), ("c4r4_h128", [17], [0, 1, 64, 127]),
-        ("c2r4_h64_long", [2], [0, 33, 63])]
+# of heads) are decoded by the oracle one by one, and the cache bytes of the
+# sampled sequences (of every sequence where cache_all) are compared
 
 
-@pytest.mark.parametrize("wname,seqs,heads_sub", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled(torch_cuda, wname, seqs, heads_sub):
-    torch = torch_cuda
+def _full_size(torch, w, decode_seqs, heads_sub, cache_all=False, latent_mult=1.0, tag=""):
     from bit_kv_cache_writer_amd import mla
-    w = wl.WORKLOADS[wname]
+    name = w.name + tag
     glay, olay = layouts(w.page_size, w.latent_bits, w.clip_q, w.sink, w.local)
     max_pages = w.pages_per_seq()
     bt, n_pool = wl.block_table(w, max_pages)
@@ -223,39 +221,80 @@ def test_full_size_sampled(torch_cuda, wname, seqs, heads_sub):
     n = w.seqlen
     ckv_d = torch.empty((w.batch * n, 512), dtype=torch.int16, device="cuda")
     kr_d = torch.empty((w.batch * n, 64), dtype=torch.int16, device="cuda")
-    say(wname, "generate inputs", w.batch, "x", n)
+    say(name, "generate inputs", w.batch, "x", n, "latent x", latent_mult)
     for b in range(w.batch):
-        c, k = wl.seq_tokens(w, b)
+        c, k = wl.seq_tokens(w, b, latent_mult=latent_mult)
         ckv_d[b * n:(b + 1) * n] = _to_dev(torch, c)
         kr_d[b * n:(b + 1) * n] = _to_dev(torch, k)
-    say(wname, "GPU bulk write")
+    say(name, "GPU bulk write")
     gpu.append(ckv_d, kr_d, [n] * w.batch)
     del ckv_d, kr_d
     ql, qr = wl.queries(w)
-    say(wname, "GPU decode")
+    say(name, "GPU decode")
     out, lse = gpu.decode(_to_dev(torch, ql), _to_dev(torch, qr), w.softmax_scale)
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    if cache_all:  # every sequence's bytes, from one oracle append of the whole batch
+        say(name, "oracle cache of all", w.batch, "sequences")
+        ref = OracleCache(olay, w.batch, max_pages, bt, n_pool)
+        toks = [wl.seq_tokens(w, b, latent_mult=latent_mult) for b in range(w.batch)]
+        ref.append(np.concatenate([t[0] for t in toks]), np.concatenate([t[1] for t in toks]), [n] * w.batch)
+        del toks
+        compare_cache(gpu, ref)
+        del ref
     pool = gpu.pool.cpu().numpy()
     ring, sink, tail = (gpu.ring.cpu().numpy().view(np.uint16), gpu.sink.cpu().numpy().view(np.uint16),
                         gpu.tail.cpu().numpy().view(np.uint16))
     hs = list(range(w.heads)) if heads_sub is None else heads_sub
-    for b in seqs:
-        say(wname, "oracle sequence", b)
+    for b in decode_seqs:
+        say(name, "oracle sequence", b)
         ref = OracleCache(olay, 1, max_pages, bt[b:b + 1], n_pool)
-        c, k = wl.seq_tokens(w, b)
+        c, k = wl.seq_tokens(w, b, latent_mult=latent_mult)
         ref.append(c, k, [n])
 
         class View:  # the GPU cache restricted to sequence b
             pass
         v = View()
-        import torch as _t
-        v.pool = _t.from_numpy(pool)
-        v.sink = _t.from_numpy(sink[b:b + 1].view(np.int16))
-        v.ring = _t.from_numpy(ring[b:b + 1].view(np.int16))
-        v.tail = _t.from_numpy(tail[b:b + 1].view(np.int16))
+        v.pool = torch.from_numpy(pool)
+        v.sink = torch.from_numpy(sink[b:b + 1].view(np.int16))
+        v.ring = torch.from_numpy(ring[b:b + 1].view(np.int16))
+        v.tail = torch.from_numpy(tail[b:b + 1].view(np.int16))
         compare_cache(v, ref)
-        r_out, r_lse = ref.decode(np.ascontiguousarray(ql[b:b + 1, hs]), np.ascontiguousarray(qr[b:b + 1, hs]),
-                                  w.softmax_scale)
-        worst = compare_decode(out[b:b + 1, hs], lse[b:b + 1, hs], r_out, r_lse, seqs=[b])
-        say(wname, f"seq {b} worst row rel err {worst:.2e}")
+        qlb, qrb = np.ascontiguousarray(ql[b:b + 1, hs]), np.ascontiguousarray(qr[b:b + 1, hs])
+        r_out, r_lse = ref.decode(qlb, qrb, w.softmax_scale)
+        worst = compare_decode(out[b:b + 1, hs], lse[b:b + 1, hs], r_out, r_lse, seqs=[b],
+                               case=f"{name} seq {b}", lse_slack=ref.lse_slack(qlb, qrb, w.softmax_scale))
+        say(name, f"seq {b} worst row rel err {worst:.2e}")
+
+
+FULL = [("tiny_c4r4", [0], None, True), ("c4r4_h16_b8", [0, 7], None, False),
+        ("c4r4_h16_b32", [5, 31], None, True), ("c2r4_h20", [3], None, True),
+        ("c4r4_h128", [17], [0, 1, 64, 127], False), ("c2r4_h64_long", [2], [0, 33, 63], False)]
+
+
+@pytest.mark.parametrize("wname,seqs,heads_sub,cache_all", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(torch_cuda, wname, seqs, heads_sub, cache_all):
+    _full_size(torch_cuda, wl.WORKLOADS[wname], seqs, heads_sub, cache_all=cache_all)
+
+
+# Large latent magnitudes in the same launch configurations: C2R4 latents
+# x300 and x3000 (clip on, and a clip-free variant) and C4R4 latents x1500
+# (group spans of several thousand, so fp16 weights p s_g would pass the fp16
+# range without the scale headroom of the running max).
+LARGE = [("c2r4_h20", 300.0, None, [3, 12], [0, 7, 19]),
+         ("c2r4_h20", 3000.0, None, [5], [0, 11, 19]),
+         ("c2r4_h64_long", 3000.0, 0.0, [1], [0, 40, 63]),
+         ("c4r4_h16_b32", 1500.0, None, [0, 17], None),
+         ("c4r4_h128", 1500.0, None, [9], [0, 77, 127])]
+
+
+@pytest.mark.parametrize("wname,mult,clip,seqs,heads_sub", LARGE,
+                         ids=[f"{w}_x{int(m)}" + ("_noclip" if c == 0.0 else "") for w, m, c, _, _ in LARGE])
+def test_large_latents(torch_cuda, wname, mult, clip, seqs, heads_sub):
+    import dataclasses
+    w = wl.WORKLOADS[wname]
+    tag = f"_x{int(mult)}"
+    if clip is not None:
+        w = dataclasses.replace(w, clip_q=clip)
+        tag += "_noclip"
+    _full_size(torch_cuda, w, seqs, heads_sub, latent_mult=mult, tag=tag)
