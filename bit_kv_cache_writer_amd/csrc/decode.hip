@@ -53,6 +53,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "decode_plan.h"
 #include "geometry.h"
@@ -1543,6 +1544,30 @@ int launch_combine(const DecodeParams& p, int64_t groups, int heads, int n_hb, i
   return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
 }
 
+// The no-allocation entry point's split partials: one fixed array per GPU
+// (each device holds its own copy at its own address for the life of the
+// process).  Host code never uses this name as an address: it takes the
+// device's address from hipGetSymbolAddress once per device (scratch_of).
+static __device__ __align__(256) uint8_t scratch[MLA_LOWBIT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made on that device; nullptr if the lookup fails.
+void* scratch_of_current_device() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
 // Sets the decode kernels' dynamic-LDS limits once per process (thread-safe
 // static initialization).
 int set_decode_attributes() {
@@ -1557,12 +1582,14 @@ int set_decode_attributes() {
   return rc;
 }
 
-// Validation, work split and launches of the decode entry point.
+// Validation, work split and launches shared by both decode entry points.
+// With noalloc the partials go to the device's fixed scratch array instead of
+// the caller's workspace.
 int decode_impl(const mla_lowbit_layout* layout, const void* q_lat, const void* q_rope, int32_t batch,
                 int32_t heads, float softmax_scale, const void* page_pool, int32_t num_pool_pages,
                 const int32_t* block_table, int32_t max_pages, const int32_t* seqlens, int32_t max_seqlen,
                 const void* sink_buf, const void* ring_buf, const void* rope_tail, float* out, float* lse,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                void* workspace, size_t workspace_bytes, bool noalloc, hipStream_t stream) {
   Geometry g;
   int rc = make_geometry(layout, &g);
   if (rc) return rc;
@@ -1582,6 +1609,16 @@ int decode_impl(const mla_lowbit_layout* layout, const void* q_lat, const void* 
     return MLA_LOWBIT_ERR_ARG;
   const DecodePlan plan = plan_decode(g, batch, heads, max_seqlen);
   if (!plan.ok) return MLA_LOWBIT_ERR_UNSUPPORTED;
+  if (noalloc) {
+    if (plan.workspace_bytes > MLA_LOWBIT_NOALLOC_SCRATCH_BYTES) return MLA_LOWBIT_ERR_SCRATCH;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (plan.workspace_bytes > 0) {
+      workspace = scratch_of_current_device();
+      if (!workspace) return MLA_LOWBIT_ERR_HIP;
+      workspace_bytes = MLA_LOWBIT_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return MLA_LOWBIT_ERR_WORKSPACE;
   DecodeParams p{};
@@ -1658,5 +1695,16 @@ extern "C" int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return mla::decode_impl(layout, q_lat, q_rope, batch, heads, softmax_scale, page_pool, num_pool_pages,
                           block_table, max_pages, seqlens, max_seqlen, sink_buf, ring_buf, rope_tail, out, lse,
-                          workspace, workspace_bytes, stream);
+                          workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int mla_lowbit_decode_noalloc(const mla_lowbit_layout* layout, const void* q_lat, const void* q_rope,
+                                         int32_t batch, int32_t heads, float softmax_scale, const void* page_pool,
+                                         int32_t num_pool_pages, const int32_t* block_table, int32_t max_pages,
+                                         const int32_t* seqlens, int32_t max_seqlen, const void* sink_buf,
+                                         const void* ring_buf, const void* rope_tail, float* out, float* lse,
+                                         hipStream_t stream) {
+  return mla::decode_impl(layout, q_lat, q_rope, batch, heads, softmax_scale, page_pool, num_pool_pages,
+                          block_table, max_pages, seqlens, max_seqlen, sink_buf, ring_buf, rope_tail, out, lse,
+                          nullptr, 0, true, stream);
 }

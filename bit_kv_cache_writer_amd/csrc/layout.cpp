@@ -83,6 +83,8 @@ extern "C" const char* mla_lowbit_strerror(int code) {
     case MLA_LOWBIT_ERR_UNSUPPORTED: return "valid request the library does not run";
     case MLA_LOWBIT_ERR_WORKSPACE: return "workspace smaller than mla_lowbit_decode_workspace()";
     case MLA_LOWBIT_ERR_HIP: return "HIP kernel launch failed";
+    case MLA_LOWBIT_ERR_SCRATCH:
+      return "shape needs more split-partial memory than MLA_LOWBIT_NOALLOC_SCRATCH_BYTES (use mla_lowbit_decode)";
     default: return "unknown error code";
   }
 }

@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(HERE, "libmla_lowbit.so")
 
 ERRORS = {
     0: "ok", -1: "MLA_LOWBIT_ERR_LAYOUT", -2: "MLA_LOWBIT_ERR_ARG", -3: "MLA_LOWBIT_ERR_UNSUPPORTED",
-    -4: "MLA_LOWBIT_ERR_WORKSPACE", -5: "MLA_LOWBIT_ERR_HIP",
+    -4: "MLA_LOWBIT_ERR_WORKSPACE", -5: "MLA_LOWBIT_ERR_HIP", -6: "MLA_LOWBIT_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_LOWBIT_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("mla_lowbit_layout_query", "mla_lowbit_write", "mla_lowbit_write_transformed",
            "mla_lowbit_decode_workspace",
-           "mla_lowbit_decode", "mla_lowbit_strerror")
+           "mla_lowbit_decode", "mla_lowbit_decode_noalloc", "mla_lowbit_strerror")
 
 
 class MlaError(RuntimeError):
@@ -87,6 +88,9 @@ def lib():
         L.mla_lowbit_decode.restype = ctypes.c_int
         L.mla_lowbit_decode.argtypes = [P, P, P, i32, i32, ctypes.c_float, P, i32, P, i32, P, i32, P, P,
                                         P, P, P, P, ctypes.c_size_t, P]
+        L.mla_lowbit_decode_noalloc.restype = ctypes.c_int
+        L.mla_lowbit_decode_noalloc.argtypes = [P, P, P, i32, i32, ctypes.c_float, P, i32, P, i32, P, i32, P, P,
+                                                P, P, P, P]
         L.mla_lowbit_strerror.restype = ctypes.c_char_p
         L.mla_lowbit_strerror.argtypes = [ctypes.c_int]
         _lib = L
@@ -166,6 +170,16 @@ def mla_lowbit_decode(layout: Layout, q_lat, q_rope, batch: int, heads: int, sof
         _ptr(sink_buf), _ptr(ring_buf), _ptr(rope_tail), _ptr(out), _ptr(lse), _ptr(workspace),
         workspace_bytes, _stream(stream))
     _check(rc, "mla_lowbit_decode")
+
+
+def mla_lowbit_decode_noalloc(layout: Layout, q_lat, q_rope, batch: int, heads: int, softmax_scale: float,
+                              page_pool, num_pool_pages: int, block_table, max_pages: int, seqlens,
+                              max_seqlen: int, sink_buf, ring_buf, rope_tail, out, lse, stream=None) -> None:
+    rc = lib().mla_lowbit_decode_noalloc(
+        ctypes.byref(layout.c()), _ptr(q_lat), _ptr(q_rope), batch, heads, softmax_scale,
+        _ptr(page_pool), num_pool_pages, _ptr(block_table), max_pages, _ptr(seqlens), max_seqlen,
+        _ptr(sink_buf), _ptr(ring_buf), _ptr(rope_tail), _ptr(out), _ptr(lse), _stream(stream))
+    _check(rc, "mla_lowbit_decode_noalloc")
 
 
 class DeviceCache:

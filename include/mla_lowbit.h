@@ -47,6 +47,7 @@ extern "C" {
 #define MLA_LOWBIT_ERR_UNSUPPORTED (-3) /* valid request the library does not run */
 #define MLA_LOWBIT_ERR_WORKSPACE (-4)   /* workspace smaller than required */
 #define MLA_LOWBIT_ERR_HIP (-5)         /* a HIP launch failed */
+#define MLA_LOWBIT_ERR_SCRATCH (-6)     /* shape needs more than the fixed no-allocation scratch */
 
 /*
  * Cache-layout descriptor (RAQ-MLA appendix Table 5: bits, grouping,
@@ -197,6 +198,31 @@ int mla_lowbit_decode(const mla_lowbit_layout* layout, const void* q_lat, const 
                       const int32_t* seqlens, int32_t max_seqlen, const void* sink_buf,
                       const void* ring_buf, const void* rope_tail, float* out, float* lse,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mla_lowbit_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid hipMalloc).
+ * Arguments, results and errors are those of mla_lowbit_decode without the
+ * workspace: the per-split partials go to a fixed device array inside the
+ * library, MLA_LOWBIT_NOALLOC_SCRATCH_BYTES long, of which every GPU the
+ * library runs on holds its own copy until the process ends (its address is
+ * looked up on the first call made on a device, with that device current).
+ * The call allocates, frees and synchronizes nothing.
+ *   - A shape whose mla_lowbit_decode_workspace() exceeds the scratch size
+ *     returns MLA_LOWBIT_ERR_SCRATCH and launches nothing.
+ *   - All calls on one GPU share its array and it keeps the last call's
+ *     contents (nothing in it needs to start at zero): calls that may overlap
+ *     on one GPU (different streams, or different threads without ordering)
+ *     race; calls enqueued on one stream are ordered and safe.
+ *   - The calling thread's current device must be the device of `stream`.
+ */
+#define MLA_LOWBIT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int mla_lowbit_decode_noalloc(const mla_lowbit_layout* layout, const void* q_lat, const void* q_rope,
+                              int32_t batch, int32_t heads, float softmax_scale, const void* page_pool,
+                              int32_t num_pool_pages, const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seqlens, int32_t max_seqlen, const void* sink_buf,
+                              const void* ring_buf, const void* rope_tail, float* out, float* lse,
+                              hipStream_t stream);
 
 /* Static description of an error code. */
 const char* mla_lowbit_strerror(int code);

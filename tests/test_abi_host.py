@@ -144,6 +144,34 @@ def test_decode_rejects_bad_arguments_without_launch():
     assert _decode(mla.Layout(64, 3, 0.0, 4, 32)) == -1
 
 
+def _decode_noalloc(lay, **kw):
+    a = dict(q_lat=256, q_rope=256, batch=1, heads=16, scale=0.07, pool=256, num_pool_pages=4,
+             block_table=256, max_pages=4, seqlens=256, max_seqlen=100, sink=256, ring=256, tail=256,
+             out=256, lse=256)
+    a.update(kw)
+    L = mla.lib()
+    return L.mla_lowbit_decode_noalloc(ctypes.byref(lay.c()), a["q_lat"], a["q_rope"], a["batch"], a["heads"],
+                                       a["scale"], a["pool"], a["num_pool_pages"], a["block_table"],
+                                       a["max_pages"], a["seqlens"], a["max_seqlen"], a["sink"], a["ring"],
+                                       a["tail"], a["out"], a["lse"], None)
+
+
+def test_decode_noalloc_rejects_without_launch():
+    """Argument errors and shapes whose partials exceed the fixed scratch are
+    refused on the host, before any HIP call."""
+    lay = mla.Layout(64, 4, 0.0, 4, 128)
+    assert _decode_noalloc(lay, q_lat=None) == -2
+    assert _decode_noalloc(lay, heads=0) == -2
+    assert _decode_noalloc(lay, batch=0) == 0
+    assert _decode_noalloc(mla.Layout(64, 3, 0.0, 4, 32)) == -1
+    # 512 sequences x 32768 tokens x 128 heads: the split partials need far
+    # more than the scratch array
+    need = mla.mla_lowbit_decode_workspace(lay, 512, 128, 32768)
+    assert need > mla.NOALLOC_SCRATCH_BYTES
+    assert _decode_noalloc(lay, batch=512, heads=128, max_seqlen=32768, max_pages=512, num_pool_pages=512 * 512) == -6
+    assert "NOALLOC" in mla.strerror(-6)
+
+
 def test_strerror():
-    for c in (0, -1, -2, -3, -4, -5, 99):
+    for c in (0, -1, -2, -3, -4, -5, -6, 99):
         assert isinstance(mla.strerror(c), str) and mla.strerror(c)
