@@ -13,8 +13,12 @@ and the whole step are reported beside it.
 `--calibrate-copy` instead times a plain 1 GiB device copy (the reference
 kernel for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes).
 
-Workload: C4R4 decode, 16 heads, latent 512 + rope 64, batch 32 x 4096 cached
-tokens, page 128, sink 4 + local 128 in BF16 (synthetic, seeded inputs).
+Workload (the headline; the largest configuration): C4R4 decode, 128 heads,
+latent 512 + rope 64, batch 64 x 32768 cached tokens, page 64, sink 4 + local
+128 in BF16 (synthetic, seeded inputs); 64 new tokens per step.  The same run
+also times every other workload (inputs drawn on the GPU, same
+distributions) into the line's "configs" table, and measures the HBM read,
+device copy and fp16 matrix-core rates the GPU sustains ("probes").
 
 Prints one JSON line.  Run on one GPU: python bench.py [--steps K] [--warmup W]
 """
@@ -432,14 +436,211 @@ def transform_cost(steps: int) -> int:
     return 0
 
 
+def probes() -> dict:
+    """Measured peaks beside the published ones: a 4 GiB read stream and the
+    fp16 matrix-core probe (include/mla_lowbit_probe.h), and a plain 1 GiB
+    device copy (read + write)."""
+    import torch
+
+    from bit_kv_cache_writer_amd import mla
+
+    stream = torch.cuda.current_stream()
+    n = 4 << 30
+    src = torch.ones(n // 2, dtype=torch.int16, device="cuda")
+    sink_u = torch.empty(mla.PROBE_BLOCKS * 256, dtype=torch.int32, device="cuda")
+    sink_f = torch.empty(mla.PROBE_BLOCKS * 256, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    t_read = timed(lambda: mla.mla_lowbit_probe_read(src, n, sink_u, stream), 5)
+    flops = [0.0]
+
+    def mf():
+        flops[0] = mla.mla_lowbit_probe_mfma(sink_f, 10000, stream)
+    t_mfma = timed(mf, 3)
+    del src
+    cp_src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    cp_dst = torch.empty_like(cp_src)
+    t_copy = timed(lambda: cp_dst.copy_(cp_src), 5)
+    del cp_src, cp_dst
+    torch.cuda.empty_cache()
+    return {"hbm_read_probe_gbs": round(n / t_read / 1e9, 1),
+            "hbm_copy_probe_gbs": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "mfma_f16_probe_tflops": round(flops[0] / t_mfma / 1e12, 1),
+            "spec_hbm_gbs": HBM_PEAK_GBS, "spec_mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS,
+            "what": "read: 4 GiB streamed once with 16-B loads; copy: 1 GiB device copy, read + write bytes; "
+                    "mfma: 8 independent v_mfma_f32_32x32x16_f16 chains per wave, 2048 x 4 waves"}
+
+
+def make_inputs(w, n, source: str):
+    """Device inputs of a workload: N-1 cached tokens per sequence and the
+    incoming token.  source 'numpy': the seeded per-sequence generator the
+    tests and the oracle use; 'gpu': the same distributions drawn on the GPU
+    (timing only)."""
+    import torch
+
+    from bit_kv_cache_writer_amd import workloads as wl
+
+    B = w.batch
+    if source == "numpy":
+        ckv = torch.empty((B * (n - 1), 512), dtype=torch.int16, device="cuda")
+        kr = torch.empty((B * (n - 1), 64), dtype=torch.int16, device="cuda")
+        new_ckv = torch.empty((B, 512), dtype=torch.int16, device="cuda")
+        new_kr = torch.empty((B, 64), dtype=torch.int16, device="cuda")
+        for b in range(B):
+            c, k = wl.seq_tokens(w, b)
+            ckv[b * (n - 1):(b + 1) * (n - 1)] = torch.from_numpy(c[: n - 1].view(np.int16))
+            kr[b * (n - 1):(b + 1) * (n - 1)] = torch.from_numpy(k[: n - 1].view(np.int16))
+            new_ckv[b] = torch.from_numpy(c[n - 1].view(np.int16))
+            new_kr[b] = torch.from_numpy(k[n - 1].view(np.int16))
+        ql, qr = wl.queries(w)
+        return ckv, kr, new_ckv, new_kr, torch.from_numpy(ql.view(np.int16)).cuda(), \
+            torch.from_numpy(qr.view(np.int16)).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    outl = torch.ones(64, device="cuda")
+    outl[list(w.outlier_channels)] = w.outlier_mult
+
+    def rows(m, width, mult=None):
+        out = torch.empty((m, width), dtype=torch.int16, device="cuda")
+        for a in range(0, m, 1 << 20):
+            e = min(m, a + (1 << 20))
+            x = torch.randn((e - a, width), generator=gen, device="cuda", dtype=torch.float32)
+            if mult is not None:
+                x *= mult
+            out[a:e] = x.to(torch.bfloat16).view(torch.int16)
+        return out
+
+    return (rows(B * (n - 1), 512), rows(B * (n - 1), 64, outl), rows(B, 512), rows(B, 64, outl),
+            rows(B * w.heads, 512).view(B, w.heads, 512).contiguous(),
+            rows(B * w.heads, 64).view(B, w.heads, 64).contiguous())
+
+
+def measure(w, steps: int, warmup: int, layers: int = 0, source: str = "numpy", max_layers: int = 4096) -> dict:
+    """Times `steps` steps over `layers` distinct layer caches (enough for
+    >= 1 GB of packed pages unless given): per layer the writer appends the
+    incoming token of every sequence (completing a page) and the decode attends
+    over the N cached tokens; HIP events on the launch stream around every
+    decode call."""
+    import torch
+
+    from bit_kv_cache_writer_amd import mla
+    from bit_kv_cache_writer_amd import workloads as wl
+
+    lay = mla.Layout(w.page_size, w.latent_bits, w.clip_q, w.sink, w.local)
+    n = w.seqlen
+    max_pages = w.pages_per_seq()
+    bt, n_pool = wl.block_table(w, max_pages)
+    page_bytes = mla.mla_lowbit_layout_query(lay)["page_bytes"]
+    packed_layer = w.batch * max_pages * page_bytes
+    layers = layers or min(max_layers, max(2, math.ceil(1.0e9 / packed_layer)))
+    print(f"[bench] {w.name}: {layers} layers x {packed_layer / 1e6:.1f} MB packed ({source} inputs)",
+          file=sys.stderr, flush=True)
+    ckv, kr, new_ckv, new_kr, q_lat, q_rope = make_inputs(w, n, source)
+    caches, fill_ms = [], []
+    for _ in range(layers):
+        cache = mla.DeviceCache(lay, w.batch, max_pages, bt, n_pool)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cache.append(ckv, kr, [n - 1] * w.batch)
+        e1.record()
+        caches.append(cache)
+        if len(fill_ms) < 4:
+            torch.cuda.synchronize()
+            fill_ms.append(e0.elapsed_time(e1))
+    del ckv, kr
+    fill_bytes = w.batch * (n - 1) * 1152 + w.batch * (n - 1) * (512 * w.latent_bits // 8 + 16 + 32)
+    stream = torch.cuda.current_stream()
+    cu_new = torch.arange(w.batch + 1, dtype=torch.int32, device="cuda")
+    before = torch.full((w.batch,), n - 1, dtype=torch.int32, device="cuda")
+    seqlens = torch.full((w.batch,), n, dtype=torch.int32, device="cuda")
+    ws_bytes = mla.mla_lowbit_decode_workspace(lay, w.batch, w.heads, n)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
+
+    def layer_step(c, ev=None):
+        mla.mla_lowbit_write(lay, new_ckv, new_kr, cu_new, before, w.batch, w.batch, 1, c.block_table,
+                             max_pages, n_pool, c.pool, c.sink, c.ring, c.tail, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_lowbit_decode(lay, q_lat, q_rope, w.batch, w.heads, w.softmax_scale, c.pool, n_pool,
+                              c.block_table, max_pages, seqlens, n, c.sink, c.ring, c.tail, out, lse,
+                              ws, ws_bytes, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        for c in caches:
+            layer_step(c)
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in caches] for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(steps):
+        for li, c in enumerate(caches):
+            layer_step(c, evs[s][li])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    dec_ms = np.array([a.elapsed_time(b) for row in evs for a, b in row])
+    del caches
+    torch.cuda.empty_cache()
+    ms_per_step = total_ms / steps
+    us_layer = ms_per_step * 1000.0 / layers
+    dec_us = float(dec_ms.mean() * 1000.0)
+    # the first fill also pays one-time costs (code object load): left out
+    fill = float(np.median(fill_ms[1:] if len(fill_ms) > 1 else fill_ms))
+    return {"layers": layers, "ms_per_step": ms_per_step, "us_layer": us_layer, "dec_us": dec_us,
+            "dec_us_median": float(np.median(dec_ms) * 1000.0),
+            "dec_us_p10": float(np.percentile(dec_ms, 10) * 1000.0),
+            "dec_us_p90": float(np.percentile(dec_ms, 90) * 1000.0),
+            "write_us": us_layer - dec_us, "fill_gbs": fill_bytes / (fill * 1e-3) / 1e9, "wall": wall,
+            "workspace_bytes": ws_bytes}
+
+
+def rates(w, m) -> dict:
+    """Rates of a measured workload against the binding roofline: HBM time of
+    the algorithmic bytes at 8 TB/s vs matrix-core time of the useful flops
+    (2176 per cached token and head) at 2.5 PFLOP/s."""
+    alg = algorithmic_decode_bytes(w, w.seqlen)
+    byts = alg["total"] * w.batch
+    flops = FLOPS_PER_TOKEN_HEAD * w.seqlen * w.heads * w.batch
+    dec_s = m["dec_us"] * 1e-6
+    gbs, tflops = byts / dec_s / 1e9, flops / dec_s / 1e12
+    hbm_bound = byts / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    return {"decode_us": round(m["dec_us"], 3), "decode_us_median": round(m["dec_us_median"], 3),
+            "decode_us_p10": round(m["dec_us_p10"], 3), "decode_us_p90": round(m["dec_us_p90"], 3),
+            "algorithmic_bytes": byts, "flops": flops, "bound": "hbm" if hbm_bound else "mfma",
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "packed_cache_gbs": round(alg["cache"] * w.batch / dec_s / 1e9, 1),
+            "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "write_us": round(m["write_us"], 3), "new_tokens_per_step": w.batch,
+            "writer_bulk_fill_gbs": round(m["fill_gbs"], 1), "layers": m["layers"]}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4r4_h16_b32")
+    ap.add_argument("--workload", default="c4r4_h128")
     ap.add_argument("--layers", type=int, default=0, help="0: enough layers for >= 1 GB of packed cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-table", action="store_true", help="skip the per-workload table and the probes")
     ap.add_argument("--calibrate-copy", action="store_true", help="time a plain 1 GiB copy and exit")
     ap.add_argument("--sweep", action="store_true", help="context sweep 1K..1M at batch 1 and 8 (JSON lines)")
     ap.add_argument("--ragged", action="store_true", help="ragged-batch decode and chunked-prefill writer (JSON lines)")
@@ -479,105 +680,35 @@ def main() -> int:
             return 2
         w = dataclasses.replace(w, name=w.name + "_bf16", sink=0, local=w.seqlen,
                                 description=w.description + "; every token from BF16 (sink 0, window N)")
-    lay = mla.Layout(w.page_size, w.latent_bits, w.clip_q, w.sink, w.local)
-    n = w.seqlen
-    max_pages = w.pages_per_seq()
-    bt, n_pool = wl.block_table(w, max_pages)
-    page_bytes = mla.mla_lowbit_layout_query(lay)["page_bytes"]
-    packed_layer = w.batch * max_pages * page_bytes
-    layers = args.layers or max(2, math.ceil(1.0e9 / packed_layer))
-    print(f"[bench] {w.name}: {layers} layers x {packed_layer / 1e6:.1f} MB packed", file=sys.stderr,
-          flush=True)
 
-    # inputs: N-1 cached tokens per sequence + the incoming token
-    ckv = torch.empty((w.batch * (n - 1), 512), dtype=torch.int16, device="cuda")
-    kr = torch.empty((w.batch * (n - 1), 64), dtype=torch.int16, device="cuda")
-    new_ckv = torch.empty((w.batch, 512), dtype=torch.int16, device="cuda")
-    new_kr = torch.empty((w.batch, 64), dtype=torch.int16, device="cuda")
-    for b in range(w.batch):
-        c, k = wl.seq_tokens(w, b)
-        ckv[b * (n - 1):(b + 1) * (n - 1)] = torch.from_numpy(c[: n - 1].view(np.int16))
-        kr[b * (n - 1):(b + 1) * (n - 1)] = torch.from_numpy(k[: n - 1].view(np.int16))
-        new_ckv[b] = torch.from_numpy(c[n - 1].view(np.int16))
-        new_kr[b] = torch.from_numpy(k[n - 1].view(np.int16))
-    ql, qr = wl.queries(w)
-    q_lat = torch.from_numpy(ql.view(np.int16)).cuda()
-    q_rope = torch.from_numpy(qr.view(np.int16)).cuda()
-
-    caches = []
-    fill_ms = []
-    for _ in range(layers):
-        cache = mla.DeviceCache(lay, w.batch, max_pages, bt, n_pool)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        cache.append(ckv, kr, [n - 1] * w.batch)
-        e1.record()
-        caches.append(cache)
-        torch.cuda.synchronize()
-        fill_ms.append(e0.elapsed_time(e1))
-    del ckv, kr
-    fill_bytes = w.batch * (n - 1) * 1152 + w.batch * (n - 1) * (512 * w.latent_bits // 8 + 16 + 32)
-    stream = torch.cuda.current_stream()
-    cu_new = torch.arange(w.batch + 1, dtype=torch.int32, device="cuda")
-    before = torch.full((w.batch,), n - 1, dtype=torch.int32, device="cuda")
-    seqlens = torch.full((w.batch,), n, dtype=torch.int32, device="cuda")
-    ws_bytes = mla.mla_lowbit_decode_workspace(lay, w.batch, w.heads, n)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
-    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device="cuda")
-    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
-
-    def layer_step(c, ev=None):
-        mla.mla_lowbit_write(lay, new_ckv, new_kr, cu_new, before, w.batch, w.batch, 1, c.block_table,
-                             max_pages, n_pool, c.pool, c.sink, c.ring, c.tail, stream)
-        if ev is not None:
-            ev[0].record(stream)
-        mla.mla_lowbit_decode(lay, q_lat, q_rope, w.batch, w.heads, w.softmax_scale, c.pool, n_pool,
-                              c.block_table, max_pages, seqlens, n, c.sink, c.ring, c.tail, out, lse,
-                              ws, ws_bytes, stream)
-        if ev is not None:
-            ev[1].record(stream)
-
-    for _ in range(args.warmup):
-        for c in caches:
-            layer_step(c)
-    torch.cuda.synchronize()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in caches] for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for s in range(args.steps):
-        for li, c in enumerate(caches):
-            layer_step(c, evs[s][li])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    dec_ms = np.array([a.elapsed_time(b) for row in evs for a, b in row])
-    ms_per_step = total_ms / args.steps
-    us_layer = ms_per_step * 1000.0 / layers
-    dec_us = float(dec_ms.mean() * 1000.0)
-
-    alg = algorithmic_decode_bytes(w, n)
-    dec_bytes = alg["total"] * w.batch
-    achieved = dec_bytes / (dec_us * 1e-6) / 1e9
-    packed_gbs = alg["cache"] * w.batch / (dec_us * 1e-6) / 1e9
-    # the binding roofline: HBM time of the algorithmic bytes vs matrix-core
-    # time of the useful flops (every cached token, every head)
-    dec_flops = FLOPS_PER_TOKEN_HEAD * n * w.heads * w.batch
-    tflops = dec_flops / (dec_us * 1e-6) / 1e12
-    hbm_bound = dec_bytes / (HBM_PEAK_GBS * 1e9) >= dec_flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
-    hbm_roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    mfma_roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+    m = measure(w, args.steps, args.warmup, args.layers, "numpy")
+    head = rates(w, m)
+    dec_us = m["dec_us"]
+    hbm_roof = {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": head["hbm_frac"]}
+    mfma_roof = {"bound": "mfma", "achieved": head["mfma_tflops"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": head["mfma_frac"]}
+    hbm_bound = head["bound"] == "hbm"
     roof = dict(hbm_roof if hbm_bound else mfma_roof)
     roof.update({"traffic": measured_traffic(w.name),
-                 "kernel": "mla_lowbit_decode = decode_kernel + combine_kernel (one call per layer)",
-                 "bytes_per_launch": dec_bytes, "flops_per_launch": dec_flops,
+                 "kernel": "mla_lowbit_decode call (its attention kernels + split merge), events per call",
+                 "bytes_per_launch": head["algorithmic_bytes"], "flops_per_launch": head["flops"],
                  "other": mfma_roof if hbm_bound else hbm_roof})
-    write_us = us_layer - dec_us
+
+    table, prb = None, None
+    if not args.no_table:
+        table = {}
+        for name, wk in wl.WORKLOADS.items():
+            if name == w.name:
+                table[name] = head
+                continue
+            table[name] = rates(wk, measure(wk, max(1, min(args.steps, 5)), 1, 0, "gpu", max_layers=128))
+        prb = probes()
+        roof["measured_peak"] = {"hbm_read_gbs": prb["hbm_read_probe_gbs"],
+                                 "mfma_f16_tflops": prb["mfma_f16_probe_tflops"]}
+        roof["frac_of_measured_peak"] = round(
+            (head["hbm_gbs"] / prb["hbm_read_probe_gbs"]) if hbm_bound else
+            (head["mfma_tflops"] / prb["mfma_f16_probe_tflops"]), 4)
 
     cpu = None
     if not args.no_cpu:
@@ -591,31 +722,32 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(m["ms_per_step"], 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "batch": w.batch, "heads": w.heads,
-                   "cached_tokens": n, "page": w.page_size, "paths": w.paths, "sink": w.sink,
-                   "local": w.local, "layers_per_step": layers,
+                   "cached_tokens": w.seqlen, "page": w.page_size, "paths": w.paths, "sink": w.sink,
+                   "local": w.local, "layers_per_step": m["layers"],
                    "step": "per layer: append 1 token per sequence (completes a page) + decode over N",
                    "value": "decode (attention + split merge) us per layer"},
         "decode_us": round(dec_us, 3),
-        "write_us": round(write_us, 3),
-        "writer_tokens_per_s": round(w.batch / (write_us * 1e-6), 1),
-        "step_us_per_layer": round(us_layer, 3),
-        "packed_cache_gbs": round(packed_gbs, 1),
-        "packed_cache_frac_of_hbm": round(packed_gbs / HBM_PEAK_GBS, 4),
-        # the first fill also pays one-time costs (code object load): left out
-        "writer_bulk_fill_gbs": round(fill_bytes / (np.median(fill_ms[1:] if len(fill_ms) > 1 else fill_ms) * 1e-3)
-                                      / 1e9, 1),
-        "writer_bulk_fill_frac_of_hbm": round(fill_bytes / (np.median(fill_ms[1:] if len(fill_ms) > 1 else fill_ms)
-                                                            * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "wall_s": round(wall, 3),
+        "decode_us_median": head["decode_us_median"],
+        "write_us": round(m["write_us"], 3),
+        "writer_new_tokens_per_step": w.batch,
+        "writer_tokens_per_s": round(w.batch / (m["write_us"] * 1e-6), 1),
+        "step_us_per_layer": round(m["us_layer"], 3),
+        "packed_cache_gbs": head["packed_cache_gbs"],
+        "packed_cache_frac_of_hbm": round(head["packed_cache_gbs"] / HBM_PEAK_GBS, 4),
+        "writer_bulk_fill_gbs": round(m["fill_gbs"], 1),
+        "writer_bulk_fill_frac_of_hbm": round(m["fill_gbs"] / HBM_PEAK_GBS, 4),
+        "wall_s": round(m["wall"], 3),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "probes": prb,
+        "configs": table,
         "context_h20": {"raq_mla_us_per_layer": 12.6, "flashmla_us_per_layer": 17.4,
                         "tpot_ms": [5.97, 6.56]},
     }

@@ -17,8 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_lowbit.so")
-SOURCES = ["layout.cpp", "writer.hip", "decode.hip"]
+SOURCES = ["layout.cpp", "writer.hip", "decode.hip", "probe.hip"]
 ARCH = "gfx950"
+EXTRA: dict = {}  # per-source extra flags
 
 
 def hipcc() -> str:
@@ -39,7 +40,7 @@ def _flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

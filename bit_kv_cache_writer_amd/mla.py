@@ -23,6 +23,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_LOWBIT_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("mla_lowbit_layout_query", "mla_lowbit_write", "mla_lowbit_write_transformed",
            "mla_lowbit_decode_workspace",
            "mla_lowbit_decode", "mla_lowbit_decode_noalloc", "mla_lowbit_strerror")
+PROBE_EXPORTS = ("mla_lowbit_probe_read", "mla_lowbit_probe_mfma")  # include/mla_lowbit_probe.h
+PROBE_BLOCKS = 2048  # MLA_LOWBIT_PROBE_BLOCKS
 
 
 class MlaError(RuntimeError):
@@ -91,6 +93,10 @@ def lib():
         L.mla_lowbit_decode_noalloc.restype = ctypes.c_int
         L.mla_lowbit_decode_noalloc.argtypes = [P, P, P, i32, i32, ctypes.c_float, P, i32, P, i32, P, i32, P, P,
                                                 P, P, P, P]
+        L.mla_lowbit_probe_read.restype = ctypes.c_int
+        L.mla_lowbit_probe_read.argtypes = [P, ctypes.c_size_t, P, P]
+        L.mla_lowbit_probe_mfma.restype = ctypes.c_int
+        L.mla_lowbit_probe_mfma.argtypes = [P, i32, ctypes.POINTER(ctypes.c_double), P]
         L.mla_lowbit_strerror.restype = ctypes.c_char_p
         L.mla_lowbit_strerror.argtypes = [ctypes.c_int]
         _lib = L
@@ -180,6 +186,18 @@ def mla_lowbit_decode_noalloc(layout: Layout, q_lat, q_rope, batch: int, heads: 
         _ptr(page_pool), num_pool_pages, _ptr(block_table), max_pages, _ptr(seqlens), max_seqlen,
         _ptr(sink_buf), _ptr(ring_buf), _ptr(rope_tail), _ptr(out), _ptr(lse), _stream(stream))
     _check(rc, "mla_lowbit_decode_noalloc")
+
+
+def mla_lowbit_probe_read(src, nbytes: int, sink, stream=None) -> None:
+    _check(lib().mla_lowbit_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "mla_lowbit_probe_read")
+
+
+def mla_lowbit_probe_mfma(sink, iters: int, stream=None) -> float:
+    """Launches the matrix-core probe; returns its flop count."""
+    flops = ctypes.c_double()
+    _check(lib().mla_lowbit_probe_mfma(_ptr(sink), iters, ctypes.byref(flops), _stream(stream)),
+           "mla_lowbit_probe_mfma")
+    return flops.value
 
 
 class DeviceCache:

@@ -26,6 +26,21 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_exports_every_probe_symbol():
+    text = open(os.path.join(ROOT, "include", "mla_lowbit_probe.h")).read()
+    names = set(re.findall(r"\b(mla_lowbit_\w+)\s*\(", text))
+    assert names == set(mla.PROBE_EXPORTS)
+    lib = mla.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    # argument errors are found on the host
+    flops = ctypes.c_double()
+    assert lib.mla_lowbit_probe_mfma(None, 10, ctypes.byref(flops), None) == -2
+    assert lib.mla_lowbit_probe_mfma(256, 0, ctypes.byref(flops), None) == -2
+    assert lib.mla_lowbit_probe_read(256, 100, 256, None) == -2   # not a multiple of 64
+    assert lib.mla_lowbit_probe_read(None, 64, 256, None) == -2
+
+
 @pytest.mark.parametrize("P", [32, 64, 128, 256])
 @pytest.mark.parametrize("bits", [2, 4])
 def test_layout_query_matches_oracle(orc, P, bits):
