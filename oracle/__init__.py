@@ -101,6 +101,7 @@ def lib():
         L.oracle_read_token.restype = i32
         L.oracle_read_token.argtypes = [P, P, P, P, P, P, i32, i32, i32, P]
         L.oracle_decode.argtypes = [P, P, P, i32, i32, f64, P, P, i32, P, P, P, P, P, P]
+        L.oracle_decode_bf16.argtypes = [P, P, i32, i32, f64, P, i32, P, i32, P, P, P]
         L.oracle_transform.argtypes = [P, P, i64, i32, P]
         L.oracle_transform.restype = None
         _lib = L
@@ -220,4 +221,34 @@ def decode(layout: Layout, q_lat, q_rope, scale: float, pool, block_table, seqle
     lib().oracle_decode(ctypes.byref(layout.c()), _p(q_lat), _p(q_rope), B, H, scale, _p(pool),
                         _p(block_table), block_table.shape[1], _p(seqlens), _p(sink_buf),
                         _p(ring_buf), _p(tail_buf), _p(out), _p(lse))
+    return out, lse
+
+
+def append_bf16(pool, page_size: int, block_table, seqlens_before, c_kv, k_r, counts):
+    """Plain BF16 paged cache (the baseline of QuantMLA Table 9 caption):
+    sequence b's new rows go, in order, to positions seqlens_before[b] + i,
+    position j at page block_table[b][j // P], slot j % P of pool
+    [pages][P][576] as (c_KV, k_R) bf16 bits.  Writes pool in place."""
+    n = 0
+    for b, cnt in enumerate(counts):
+        for i in range(cnt):
+            j = int(seqlens_before[b]) + i
+            pool[block_table[b][j // page_size], j % page_size, :512] = c_kv[n]
+            pool[block_table[b][j // page_size], j % page_size, 512:] = k_r[n]
+            n += 1
+    return pool
+
+
+def decode_bf16(q_lat, q_rope, scale: float, pool, page_size: int, block_table, seqlens):
+    """fp64 decode over the plain BF16 paged cache; returns (out [B][H][512],
+    lse [B][H])."""
+    B, H, D = q_lat.shape
+    assert D == 512 and q_rope.shape == (B, H, 64) and pool.shape[1:] == (page_size, 576)
+    for a in (q_lat, q_rope, pool, block_table, seqlens):
+        assert a.flags["C_CONTIGUOUS"]
+    assert seqlens.dtype == np.int32 and block_table.dtype == np.int32
+    out = np.zeros((B, H, D), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    lib().oracle_decode_bf16(_p(q_lat), _p(q_rope), B, H, scale, _p(pool), page_size,
+                             _p(block_table), block_table.shape[1], _p(seqlens), _p(out), _p(lse))
     return out, lse

@@ -511,6 +511,58 @@ void oracle_decode(const orc_layout* L, const uint16_t* q_lat,
 }
 
 /* ------------------------------------------------------------------ */
+/* Decode over a plain BF16 paged cache: the baseline the low-bit cache is
+ * measured against (QuantMLA, Table 9 caption: BF16 attention with native
+ * partitioning).  Reading taken: the cache keeps every token's pre-
+ * quantization row (c_KV 512 then k_R 64, bf16) at page
+ * block_table[b][j / P], slot j % P of a pool [pages][P][576]; the attention
+ * is the same as oracle_decode's with every token read from that row:
+ *   z_j = scale * (q_lat . c_j + q_rope . k_j)
+ *   out = sum_j exp(z_j - max z) c_j / sum_j exp(z_j - max z)
+ *   lse = max z + log(sum_j exp(z_j - max z)),  fp64.
+ * Lb = 0 gives out = 0 and lse = -inf. */
+void oracle_decode_bf16(const uint16_t* q_lat, const uint16_t* q_rope, int32_t batch, int32_t heads,
+                        double scale, const uint16_t* pool, int32_t page_size,
+                        const int32_t* block_table, int32_t max_pages, const int32_t* seqlens,
+                        double* out, double* lse) {
+  const int D = 512, R = 64, W = D + R;
+  double* q = (double*)malloc(sizeof(double) * (size_t)W);
+  for (int b = 0; b < batch; ++b) {
+    int Lb = seqlens[b];
+    const int32_t* bt = block_table + (int64_t)b * max_pages;
+    double* z = (double*)malloc(sizeof(double) * (size_t)(Lb > 0 ? Lb : 1));
+    for (int h = 0; h < heads; ++h) {
+      for (int c = 0; c < D; ++c) q[c] = bf16_to_f32(q_lat[((int64_t)b * heads + h) * D + c]);
+      for (int c = 0; c < R; ++c) q[D + c] = bf16_to_f32(q_rope[((int64_t)b * heads + h) * R + c]);
+      double* o = out + ((int64_t)b * heads + h) * D;
+      memset(o, 0, sizeof(double) * D);
+      if (Lb == 0) {
+        lse[(int64_t)b * heads + h] = -INFINITY;
+        continue;
+      }
+      double m = -INFINITY;
+      for (int j = 0; j < Lb; ++j) {
+        const uint16_t* row = pool + ((int64_t)bt[j / page_size] * page_size + j % page_size) * W;
+        double acc = 0.0;
+        for (int c = 0; c < W; ++c) acc += q[c] * bf16_to_f32(row[c]);
+        z[j] = scale * acc;
+        m = fmax(m, z[j]);
+      }
+      double sum = 0.0;
+      for (int j = 0; j < Lb; ++j) sum += exp(z[j] - m);
+      for (int j = 0; j < Lb; ++j) {
+        const uint16_t* row = pool + ((int64_t)bt[j / page_size] * page_size + j % page_size) * W;
+        double p = exp(z[j] - m) / sum;
+        for (int c = 0; c < D; ++c) o[c] += p * bf16_to_f32(row[c]);
+      }
+      lse[(int64_t)b * heads + h] = m + log(sum);
+    }
+    free(z);
+  }
+  free(q);
+}
+
+/* ------------------------------------------------------------------ */
 /* Array helpers for the tests' pins. */
 void oracle_f16_round_down_n(const float* x, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_round_down(x[i]);

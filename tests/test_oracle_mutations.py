@@ -29,6 +29,10 @@ MUTANTS = {
     "page_complete_wrong": ("int page_complete = (int64_t)(pidx + 1) * P <= Lb;",
                             "int page_complete = (int64_t)(pidx + 1) * P < Lb;"),
     "softmax_not_max_subtracted": ("s += exp(z[(int64_t)h * Lb + j] - m);", "s += exp(z[(int64_t)h * Lb + j] - m) * 1.0001;"),
+    "bf16_cache_slot_off_by_one": ("bt[j / page_size] * page_size + j % page_size) * W;\n        double acc",
+                                   "bt[j / page_size] * page_size + (j + 1) % page_size) * W;\n        double acc"),
+    "bf16_cache_rope_dropped": ("for (int c = 0; c < W; ++c) acc += q[c] * bf16_to_f32(row[c]);",
+                                "for (int c = 0; c < D; ++c) acc += q[c] * bf16_to_f32(row[c]);"),
     "transform_ties_away": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))",
                             "if (dropped >= 0x8000u)"),
     "transform_matrix_transposed": ("acc = fmaf(bf16_to_f32(a_c[(int64_t)c * dim + k])",

@@ -492,3 +492,54 @@ def test_transform_within_fp32_bound_of_exact(orc):
     assert np.all(np.abs(y - exact) <= 0.5 * step + 512 * 2.0**-24 * absum)
     # the transform is (nearly) orthogonal: row norms are kept to bf16 accuracy
     assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(xf, axis=1), rtol=2e-2)
+
+
+# ----------------------------------------------------------------------------
+# BF16 paged cache (the baseline of QuantMLA Table 9 caption)
+
+def test_bf16_cache_decode_equals_sdpa(orc):
+    """Ragged sequences through a permuted block table: each sequence's
+    output and lse equal torch attention over its rows in order."""
+    rng = np.random.default_rng(31)
+    P, H = 16, 3
+    lengths = [0, 1, 15, 16, 17, 40]
+    max_pages = (max(lengths) + P - 1) // P
+    n_pool = len(lengths) * max_pages + 3
+    bt = rng.permutation(n_pool)[: len(lengths) * max_pages].astype(np.int32).reshape(len(lengths), max_pages)
+    pool = np.zeros((n_pool, P, 576), np.uint16)
+    ckv = _rand_bf16(rng, (sum(lengths), 512), (3, 300))
+    kr = _rand_bf16(rng, (sum(lengths), 64), (9,))
+    orc.append_bf16(pool, P, bt, np.zeros(len(lengths), np.int32), ckv, kr, lengths)
+    ql, qr = _rand_bf16(rng, (len(lengths), H, 512)), _rand_bf16(rng, (len(lengths), H, 64))
+    out, lse = orc.decode_bf16(ql, qr, 0.06, pool, P, bt, np.asarray(lengths, np.int32))
+    start = 0
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b]))
+            continue
+        toks = wl.bf16_bits_to_f32(np.concatenate([ckv[start:start + L], kr[start:start + L]], -1))
+        ref, rlse = _sdpa(wl.bf16_bits_to_f32(ql[b]), wl.bf16_bits_to_f32(qr[b]), toks.astype(np.float64), 0.06)
+        np.testing.assert_allclose(out[b], ref, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rlse, rtol=1e-12)
+        start += L
+
+
+def test_bf16_cache_single_token_and_appends(orc):
+    """One token: out is its latent row exactly and lse its scaled score.
+    Rows appended in two calls land where one call puts them."""
+    rng = np.random.default_rng(32)
+    P = 32
+    bt = np.array([[4, 1, 7]], np.int32)
+    ckv, kr = _rand_bf16(rng, (70, 512)), _rand_bf16(rng, (70, 64))
+    one = orc.append_bf16(np.zeros((8, P, 576), np.uint16), P, bt, np.zeros(1, np.int32), ckv, kr, [70])
+    two = orc.append_bf16(np.zeros((8, P, 576), np.uint16), P, bt, np.zeros(1, np.int32), ckv[:33], kr[:33], [33])
+    orc.append_bf16(two, P, bt, np.array([33], np.int32), ckv[33:], kr[33:], [37])
+    np.testing.assert_array_equal(one, two)
+    assert np.array_equal(one[7, 69 - 64, :512], ckv[69]) and np.array_equal(one[1, 0, 512:], kr[32])
+    ql, qr = _rand_bf16(rng, (1, 2, 512)), _rand_bf16(rng, (1, 2, 64))
+    out, lse = orc.decode_bf16(ql, qr, 0.1, one, P, bt, np.array([1], np.int32))
+    x = wl.bf16_bits_to_f32(ckv[0]).astype(np.float64)
+    k = wl.bf16_bits_to_f32(kr[0]).astype(np.float64)
+    np.testing.assert_array_equal(out[0], np.broadcast_to(x, (2, 512)))
+    z = 0.1 * (wl.bf16_bits_to_f32(ql[0]).astype(np.float64) @ x + wl.bf16_bits_to_f32(qr[0]).astype(np.float64) @ k)
+    np.testing.assert_allclose(lse[0], z, rtol=1e-13)
