@@ -56,6 +56,7 @@
 #include <mutex>
 
 #include "decode_plan.h"
+#include "mla_bf16.h"
 #include "geometry.h"
 
 namespace mla {
@@ -1544,6 +1545,68 @@ int launch_combine(const DecodeParams& p, int64_t groups, int heads, int n_hb, i
   return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
 }
 
+#include "decode_bf16.h"
+
+// Validation and launches of the BF16-cache entry points.
+int bf16_decode_impl(const void* q_lat, const void* q_rope, int32_t batch, int32_t heads, float softmax_scale,
+                     const void* pool, int32_t num_pool_pages, int32_t page_size, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* seqlens, int32_t max_seqlen, float* out, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (batch < 0 || heads < 1 || heads > kMaxHeads || max_seqlen < 0 || max_pages < 0 || num_pool_pages < 0 ||
+      page_size < 16 || page_size > 1024 || (page_size & (page_size - 1)) || !std::isfinite(softmax_scale))
+    return MLA_LOWBIT_ERR_ARG;
+  if (batch == 0) return MLA_LOWBIT_OK;
+  if (static_cast<int64_t>(max_seqlen) > static_cast<int64_t>(max_pages) * page_size) return MLA_LOWBIT_ERR_ARG;
+  if (!q_lat || !q_rope || !seqlens || !out || !lse) return MLA_LOWBIT_ERR_ARG;
+  if (max_seqlen > 0 && (!pool || !block_table || num_pool_pages == 0)) return MLA_LOWBIT_ERR_ARG;
+  if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(out) || (pool && !aligned16(pool)) ||
+      (workspace && !aligned16(workspace)))
+    return MLA_LOWBIT_ERR_ARG;
+  const bf16c::Plan plan = bf16c::plan(page_size, batch, heads, max_seqlen);
+  if (!plan.ok) return MLA_LOWBIT_ERR_UNSUPPORTED;
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return MLA_LOWBIT_ERR_WORKSPACE;
+  const int64_t groups = static_cast<int64_t>(batch) * plan.n_hb;
+  const int64_t blocks = groups * plan.n_splits;
+  if (blocks > 0x7FFFFFFF || groups * 64 > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
+  static const bool attr_ok =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&bf16c::decode_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bf16c::kLdsBytes) == hipSuccess;
+  if (!attr_ok) return MLA_LOWBIT_ERR_HIP;
+  bf16c::Params p{};
+  p.q_lat = static_cast<const uint16_t*>(q_lat);
+  p.q_rope = static_cast<const uint16_t*>(q_rope);
+  p.pool = static_cast<const uint8_t*>(pool);
+  p.block_table = block_table;
+  p.seqlens = seqlens;
+  p.parts = static_cast<uint8_t*>(workspace);
+  p.out = out;
+  p.lse = lse;
+  p.batch = batch;
+  p.heads = heads;
+  p.max_pages = max_pages;
+  p.num_pool_pages = num_pool_pages;
+  p.n_hb = plan.n_hb;
+  p.n_splits = plan.n_splits;
+  p.per = plan.per;
+  p.log2P = 0;
+  while ((1 << p.log2P) < page_size) ++p.log2P;
+  p.page_bytes = static_cast<int64_t>(page_size) * bf16c::kRowBytes;
+  p.c_log2 = softmax_scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(bf16c::decode_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(bf16c::kThreads),
+                     bf16c::kLdsBytes, stream, p);
+  if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
+  if (plan.n_splits > 1) {
+    DecodeParams cp{};
+    cp.parts = p.parts;
+    cp.out = out;
+    cp.lse = lse;
+    return plan.n_splits <= 32 ? launch_combine<32, 1>(cp, groups, heads, plan.n_hb, plan.n_splits, stream)
+                               : launch_combine<8, 16>(cp, groups, heads, plan.n_hb, plan.n_splits, stream);
+  }
+  return MLA_LOWBIT_OK;
+}
+
 // The no-allocation entry point's split partials: one fixed array per GPU
 // (each device holds its own copy at its own address for the life of the
 // process).  Host code never uses this name as an address: it takes the
@@ -1707,4 +1770,47 @@ extern "C" int mla_lowbit_decode_noalloc(const mla_lowbit_layout* layout, const 
   return mla::decode_impl(layout, q_lat, q_rope, batch, heads, softmax_scale, page_pool, num_pool_pages,
                           block_table, max_pages, seqlens, max_seqlen, sink_buf, ring_buf, rope_tail, out, lse,
                           nullptr, 0, true, stream);
+}
+
+extern "C" int mla_bf16_decode_workspace(int32_t page_size, int32_t batch, int32_t heads, int32_t max_seqlen,
+                                         size_t* bytes) {
+  if (!bytes || batch < 0 || heads < 1 || heads > mla::kMaxHeads || max_seqlen < 0 || page_size < 16 ||
+      page_size > 1024 || (page_size & (page_size - 1)))
+    return MLA_LOWBIT_ERR_ARG;
+  const mla::bf16c::Plan plan = mla::bf16c::plan(page_size, batch, heads, max_seqlen);
+  if (!plan.ok) return MLA_LOWBIT_ERR_UNSUPPORTED;
+  *bytes = batch == 0 ? 0 : plan.workspace_bytes;
+  return MLA_LOWBIT_OK;
+}
+
+extern "C" int mla_bf16_decode(const void* q_lat, const void* q_rope, int32_t batch, int32_t heads,
+                               float softmax_scale, const void* pool, int32_t num_pool_pages, int32_t page_size,
+                               const int32_t* block_table, int32_t max_pages, const int32_t* seqlens,
+                               int32_t max_seqlen, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return mla::bf16_decode_impl(q_lat, q_rope, batch, heads, softmax_scale, pool, num_pool_pages, page_size,
+                               block_table, max_pages, seqlens, max_seqlen, out, lse, workspace, workspace_bytes,
+                               stream);
+}
+
+extern "C" int mla_bf16_append(const void* c_kv, const void* k_r, const int32_t* cu_new,
+                               const int32_t* seqlens_before, int32_t batch, int32_t total_new,
+                               int32_t max_new_per_seq, int32_t page_size, const int32_t* block_table,
+                               int32_t max_pages, int32_t num_pool_pages, void* pool, hipStream_t stream) {
+  if (batch < 0 || total_new < 0 || max_new_per_seq < 0 || max_pages < 0 || num_pool_pages < 0 ||
+      page_size < 16 || page_size > 1024 || (page_size & (page_size - 1)))
+    return MLA_LOWBIT_ERR_ARG;
+  if (batch == 0 || total_new == 0 || max_new_per_seq == 0) return MLA_LOWBIT_OK;
+  if (!c_kv || !k_r || !cu_new || !seqlens_before || !block_table || !pool || max_pages == 0 ||
+      num_pool_pages == 0)
+    return MLA_LOWBIT_ERR_ARG;
+  if (!mla::aligned16(c_kv) || !mla::aligned16(k_r) || !mla::aligned16(pool)) return MLA_LOWBIT_ERR_ARG;
+  int log2P = 0;
+  while ((1 << log2P) < page_size) ++log2P;
+  const dim3 grid(static_cast<uint32_t>((max_new_per_seq + 3) / 4), static_cast<uint32_t>(batch));
+  if (grid.y > 65535u) return MLA_LOWBIT_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(mla::bf16c::append_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(c_kv),
+                     static_cast<const uint16_t*>(k_r), cu_new, seqlens_before, log2P, block_table, max_pages,
+                     num_pool_pages, static_cast<uint16_t*>(pool));
+  return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
 }

@@ -24,6 +24,7 @@ EXPORTS = ("mla_lowbit_layout_query", "mla_lowbit_write", "mla_lowbit_write_tran
            "mla_lowbit_decode_workspace",
            "mla_lowbit_decode", "mla_lowbit_decode_noalloc", "mla_lowbit_strerror")
 PROBE_EXPORTS = ("mla_lowbit_probe_read", "mla_lowbit_probe_mfma")  # include/mla_lowbit_probe.h
+BF16_EXPORTS = ("mla_bf16_append", "mla_bf16_decode_workspace", "mla_bf16_decode")  # include/mla_bf16.h
 PROBE_BLOCKS = 2048  # MLA_LOWBIT_PROBE_BLOCKS
 
 
@@ -97,6 +98,13 @@ def lib():
         L.mla_lowbit_probe_read.argtypes = [P, ctypes.c_size_t, P, P]
         L.mla_lowbit_probe_mfma.restype = ctypes.c_int
         L.mla_lowbit_probe_mfma.argtypes = [P, i32, ctypes.POINTER(ctypes.c_double), P]
+        L.mla_bf16_append.restype = ctypes.c_int
+        L.mla_bf16_append.argtypes = [P, P, P, P, i32, i32, i32, i32, P, i32, i32, P, P]
+        L.mla_bf16_decode_workspace.restype = ctypes.c_int
+        L.mla_bf16_decode_workspace.argtypes = [i32, i32, i32, i32, P]
+        L.mla_bf16_decode.restype = ctypes.c_int
+        L.mla_bf16_decode.argtypes = [P, P, i32, i32, ctypes.c_float, P, i32, i32, P, i32, P, i32, P, P, P,
+                                      ctypes.c_size_t, P]
         L.mla_lowbit_strerror.restype = ctypes.c_char_p
         L.mla_lowbit_strerror.argtypes = [ctypes.c_int]
         _lib = L
@@ -198,6 +206,82 @@ def mla_lowbit_probe_mfma(sink, iters: int, stream=None) -> float:
     _check(lib().mla_lowbit_probe_mfma(_ptr(sink), iters, ctypes.byref(flops), _stream(stream)),
            "mla_lowbit_probe_mfma")
     return flops.value
+
+
+def mla_bf16_append(c_kv, k_r, cu_new, seqlens_before, batch: int, total_new: int, max_new_per_seq: int,
+                    page_size: int, block_table, max_pages: int, num_pool_pages: int, pool, stream=None) -> None:
+    rc = lib().mla_bf16_append(_ptr(c_kv), _ptr(k_r), _ptr(cu_new), _ptr(seqlens_before), batch, total_new,
+                               max_new_per_seq, page_size, _ptr(block_table), max_pages, num_pool_pages,
+                               _ptr(pool), _stream(stream))
+    _check(rc, "mla_bf16_append")
+
+
+def mla_bf16_decode_workspace(page_size: int, batch: int, heads: int, max_seqlen: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mla_bf16_decode_workspace(page_size, batch, heads, max_seqlen, ctypes.byref(n)),
+           "mla_bf16_decode_workspace")
+    return n.value
+
+
+def mla_bf16_decode(q_lat, q_rope, batch: int, heads: int, softmax_scale: float, pool, num_pool_pages: int,
+                    page_size: int, block_table, max_pages: int, seqlens, max_seqlen: int, out, lse, workspace,
+                    workspace_bytes: int, stream=None) -> None:
+    rc = lib().mla_bf16_decode(_ptr(q_lat), _ptr(q_rope), batch, heads, softmax_scale, _ptr(pool),
+                               num_pool_pages, page_size, _ptr(block_table), max_pages, _ptr(seqlens),
+                               max_seqlen, _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
+                               _stream(stream))
+    _check(rc, "mla_bf16_decode")
+
+
+class Bf16Cache:
+    """Device buffers of one layer's plain BF16 paged cache (torch-owned):
+    pool [pages][P][576] bf16 bits, block table and lengths."""
+
+    def __init__(self, page_size: int, batch: int, max_pages: int, block_table, num_pool_pages: int,
+                 device="cuda"):
+        import torch
+        self.page_size, self.batch, self.max_pages = page_size, batch, max_pages
+        self.num_pool_pages = num_pool_pages
+        self.pool = torch.zeros((num_pool_pages, page_size, 576), dtype=torch.int16, device=device)
+        self.block_table = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
+        self.lengths = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.host_lengths = [0] * batch
+
+    def append(self, c_kv, k_r, counts, stream=None) -> None:
+        import torch
+        counts = [int(c) for c in counts]
+        if len(counts) != self.batch or min(counts) < 0:
+            raise ValueError("append needs one non-negative count per sequence")
+        if max(a + c for a, c in zip(self.host_lengths, counts)) > self.max_pages * self.page_size:
+            raise ValueError("append beyond the block table's capacity")
+        cu = [0]
+        for c in counts:
+            cu.append(cu[-1] + c)
+        dev = self.pool.device
+        cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
+        mla_bf16_append(c_kv, k_r, cu_t, self.lengths, self.batch, cu[-1], max(counts), self.page_size,
+                        self.block_table, self.max_pages, self.num_pool_pages, self.pool, stream)
+        self.lengths += torch.tensor(counts, dtype=torch.int32, device=dev)
+        self.host_lengths = [a + c for a, c in zip(self.host_lengths, counts)]
+
+    def workspace_bytes(self, heads: int) -> int:
+        return mla_bf16_decode_workspace(self.page_size, self.batch, heads, max(self.host_lengths))
+
+    def decode(self, q_lat, q_rope, softmax_scale: float, out=None, lse=None, workspace=None, stream=None):
+        import torch
+        B, H, _ = q_lat.shape
+        dev = self.pool.device
+        out = torch.empty((B, H, 512), dtype=torch.float32, device=dev) if out is None else out
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev) if lse is None else lse
+        ws_bytes = self.workspace_bytes(H)
+        if workspace is None:
+            if getattr(self, "_ws", None) is None or self._ws.numel() < ws_bytes:
+                self._ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+            workspace = self._ws
+        mla_bf16_decode(q_lat, q_rope, B, H, softmax_scale, self.pool, self.num_pool_pages, self.page_size,
+                        self.block_table, self.max_pages, self.lengths, max(self.host_lengths), out, lse,
+                        workspace, workspace.numel(), stream)
+        return out, lse
 
 
 class DeviceCache:

@@ -190,3 +190,60 @@ def test_decode_noalloc_rejects_without_launch():
 def test_strerror():
     for c in (0, -1, -2, -3, -4, -5, -6, 99):
         assert isinstance(mla.strerror(c), str) and mla.strerror(c)
+
+
+# ----------------------------------------------------------------------------
+# the plain BF16 paged cache (include/mla_bf16.h)
+
+def test_exports_every_bf16_symbol():
+    text = open(os.path.join(ROOT, "include", "mla_bf16.h")).read()
+    names = set(re.findall(r"\b(mla_bf16_\w+)\s*\(", text))
+    assert names == set(mla.BF16_EXPORTS)
+    lib = mla.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+# Work split of the BF16 decode, seen through its workspace: two workgroups
+# per CU (512) over (sequence, head block, split), at least 4 tiles of 16
+# tokens per split, at most 510 pages per split, at most 512 splits.
+BF16_SPLITS = [
+    # (P, batch, heads, max_seqlen, splits per (sequence, head block))
+    (64, 32, 16, 4096, 16),       # 512 / 32
+    (64, 8, 16, 65536, 64),       # 512 / 8
+    (64, 1, 16, 1 << 20, 512),    # one sequence fills the chip
+    (16, 1, 16, 1 << 20, 512),    # 65536 tiles over 510-page windows: 129 at least, 512 taken
+    (64, 64, 128, 32768, 2),      # 512 groups already, but 512 pages pass the window
+    (64, 4, 16, 100, 2),          # 7 tiles: at least 4 per split
+]
+
+
+@pytest.mark.parametrize("P,batch,heads,L,splits", BF16_SPLITS)
+def test_bf16_decode_split_plan(P, batch, heads, L, splits):
+    part = 16 * 512 * 2 + 32 * 4
+    groups = batch * ((heads + 15) // 16)
+    n = mla.mla_bf16_decode_workspace(P, batch, heads, L)
+    assert n == (0 if splits == 1 else groups * splits * part)
+
+
+def test_bf16_argument_errors():
+    lib = mla.lib()
+    for args in [(8, 32, 16, 4096), (64, 32, 0, 4096), (64, 32, 129, 4096), (64, 32, 16, -1), (48, 1, 16, 64),
+                 (2048, 1, 16, 64)]:
+        with pytest.raises(mla.MlaError) as e:
+            mla.mla_bf16_decode_workspace(*args)
+        assert e.value.code == -2
+    # decode: bad page size, max_seqlen beyond the block table, missing pool
+    f = lib.mla_bf16_decode
+    assert f(256, 256, 1, 16, 0.1, 256, 1, 40, 256, 1, 256, 16, 256, 256, None, 0, None) == -2
+    assert f(256, 256, 1, 16, 0.1, 256, 1, 64, 256, 1, 256, 65, 256, 256, None, 0, None) == -2
+    assert f(256, 256, 1, 16, 0.1, None, 1, 64, 256, 1, 256, 64, 256, 256, None, 0, None) == -2
+    assert f(256, 256, 1, 16, float("nan"), 256, 1, 64, 256, 1, 256, 64, 256, 256, None, 0, None) == -2
+    # a missing workspace where one is needed
+    assert f(256, 256, 8, 16, 0.1, 256, 1, 64, 256, 64, 256, 4096, 256, 256, None, 0, None) == -4
+    # append: bad page size, misaligned rows, missing block table
+    g = lib.mla_bf16_append
+    assert g(256, 256, 256, 256, 1, 4, 4, 40, 256, 1, 1, 256, None) == -2
+    assert g(257, 256, 256, 256, 1, 4, 4, 64, 256, 1, 1, 256, None) == -2
+    assert g(256, 256, 256, 256, 1, 4, 4, 64, None, 1, 1, 256, None) == -2
+    assert g(None, None, None, None, 1, 0, 0, 64, None, 0, 0, None, None) == 0  # nothing to append
