@@ -240,6 +240,116 @@ def sweep(steps: int) -> int:
     return 0
 
 
+def bf16_compare(steps: int) -> int:
+    """Low-bit cache against the plain BF16 paged cache (QuantMLA Table 9
+    caption: BF16 with native partitioning; Delta = t_low / t_BF16 - 1), timing
+    only (parity of both is covered by the tests).  (1) Context sweep: C4R4
+    page 128 sink 4 + local 128 against BF16 page 64, 16 heads, batch 1 and 8,
+    N = 1K to 1M; (2) the six workloads at their shapes (BF16 page = the
+    workload's page).  Inputs drawn on the GPU (N(0,1) latent and queries,
+    k_R N(0,1) with channels 7, 23, 39, 55 x20, bf16); each side gets enough
+    layer caches for >= 1 GB (at least 2).  One JSON line per configuration."""
+    import torch
+
+    from bit_kv_cache_writer_amd import mla
+    from bit_kv_cache_writer_amd import workloads as wl
+
+    mla.lib()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    outl = torch.ones(64, device="cuda")
+    outl[[7, 23, 39, 55]] = 20.0
+
+    def bf16_rows(n, width, mult=None):
+        out = torch.empty((n, width), dtype=torch.int16, device="cuda")
+        for a in range(0, n, 1 << 21):
+            e = min(n, a + (1 << 21))
+            x = torch.randn((e - a, width), generator=gen, device="cuda", dtype=torch.float32)
+            if mult is not None:
+                x *= mult
+            out[a:e] = x.to(torch.bfloat16).view(torch.int16)
+        return out
+
+    def timed(calls):
+        stream = torch.cuda.current_stream()
+        for c in calls:
+            c(stream)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps * len(calls))]
+        for st in range(steps):
+            for i, c in enumerate(calls):
+                e = evs[st * len(calls) + i]
+                e[0].record(stream)
+                c(stream)
+                e[1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1000.0)
+
+    def one(tag, B, N, H, P_low, bits, clip, sink, local, P_bf, scale):
+        lay = mla.Layout(P_low, bits, clip, sink, local)
+        page_bytes = mla.mla_lowbit_layout_query(lay)["page_bytes"]
+        rng = np.random.default_rng(np.random.SeedSequence([11, B, N, H]))
+        q_lat = bf16_rows(B * H, 512).view(B, H, 512).contiguous()
+        q_rope = bf16_rows(B * H, 64).view(B, H, 64).contiguous()
+        # low-bit side
+        mp = (N + P_low - 1) // P_low
+        n_pool = int(math.ceil(B * mp * 1.25))
+        bt = rng.permutation(n_pool)[: B * mp].astype(np.int32).reshape(B, mp)
+        layers = min(64, max(2, math.ceil(1.0e9 / (B * mp * page_bytes))))
+        caches = []
+        for _ in range(layers):
+            c = mla.DeviceCache(lay, B, mp, bt, n_pool)
+            done = 0
+            while done < N:
+                t = min(1 << 17, N - done)
+                c.append(bf16_rows(B * t, 512), bf16_rows(B * t, 64, outl), [t] * B)
+                done += t
+            caches.append(c)
+        t_low = timed([lambda s, c=c: c.decode(q_lat, q_rope, scale, stream=s) for c in caches])
+        alg = algorithmic_decode_bytes(type("W", (), {"latent_bits": bits, "page_size": P_low, "sink": sink,
+                                                      "local": local, "heads": H})(), N)
+        low_bytes = alg["total"] * B
+        del caches
+        torch.cuda.empty_cache()
+        # BF16 side
+        mpb = (N + P_bf - 1) // P_bf
+        n_pool_b = int(math.ceil(B * mpb * 1.25))
+        btb = rng.permutation(n_pool_b)[: B * mpb].astype(np.int32).reshape(B, mpb)
+        bf_layer = B * N * 1152
+        layers_b = min(64, max(2, math.ceil(1.0e9 / bf_layer)))
+        bcs = []
+        for _ in range(layers_b):
+            c = mla.Bf16Cache(P_bf, B, mpb, btb, n_pool_b)
+            done = 0
+            while done < N:
+                t = min(1 << 17, N - done)
+                c.append(bf16_rows(B * t, 512), bf16_rows(B * t, 64, outl), [t] * B)
+                done += t
+            bcs.append(c)
+        t_bf = timed([lambda s, c=c: c.decode(q_lat, q_rope, scale, stream=s) for c in bcs])
+        del bcs
+        torch.cuda.empty_cache()
+        gbs = bf_layer / (t_bf * 1e-6) / 1e9
+        print(json.dumps({"compare": tag, "batch": B, "cached_tokens": N, "heads": H,
+                          "lowbit": f"{'C4R4' if bits == 4 else 'C2R4'} page {P_low} sink {sink} local {local}",
+                          "bf16_page": P_bf, "lowbit_us": round(t_low, 3), "bf16_us": round(t_bf, 3),
+                          "delta_pct": round((t_low / t_bf - 1.0) * 100.0, 1),
+                          "speedup_vs_bf16": round(t_bf / t_low, 3),
+                          "lowbit_hbm_gbs": round(low_bytes / (t_low * 1e-6) / 1e9, 1),
+                          "bf16_bytes": bf_layer, "bf16_hbm_gbs": round(gbs, 1),
+                          "bf16_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "layers": [layers, layers_b]}), flush=True)
+
+    for B in (1, 8):
+        for N in (1024, 4096, 16384, 65536, 262144, 1048576):
+            one("context sweep", B, N, 16, 128, 4, 0.0, 4, 128, 64, 1.0 / math.sqrt(192.0))
+    for name, w in wl.WORKLOADS.items():
+        one(name, w.batch, w.seqlen, w.heads, w.page_size, w.latent_bits, w.clip_q, w.sink, w.local,
+            w.page_size, w.softmax_scale)
+    return 0
+
+
 def ragged(steps: int) -> int:
     """Ragged decode and chunked prefill (timing only; parity of both is
     covered by the tests): (1) C4R4 decode, 16 heads, page 128, sink 4 + local
@@ -647,8 +757,8 @@ def main() -> int:
     ap.add_argument("--transform", action="store_true",
                     help="cost of the latent transform fused into the writer vs a standalone GEMM (JSON lines)")
     ap.add_argument("--bf16-baseline", action="store_true",
-                    help="the same workload with every token protected (sink 0, window = N <= 4096): the decode "
-                         "reads a BF16 cache through the same split-KV skeleton")
+                    help="low-bit decode against the plain BF16 paged cache (mla_bf16.h): context sweep 1K..1M at "
+                         "batch 1 and 8, then the six workloads (JSON lines, Delta %% as QuantMLA Table 9)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
@@ -671,15 +781,10 @@ def main() -> int:
         return ragged(max(1, min(args.steps, 5)))
     if args.transform:
         return transform_cost(max(1, min(args.steps, 5)))
+    if args.bf16_baseline:
+        return bf16_compare(max(1, min(args.steps, 5)))
     mla.lib()
     w = wl.WORKLOADS[args.workload]
-    if args.bf16_baseline:
-        import dataclasses
-        if w.seqlen > 4096:
-            print("--bf16-baseline needs N <= 4096 (the longest recent window a layout allows)", file=sys.stderr)
-            return 2
-        w = dataclasses.replace(w, name=w.name + "_bf16", sink=0, local=w.seqlen,
-                                description=w.description + "; every token from BF16 (sink 0, window N)")
 
     m = measure(w, args.steps, args.warmup, args.layers, "numpy")
     head = rates(w, m)
