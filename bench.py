@@ -40,13 +40,25 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
 FLOPS_PER_TOKEN_HEAD = 2 * 576 + 2 * 512  # QK over 576 channels + PV over 512
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "bit_kv_cache_writer_amd", "csrc", "decode.hip")
+# the decode translation unit: its source and the headers it includes
+DECODE_SRCS = [os.path.join(ROOT, "bit_kv_cache_writer_amd", "csrc", f)
+               for f in ("decode.hip", "decode_plan.h", "decode_bf16.h", "geometry.h")]
+
+
+def decode_source_sha256() -> str:
+    """sha256 over the decode sources in a fixed order (a profile taken with
+    other sources no longer describes the kernels)."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
     """HBM bytes per decode call from the committed counter summary, or None
     when there is none or the decode source changed since it was taken."""
-    import hashlib
     path = os.path.join(PROFILES, f"decode_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -56,9 +68,7 @@ def measured_traffic(workload: str):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    with open(DECODE_SRC, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    if fields.get("decode_source_sha256") != digest or "traffic_bytes_per_call" not in fields:
+    if fields.get("decode_source_sha256") != decode_source_sha256() or "traffic_bytes_per_call" not in fields:
         return None
     return int(float(fields["traffic_bytes_per_call"]))
 
