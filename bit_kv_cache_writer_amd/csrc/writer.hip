@@ -51,6 +51,10 @@ struct WriterParams {
 };
 
 __device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+// Workgroup barrier for LDS traffic only (__syncthreads would also wait for
+// every outstanding global load, prefetches included).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // fp32 -> bf16 bits, nearest with ties to even (finite values)
 __device__ inline uint32_t f32_to_bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -378,39 +382,23 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       float acc[kWaves];
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) acc[w] = 0.0f;
-      // this thread's 16-byte pieces of the next pass's A_c columns, loaded
-      // one pass ahead so that they arrive while the current pass computes
-      auto a_piece = [&](int j, int k0) {
-        return reinterpret_cast<const uint4*>(p.a_c + static_cast<int64_t>(st_row + 64 * j) * kLatentDim + k0)[st_part];
-      };
-      uint4 nx0 = a_piece(0, 0), nx1 = a_piece(1, 0), nx2 = a_piece(2, 0), nx3 = a_piece(3, 0);
-      uint4 nx4 = a_piece(4, 0), nx5 = a_piece(5, 0), nx6 = a_piece(6, 0), nx7 = a_piece(7, 0);
-#pragma unroll 1
-      for (int k0 = 0; k0 < kLatentDim; k0 += kAChunk) {
-        __syncthreads();  // the previous pass's reads of s_a are done
-        {
-          uint8_t* const dst = s_a + st_row * kAPitch + 16 * st_part;
-          *reinterpret_cast<uint4*>(dst + 0 * 64 * kAPitch) = nx0;
-          *reinterpret_cast<uint4*>(dst + 1 * 64 * kAPitch) = nx1;
-          *reinterpret_cast<uint4*>(dst + 2 * 64 * kAPitch) = nx2;
-          *reinterpret_cast<uint4*>(dst + 3 * 64 * kAPitch) = nx3;
-          *reinterpret_cast<uint4*>(dst + 4 * 64 * kAPitch) = nx4;
-          *reinterpret_cast<uint4*>(dst + 5 * 64 * kAPitch) = nx5;
-          *reinterpret_cast<uint4*>(dst + 6 * 64 * kAPitch) = nx6;
-          *reinterpret_cast<uint4*>(dst + 7 * 64 * kAPitch) = nx7;
-        }
-        __syncthreads();  // s_a (and, on the first pass, s_x) filled
-        if (k0 + kAChunk < kLatentDim) {
-          const int k1 = k0 + kAChunk;
-          nx0 = a_piece(0, k1);
-          nx1 = a_piece(1, k1);
-          nx2 = a_piece(2, k1);
-          nx3 = a_piece(3, k1);
-          nx4 = a_piece(4, k1);
-          nx5 = a_piece(5, k1);
-          nx6 = a_piece(6, k1);
-          nx7 = a_piece(7, k1);
-        }
+      // this thread's 16-byte pieces of a pass's A_c columns, loaded two
+      // passes ahead (two register sets in turn) so that they arrive while
+      // the passes between compute; the barriers here wait for LDS traffic
+      // only (__syncthreads would also drain these loads)
+      const uint4* const a_src = reinterpret_cast<const uint4*>(p.a_c + static_cast<int64_t>(st_row) * kLatentDim) + st_part;
+      uint8_t* const a_dst = s_a + st_row * kAPitch + 16 * st_part;
+      constexpr int kRowStep = 64 * kLatentDim / 8;  // uint4 elements between rows st_row + 64 j
+      uint4 a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
+      a0 = a_src[0 * kRowStep]; a1 = a_src[1 * kRowStep]; a2 = a_src[2 * kRowStep]; a3 = a_src[3 * kRowStep];
+      a4 = a_src[4 * kRowStep]; a5 = a_src[5 * kRowStep]; a6 = a_src[6 * kRowStep]; a7 = a_src[7 * kRowStep];
+      {
+        constexpr int o = kAChunk / 8;
+        b0 = a_src[0 * kRowStep + o]; b1 = a_src[1 * kRowStep + o]; b2 = a_src[2 * kRowStep + o];
+        b3 = a_src[3 * kRowStep + o]; b4 = a_src[4 * kRowStep + o]; b5 = a_src[5 * kRowStep + o];
+        b6 = a_src[6 * kRowStep + o]; b7 = a_src[7 * kRowStep + o];
+      }
+      auto run_pass = [&](int k0) {
         static_assert(kAChunk == 64, "transform_pass takes 64 columns");
         const uint8_t* const arow = s_a + c * kAPitch;
         switch (n) {
@@ -423,12 +411,52 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
           case 7: transform_pass<7>(acc, arow, s_x, k0); break;
           default: transform_pass<8>(acc, arow, s_x, k0); break;
         }
+      };
+      static_assert(kLatentDim % (2 * kAChunk) == 0, "passes go in pairs");
+#pragma unroll 1
+      for (int k0 = 0; k0 < kLatentDim; k0 += 2 * kAChunk) {
+        // a pass's pieces into LDS between two LDS-only barriers, then the
+        // set is reloaded for the pass two ahead
+        lds_barrier();  // the previous pass's reads of s_a are done
+        *reinterpret_cast<uint4*>(a_dst + 0 * 64 * kAPitch) = a0;
+        *reinterpret_cast<uint4*>(a_dst + 1 * 64 * kAPitch) = a1;
+        *reinterpret_cast<uint4*>(a_dst + 2 * 64 * kAPitch) = a2;
+        *reinterpret_cast<uint4*>(a_dst + 3 * 64 * kAPitch) = a3;
+        *reinterpret_cast<uint4*>(a_dst + 4 * 64 * kAPitch) = a4;
+        *reinterpret_cast<uint4*>(a_dst + 5 * 64 * kAPitch) = a5;
+        *reinterpret_cast<uint4*>(a_dst + 6 * 64 * kAPitch) = a6;
+        *reinterpret_cast<uint4*>(a_dst + 7 * 64 * kAPitch) = a7;
+        lds_barrier();  // s_a (and, on the first pass, s_x) filled
+        if (k0 + 2 * kAChunk < kLatentDim) {
+          const int o = (k0 + 2 * kAChunk) / 8;
+          a0 = a_src[0 * kRowStep + o]; a1 = a_src[1 * kRowStep + o]; a2 = a_src[2 * kRowStep + o];
+          a3 = a_src[3 * kRowStep + o]; a4 = a_src[4 * kRowStep + o]; a5 = a_src[5 * kRowStep + o];
+          a6 = a_src[6 * kRowStep + o]; a7 = a_src[7 * kRowStep + o];
+        }
+        run_pass(k0);
+        lds_barrier();
+        *reinterpret_cast<uint4*>(a_dst + 0 * 64 * kAPitch) = b0;
+        *reinterpret_cast<uint4*>(a_dst + 1 * 64 * kAPitch) = b1;
+        *reinterpret_cast<uint4*>(a_dst + 2 * 64 * kAPitch) = b2;
+        *reinterpret_cast<uint4*>(a_dst + 3 * 64 * kAPitch) = b3;
+        *reinterpret_cast<uint4*>(a_dst + 4 * 64 * kAPitch) = b4;
+        *reinterpret_cast<uint4*>(a_dst + 5 * 64 * kAPitch) = b5;
+        *reinterpret_cast<uint4*>(a_dst + 6 * 64 * kAPitch) = b6;
+        *reinterpret_cast<uint4*>(a_dst + 7 * 64 * kAPitch) = b7;
+        lds_barrier();
+        if (k0 + 3 * kAChunk < kLatentDim) {
+          const int o = (k0 + 3 * kAChunk) / 8;
+          b0 = a_src[0 * kRowStep + o]; b1 = a_src[1 * kRowStep + o]; b2 = a_src[2 * kRowStep + o];
+          b3 = a_src[3 * kRowStep + o]; b4 = a_src[4 * kRowStep + o]; b5 = a_src[5 * kRowStep + o];
+          b6 = a_src[6 * kRowStep + o]; b7 = a_src[7 * kRowStep + o];
+        }
+        run_pass(k0 + kAChunk);
       }
       uint16_t* const ys = reinterpret_cast<uint16_t*>(&s_y[0][0]);
 #pragma unroll
       for (int w = 0; w < kWaves; ++w)
         if (w < n) ys[w * kLatentDim + c] = static_cast<uint16_t>(f32_to_bf16_rne(acc[w]));
-      __syncthreads();
+      lds_barrier();
       if (wave < n) {
         const int t = t0 + wave;
         const uint4 y = s_y[wave][lane];
@@ -438,7 +466,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
         if (p.local > 0 && t >= end - p.local)
           copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, y, kr, lane);
       }
-      __syncthreads();  // s_x and s_y are refilled for the next tokens
+      lds_barrier();  // s_x and s_y are refilled for the next tokens
     }
   } else {
     // Latent codes + metadata, BF16 sink / ring copies.
