@@ -32,8 +32,10 @@ def say(*a):
 PARITY_LOG: list = []
 
 
-def record(case: str, worst_rel: float, worst_lse: float, rows: int) -> None:
-    PARITY_LOG.append((case, worst_rel, worst_lse, rows))
+def record(case: str, worst_rel: float, worst_lse: float, rows: int, lse_use: float = 0.0) -> None:
+    """lse_use: the largest |d lse| / bar over the case's rows (the bar
+    includes the fp32 slack where one is given)."""
+    PARITY_LOG.append((case, worst_rel, worst_lse, rows, lse_use))
 
 
 def layouts(P, bits, clip, sink, local):
@@ -126,7 +128,7 @@ def compare_decode(out, lse, ref_out, ref_lse, heads=None, seqs=None, case=None,
     out = np.asarray(out, np.float64)
     lse = np.asarray(lse, np.float64)
     assert np.all(np.isfinite(out)), "non-finite decode output"
-    worst, worst_lse, rows = 0.0, 0.0, 0
+    worst, worst_lse, lse_use, rows = 0.0, 0.0, 0.0, 0
     seqs = range(ref_out.shape[0]) if seqs is None else seqs
     for bi, b in enumerate(seqs):
         for hi in range(ref_out.shape[1]):
@@ -144,9 +146,10 @@ def compare_decode(out, lse, ref_out, ref_lse, heads=None, seqs=None, case=None,
             d = abs(lse[bi, hi] - ref_lse[bi, hi])
             worst_lse = max(worst_lse, d)
             bar = TOL_LSE + (0.0 if lse_slack is None else float(lse_slack[bi, hi]))
+            lse_use = max(lse_use, d / bar)
             assert d <= bar, f"seq {b} head {hi}: lse diff {d:.3e} > {bar:.3e}"
     if case is not None:
-        record(case, worst, worst_lse, rows)
+        record(case, worst, worst_lse, rows, lse_use)
     return worst
 
 
