@@ -76,6 +76,8 @@ CASES = [
     ("p256_h7", 256, [5, 600, 256], 7),
     # one long sequence: over 32 splits, so the merge takes its many-split shape
     ("p64_b1_long", 64, [40000], 16),
+    # the largest page and a single head
+    ("p1024_h1", 1024, [2000, 5, 1024], 1),
 ]
 
 
