@@ -167,6 +167,8 @@ __device__ inline int col_to_channel(int c) {
 // Latent-code unpack by masking: slot value = code * 2^-24 * sigma (an fp16
 // subnormal, the code sitting at bit log2(sigma) of a zero-exponent half).
 // 8 nibbles -> slots [n0 n4 n1 n5 n2 n6 n3 n7], sigma = 16 in slots 2, 3, 6, 7.
+// (A nibble can sit only at bits 0-3 or 4-7 of a half: bits 10-14 are the
+// exponent, so the upper two nibbles of each half are shifted down first.)
 __device__ inline half8 unpack4(uint32_t w) {
   const uint32_t t = w >> 8;
   const u32x4 v = {w & 0x000F000Fu, w & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u};
@@ -601,13 +603,13 @@ __device__ inline void score_mfma(f32x4 (&acc)[6], const ScoreIn<BITS>& si, cons
   acc[4] = mfma(__builtin_bit_cast(half8, si.ma), q.meta, acc[4]);
 }
 
-// Scores (log2 domain) of one packed tile (tokens j0 .. j0+15 of a complete
-// page, valid in [vlo, vhi); none when !has) from its MFMA sums: lane (h, gq)
-// gets tokens 4 gq + r of head h.  md[r] = the metadata words of token 4 gq + r.
+// Scores (log2 domain: km and bias carry softmax_scale log2(e)) of one packed
+// tile (tokens j0 .. j0+15 of a complete page, valid in [vlo, vhi); none when
+// !has) from its MFMA sums: lane (h, gq) gets tokens 4 gq + r of head h.
+// md[r] = the metadata words of token 4 gq + r.
 template <int BITS>
 __device__ inline void score_finish(float (&sc)[4], u32x4 (&md)[4], const f32x4 (&acc)[6], const uint8_t* slot,
-                                    float bias, const ScoreMul& km, bool has, int j0, int vlo, int vhi, int gq,
-                                    float c_log2) {
+                                    float bias, const ScoreMul& km, bool has, int j0, int vlo, int vhi, int gq) {
   using G = TileGeom<BITS>;
 #pragma unroll
   for (int r = 0; r < 4; ++r) md[r] = lds_ld<u32x4>(slot + G::kOffMeta + 16 * (4 * gq + r));
@@ -619,14 +621,14 @@ __device__ inline void score_finish(float (&sc)[4], u32x4 (&md)[4], const f32x4 
   }
   if (has && j0 >= vlo && j0 + kTile <= vhi) {  // whole tile valid
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = score_of(v[r], acc[4][r], acc[5][r], bias, km) * c_log2;
+    for (int r = 0; r < 4; ++r) sc[r] = score_of(v[r], acc[4][r], acc[5][r], bias, km);
     return;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = j0 + 4 * gq + r;
     const float z = score_of(v[r], acc[4][r], acc[5][r], bias, km);
-    sc[r] = (has && t >= vlo && t < vhi) ? z * c_log2 : kNegInf;
+    sc[r] = (has && t >= vlo && t < vhi) ? z : kNegInf;
   }
 }
 
@@ -634,28 +636,41 @@ __device__ inline void score_finish(float (&sc)[4], u32x4 (&md)[4], const f32x4 
 // tokens 8 gq .. 8 gq + 7 of the K block (tiles 2 kb, 2 kb + 1), fp16.
 __device__ inline int p_entry(int kb, int g, int gq, int h) { return (((kb * 4 + g) * 4 + gq) * kHeadBlock + h) * 16; }
 
-// Headroom of this lane's four tokens of a packed tile (metadata words md):
-// k = E - 7, E the exponent with max_g s_g < 2^E over the tokens' latent
-// scales (fp16 bit patterns: field 0 gives E = -14, the subnormal bound).
-// The running max m of a packed workgroup is raised so that t + k <= m + 8
-// for every token (t its score), hence p = 2^(t - m) <= 2^(8 - k) and
-// p s_g < 2^15: the fp16 weights P'_g below never overflow, and the largest
-// of a tile sits near 2^14, far above the subnormal range, at any latent
-// magnitude.  k >= -21 bounds p by 2^29, which fp32 sums hold.
-__device__ inline float scale_headroom(const u32x4 (&md)[4]) {
-  uint32_t a = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) a = max(a, md[r][g] & 0x7FFFu);
-  }
+// Headroom of the four tokens 4 gq .. 4 gq + 3 of a packed tile: k = E - 7,
+// E the exponent with max_g s_g < 2^E over the tokens' latent scales (fp16
+// bit patterns: field 0 gives E = -14, the subnormal bound).  The running max
+// m of a packed workgroup is raised so that t + k <= m + 8 for every token (t
+// its score), hence p = 2^(t - m) <= 2^(8 - k) and p s_g < 2^15: the fp16
+// weights P'_g below never overflow, and the largest of a tile sits near
+// 2^14, far above the subnormal range, at any latent magnitude.  k >= -21
+// bounds p by 2^29, which fp32 sums hold.
+// Lane (n16, gq) reads the scale word of token 4 gq + n16 % 4, group n16 / 4,
+// and the row's 16 lanes take their maximum by rotations within the row.
+template <int BITS>
+__device__ inline float scale_headroom(const uint8_t* slot, int n16, int gq) {
+  uint32_t a = lds_ld<uint32_t>(slot + TileGeom<BITS>::kOffMeta + 16 * (4 * gq + (n16 & 3)) + 4 * (n16 >> 2)) & 0x7FFFu;
+  a = max(a, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(a), 0x128, 0xF, 0xF, true)));  // row_ror:8
+  a = max(a, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(a), 0x124, 0xF, 0xF, true)));  // row_ror:4
+  a = max(a, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(a), 0x122, 0xF, 0xF, true)));  // row_ror:2
+  a = max(a, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(a), 0x121, 0xF, 0xF, true)));  // row_ror:1
   return static_cast<float>(a >> 10) - 21.f;
 }
 
-// Weights of this wave's packed tile: P'_g = fp16(p s_g / sigma), one
-// rounding of the fp32 product, into the P' entries its tokens fall in
-// (tokens 4 gq + 2, 4 gq + 3 land in the output unpack's sigma = 16 slots);
-// adds this lane's sums of p and of p m_g (fp32) to st.
+// Weights of this wave's packed tile: P'_g = fp16(p s_g / sigma) into the P'
+// entries its tokens fall in (tokens 4 gq + 2, 4 gq + 3 land in the output
+// unpack's sigma = 16 slots); adds this lane's sums of p and of p m_g (fp32)
+// to st.  Each weight is one v_fma_mix{lo,hi}_f16 (p s + 0 rounded to fp16),
+// with the scale taken as the fp16 low half of its metadata word and the pair
+// packed in one register.
+__device__ inline uint32_t weight_pair(float p0, uint32_t w0, float p1, uint32_t w1) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixhi_f16 %0, %3, %4, 0 op_sel_hi:[0,1,0]"
+      : "=&v"(d)
+      : "v"(p0), "v"(w0), "v"(p1), "v"(w1));
+  return d;
+}
+
 __device__ inline void packed_weights(const float (&pr)[4], const u32x4 (&md)[4], uint8_t* pbase,
                                       float (&st)[kStatW], int wave, int n16, int gq) {
   st[0] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
@@ -663,14 +678,11 @@ __device__ inline void packed_weights(const float (&pr)[4], const u32x4 (&md)[4]
   const int at = 8 * (gq & 1);  // tokens 4 gq .. 4 gq + 3 of the tile
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    half4 pa;
     float ms = st[1 + g];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pa[r] = static_cast<_Float16>(pw[r] * lo_f16(md[r][g]));
-      ms = fmaf(pr[r], hi_f16(md[r][g]), ms);
-    }
-    lds_st<half4>(pbase + p_entry(wave >> 1, g, 2 * (wave & 1) + (gq >> 1), n16) + at, pa);
+    for (int r = 0; r < 4; ++r) ms = fmaf(pr[r], hi_f16(md[r][g]), ms);
+    const u32x2 pa = {weight_pair(pw[0], md[0][g], pw[1], md[1][g]), weight_pair(pw[2], md[2][g], pw[3], md[3][g])};
+    lds_st<u32x2>(pbase + p_entry(wave >> 1, g, 2 * (wave & 1) + (gq >> 1), n16) + at, pa);
     st[1 + g] = ms;
   }
 }
@@ -1217,9 +1229,11 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
   lds_barrier();  // query converted
   QueryOps<BITS> q;
   load_query<BITS>(q, qops, lane);
+  // the multipliers carry the softmax scale in the log2 domain, so the
+  // scores leave score_finish ready for exp2
   ScoreMul km;
-  km.lat = kCodeScale / qscale;
-  km.meta = q.meta_mul;
+  km.lat = kCodeScale / qscale * p.c_log2;
+  km.meta = q.meta_mul * p.c_log2;
 
   float m_run = kNegInf;
   RopeOps ro;
@@ -1234,6 +1248,8 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     const int pidx = ((t_lo + it) * kTile) >> p.log2P;
     if (has && pidx != ro_page) {  // (a page missing from the block table only spoils its own tiles)
       rope_ops(ro, qr_row, slot + TileGeom<BITS>::kOffRMeta, gq);
+      ro.mul *= p.c_log2;
+      ro.bias *= p.c_log2;
       ro_page = pidx;
     }
     // page ids of this tile and of the tiles issued this round, read with
@@ -1247,10 +1263,10 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     float sc[4];
     u32x4 md[4];
     km.rope = ro.mul;
-    score_finish<BITS>(sc, md, acc, slot, ro.bias, km, has, (t_lo + it) * kTile, sr.lo_p, sr.hi_p, gq,
-                       p.c_log2);
+    score_finish<BITS>(sc, md, acc, slot, ro.bias, km, has, (t_lo + it) * kTile, sr.lo_p, sr.hi_p, gq);
     if (r == 0 && it + 1 < my_end) issue(it + 1, uniform(id_1), 1);
-    const float tmax = row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) + scale_headroom(md));
+    const float tmax =
+        row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) + scale_headroom<BITS>(slot, n16, gq));
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
 
