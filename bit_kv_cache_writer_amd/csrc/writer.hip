@@ -16,6 +16,10 @@
 //     buffer, and it alone then writes the tail rows of a page left
 //     incomplete, after a barrier -- so no workgroup reads tail rows another
 //     one overwrites.
+// With the latent transform and no clipping, a page has four workgroups, one
+// per 128-channel latent group: each forms its quarter of y = A_c x (a quarter
+// of A_c) and caches that group, which is quantized on its own; the first of
+// them also does the page's k_R work.
 // The quantizer's arithmetic is IEEE fp32 with each operation rounded on its
 // own (contraction off), so codes and metadata are reproducible bit for bit.
 #include <hip/hip_runtime.h>
@@ -174,8 +178,13 @@ __device__ inline uint32_t wave_kth_smallest(const uint32_t (&a)[8], int k) {
   return prefix;
 }
 
-// Quantizes one latent token (one wave; lane l holds channels 8l..8l+7).
-__device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8_t* page, int slot, int lane) {
+// Quantizes one latent token (one wave; lane l holds channels 8l..8l+7), or,
+// without clipping, one 128-channel group of a token per 16-lane row: the
+// reductions stay inside each row, and col (= lane for whole tokens) is the
+// channel octet the lane holds, which places its codes and its group's
+// metadata word.
+__device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8_t* page, int slot, int col) {
+  const int lane = col;
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   float x[8];
 #pragma unroll
@@ -298,10 +307,16 @@ __device__ inline void transform_pass(float (&acc)[kWaves], const uint8_t* arow,
   }
 }
 
-template <bool kTransform>
+// kMode 0: plain writer; 1: with the latent transform, one workgroup per
+// page; 2: with the latent transform, four workgroups per page (latent group
+// g = blockIdx.x % 4; no clipping).
+template <int kMode>
 __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
-  const int b = blockIdx.x / p.pages_per_seq_grid;
-  const int pi = blockIdx.x % p.pages_per_seq_grid;
+  constexpr bool kTransform = kMode != 0;
+  const int g = kMode == 2 ? static_cast<int>(blockIdx.x & 3u) : 0;
+  const int blk = kMode == 2 ? static_cast<int>(blockIdx.x >> 2) : static_cast<int>(blockIdx.x);
+  const int b = blk / p.pages_per_seq_grid;
+  const int pi = blk % p.pages_per_seq_grid;
   if (b >= p.batch) return;
   const int r0 = p.cu_new[b], r1 = p.cu_new[b + 1];
   const int sb = p.seqlens_before[b];
@@ -325,7 +340,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   // looked up: they do not depend on it.  The barrier before their reduction
   // waits for them.
   __shared__ uint4 s_rows[256 * kRopeDim / 8];  // P x 64 bf16
-  const bool completes = (pg + 1) * P <= end;
+  const bool completes = g == 0 && (pg + 1) * P <= end;  // (the group-0 workgroup does the k_R work)
   if (completes) {
     for (int k = 0; k * kThreads < P * (kRopeDim / 8); ++k) {
       const int i = static_cast<int>(threadIdx.x) + k * kThreads;
@@ -349,7 +364,87 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   }
   uint8_t* page = p.pool + static_cast<int64_t>(page_id) * p.page_bytes;
 
-  if constexpr (kTransform) {
+  if constexpr (kMode == 2) {
+    // The latent transform split by latent group: thread (j, o) forms output
+    // channel 128 g + o of token slot j (of up to 4 tokens at a time) as the
+    // same ascending fp32 fma chain as below, over rows 128 g .. 128 g + 127
+    // of A_c (64 input columns per LDS pass, loaded two passes ahead); row q
+    // of wave 0 then caches group g of token q: its codes and metadata word,
+    // and its 256 bytes of the BF16 sink / ring rows (plus the k_R bytes in
+    // the group-0 workgroup).
+    constexpr int kTok = 4;
+    constexpr int kAChunk = 64;
+    constexpr int kAPitch = 2 * kAChunk + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t s_a[kGroup * kAPitch];
+    __shared__ __attribute__((aligned(16))) float s_x[kTok][kLatentDim];
+    __shared__ __attribute__((aligned(16))) uint16_t s_y[kTok][kGroup];
+    const int o = static_cast<int>(threadIdx.x) & (kGroup - 1), j = static_cast<int>(threadIdx.x) >> 7;
+    // staging: 16-byte piece st_part of rows st_row and st_row + 64 of a pass
+    const int st_row = static_cast<int>(threadIdx.x) >> 3, st_part = static_cast<int>(threadIdx.x) & 7;
+    const uint4* const a_src =
+        reinterpret_cast<const uint4*>(p.a_c + static_cast<int64_t>(kGroup * g + st_row) * kLatentDim) + st_part;
+    uint8_t* const a_dst = s_a + st_row * kAPitch + 16 * st_part;
+    constexpr int kRowStep = 64 * kLatentDim / 8;  // uint4 elements from row st_row to row st_row + 64
+    const uint8_t* const arow = s_a + o * kAPitch;
+    for (int t0 = tb; t0 < te; t0 += kTok) {
+      const int n = min(kTok, te - t0);
+      if (wave < n) {
+        const uint4 raw =
+            reinterpret_cast<const uint4*>(p.c_kv + (r0 + (t0 + wave - sb)) * static_cast<int64_t>(kLatentDim))[lane];
+        const float4 lo = {bf16_to_f32(raw.x & 0xFFFFu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xFFFFu),
+                           bf16_to_f32(raw.y >> 16)};
+        const float4 hi = {bf16_to_f32(raw.z & 0xFFFFu), bf16_to_f32(raw.z >> 16), bf16_to_f32(raw.w & 0xFFFFu),
+                           bf16_to_f32(raw.w >> 16)};
+        *reinterpret_cast<float4*>(&s_x[wave][8 * lane]) = lo;
+        *reinterpret_cast<float4*>(&s_x[wave][8 * lane + 4]) = hi;
+      }
+      float acc[kWaves];
+      acc[0] = 0.0f;
+      uint4 a0 = a_src[0], a1 = a_src[kRowStep];
+      uint4 b0 = a_src[kAChunk / 8], b1 = a_src[kRowStep + kAChunk / 8];
+      static_assert(kLatentDim % (2 * kAChunk) == 0, "passes go in pairs");
+#pragma unroll 1
+      for (int k0 = 0; k0 < kLatentDim; k0 += 2 * kAChunk) {
+        lds_barrier();  // the previous pass's reads of s_a are done
+        *reinterpret_cast<uint4*>(a_dst) = a0;
+        *reinterpret_cast<uint4*>(a_dst + 64 * kAPitch) = a1;
+        lds_barrier();  // s_a (and, on the first pass, s_x) filled
+        if (k0 + 2 * kAChunk < kLatentDim) {
+          a0 = a_src[(k0 + 2 * kAChunk) / 8];
+          a1 = a_src[kRowStep + (k0 + 2 * kAChunk) / 8];
+        }
+        if (j < n) transform_pass<1>(acc, arow, &s_x[j], k0);
+        lds_barrier();
+        *reinterpret_cast<uint4*>(a_dst) = b0;
+        *reinterpret_cast<uint4*>(a_dst + 64 * kAPitch) = b1;
+        lds_barrier();
+        if (k0 + 3 * kAChunk < kLatentDim) {
+          b0 = a_src[(k0 + 3 * kAChunk) / 8];
+          b1 = a_src[kRowStep + (k0 + 3 * kAChunk) / 8];
+        }
+        if (j < n) transform_pass<1>(acc, arow, &s_x[j], k0 + kAChunk);
+      }
+      if (j < n) s_y[j][o] = static_cast<uint16_t>(f32_to_bf16_rne(acc[0]));
+      lds_barrier();
+      const int q = lane >> 4, l16 = lane & 15;
+      if (wave == 0 && q < n) {
+        const int t = t0 + q;
+        const uint4 y = *reinterpret_cast<const uint4*>(&s_y[q][8 * l16]);
+        write_latent_token(p, y, page, t - pg * P, 16 * g + l16);
+        // this group's slice of the BF16 rows (the group-0 workgroup adds k_R)
+        auto copy_slice = [&](uint16_t* dst) {
+          reinterpret_cast<uint4*>(dst + kGroup * g)[l16] = y;
+          if (g == 0 && l16 < 8)
+            reinterpret_cast<uint4*>(dst + kLatentDim)[l16] =
+                reinterpret_cast<const uint4*>(p.k_r + (r0 + (t - sb)) * static_cast<int64_t>(kRopeDim))[l16];
+        };
+        if (t < p.sink_n) copy_slice(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems);
+        if (p.local > 0 && t >= end - p.local)
+          copy_slice(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems);
+      }
+      lds_barrier();  // s_x and s_y are refilled for the next tokens
+    }
+  } else if constexpr (kTransform) {
     // The latent transform (RAQ-MLA Figure 4 caption; appendix Table 9, the
     // fused variant): y = A_c x per token, for up to kWaves tokens at a time.
     // Thread c forms output channel c of each token as an fp32 fma chain over
@@ -568,7 +663,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
 
   // Tail rows of the page left incomplete, written by the first page's
   // workgroup after every read of the old tail rows above.
-  if (pi == 0 && end % P != 0) {
+  if (g == 0 && pi == 0 && end % P != 0) {
     __syncthreads();
     const int t0 = max(sb, (end / P) * P);
     for (int i = threadIdx.x; i < (end - t0) * (kRopeDim / 8); i += kThreads) {
@@ -636,12 +731,17 @@ int write_impl(const mla_lowbit_layout* layout, const void* a_c, const void* c_k
   p.page_bytes = g.page_bytes;
   // pages a call of n tokens can touch: (n - 1) / P + 2
   p.pages_per_seq_grid = (max_new_per_seq - 1) / g.page_size + 2;
-  const int64_t blocks = static_cast<int64_t>(batch) * p.pages_per_seq_grid;
+  // with the transform and no clipping, four workgroups per page (one per
+  // latent group); the clip needs all 512 channels of a token in one wave
+  const bool split = a_c && !g.clip;
+  const int64_t blocks = static_cast<int64_t>(batch) * p.pages_per_seq_grid * (split ? 4 : 1);
   if (blocks > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
-  if (a_c)
-    hipLaunchKernelGGL(writer_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  if (split)
+    hipLaunchKernelGGL(writer_kernel<2>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  else if (a_c)
+    hipLaunchKernelGGL(writer_kernel<1>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(writer_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(writer_kernel<0>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
 }
 

@@ -114,11 +114,15 @@ def test_chunked_appends_equal_bulk(torch_cuda):
 
 
 TRANSFORM_CASES = [
-    # name, P, bits, clip, sink, local, lengths, chunk schedule (None = one bulk append)
+    # name, P, bits, clip, sink, local, lengths, chunk schedule (None = one bulk append);
+    # without the clip the writer runs one workgroup per (page, latent group),
+    # with it one per page
     ("xf_c4r4_p64_steps", 64, 4, 0.0, 4, 32, [3, 70, 130, 9],
      [[1, 1, 1, 1]] * 3 + [[0, 67, 127, 6]]),
     ("xf_c2r4_p128_bulk", 128, 2, 0.94, 4, 128, [300, 5, 129], None),
     ("xf_c4r4_p32_noprot", 32, 4, 0.0, 0, 0, [64, 33], [[1, 1], [20, 0], [43, 32]]),
+    # INT2 latent without the clip: the per-group workgroups, 2-bit codes
+    ("xf_c2r4_p64_noclip", 64, 2, 0.0, 4, 32, [150, 64, 1], [[1, 64, 1], [149, 0, 0]]),
 ]
 
 
