@@ -123,6 +123,9 @@ TRANSFORM_CASES = [
     ("xf_c4r4_p32_noprot", 32, 4, 0.0, 0, 0, [64, 33], [[1, 1], [20, 0], [43, 32]]),
     # INT2 latent without the clip: the per-group workgroups, 2-bit codes
     ("xf_c2r4_p64_noclip", 64, 2, 0.0, 4, 32, [150, 64, 1], [[1, 64, 1], [149, 0, 0]]),
+    # the largest page: 300-token calls into 256-token pages, one page left
+    # one token short of full
+    ("xf_c4r4_p256_bulk", 256, 4, 0.0, 4, 128, [600, 255, 256, 1], [[300, 255, 0, 1], [300, 0, 256, 0]]),
 ]
 
 
