@@ -118,23 +118,65 @@ __device__ inline float rint_div(float d, float s, float rcp_s) {
   return r;
 }
 
-// Min / max over each 16-lane row by DPP lane moves (VALU, no LDS round
-// trip): swap neighbours, swap pairs, then rotate the row by 4 and by 8.
+// Codes of 8 values v[i] with offset m and step s: for s > 0 the same codes
+// as min(max(rint_div(v - m, s), 0), levels); s = 0 gives 0 (the reciprocal
+// is replaced by 0, so every quotient is 0).  The fast quotient is checked
+// for nearness to a half-integer once for the 8 values (|qa - rint(qa)| at
+// least 0.5 - 1e-5 is the same set as rint_div's test), and only a row with
+// such a value takes the IEEE division.  Codes are packed `bits` apiece.
+__device__ inline uint32_t pack_codes(const float (&v)[8], float m, float s, float rcp_s, int bits, float levels) {
+  const float rc = s > 0.0f ? rcp_s : 0.0f;
+  float r[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float qa = (v[i] - m) * rc;
+    r[i] = rintf(qa);
+    near |= fabsf(qa - r[i]) >= 0.49999f;
+  }
+  if (__builtin_expect(near, 0)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = rint_div(v[i] - m, s, rcp_s);
+  }
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    packed |= static_cast<uint32_t>(__builtin_amdgcn_fmed3f(r[i], 0.0f, levels)) << (bits * i);
+  return packed;
+}
+
+// A DPP lane move within 16-lane rows.
 template <int kCtrl>
 __device__ inline float dpp_move(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
-__device__ inline float wave_min16(float v) {
-  v = fminf(v, dpp_move<0xB1>(v));   // quad_perm [1, 0, 3, 2]
-  v = fminf(v, dpp_move<0x4E>(v));   // quad_perm [2, 3, 0, 1]
-  v = fminf(v, dpp_move<0x124>(v));  // row_ror:4
-  return fminf(v, dpp_move<0x128>(v));  // row_ror:8
+// Min and max over each 16-lane row by DPP lane moves (VALU, no LDS round
+// trip): swap neighbours, swap pairs, then rotate the row by 4 and by 8.  They
+// run on order-preserving integer keys of the floats (negative values get
+// their magnitude bits flipped), so each step is one v_min_i32 / v_max_i32
+// with its lane move fused in.  Exact for every non-NaN value; the key map is
+// its own inverse.
+__device__ inline int f32_key(float f) {
+  const int b = __float_as_int(f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
 }
-__device__ inline float wave_max16(float v) {
-  v = fmaxf(v, dpp_move<0xB1>(v));
-  v = fmaxf(v, dpp_move<0x4E>(v));
-  v = fmaxf(v, dpp_move<0x124>(v));
-  return fmaxf(v, dpp_move<0x128>(v));
+__device__ inline float key_f32(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+template <int kCtrl>
+__device__ inline int dpp_key(int k) {
+  return __builtin_amdgcn_mov_dpp(k, kCtrl, 0xF, 0xF, true);
+}
+__device__ inline void row_minmax16(float& mn, float& mx) {
+  int a = f32_key(mn), b = f32_key(mx);
+  a = min(a, dpp_key<0xB1>(a));
+  b = max(b, dpp_key<0xB1>(b));
+  a = min(a, dpp_key<0x4E>(a));
+  b = max(b, dpp_key<0x4E>(b));
+  a = min(a, dpp_key<0x124>(a));
+  b = max(b, dpp_key<0x124>(b));
+  a = min(a, dpp_key<0x128>(a));
+  b = max(b, dpp_key<0x128>(b));
+  mn = key_f32(a);
+  mx = key_f32(b);
 }
 // Min / max over lanes l, l ^ 8, l ^ 16, ... (the 8 lanes of equal l % 8):
 // a DPP row rotation by 8, then the row-swap permutes across 16 and 32 lanes.
@@ -222,8 +264,7 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
     mn = fminf(mn, x[i]);
     mx = fmaxf(mx, x[i]);
   }
-  mn = wave_min16(mn);
-  mx = wave_max16(mx);
+  row_minmax16(mn, mx);
   const int levels = (1 << p.bits) - 1;
   const uint16_t mh = f16_round_down(mn);
   const float minf = f16_to_f32(mh);
@@ -232,17 +273,7 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
   const uint16_t sh = f16_round_up(s);
   const float sf = f16_to_f32(sh);
   const float rs = __builtin_amdgcn_rcpf(sf);
-  uint32_t packed = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t code = 0;
-    if (sf > 0.0f) {
-      float r = rint_div(x[i] - minf, sf, rs);
-      r = fminf(fmaxf(r, 0.0f), static_cast<float>(levels));
-      code = static_cast<uint32_t>(r);
-    }
-    packed |= code << (p.bits * i);
-  }
+  const uint32_t packed = pack_codes(x, minf, sf, rs, p.bits, static_cast<float>(levels));
   uint8_t* row = page + static_cast<int64_t>(slot) * p.latent_row;
   if (p.bits == 4) {
     reinterpret_cast<uint32_t*>(row)[lane] = packed;
