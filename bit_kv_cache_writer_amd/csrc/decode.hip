@@ -607,12 +607,17 @@ __device__ inline void score_mfma(f32x4 (&acc)[6], const ScoreIn<BITS>& si, cons
 // tile (tokens j0 .. j0+15 of a complete page, valid in [vlo, vhi); none when
 // !has) from its MFMA sums: lane (h, gq) gets tokens 4 gq + r of head h.
 // md[r] = the metadata words of token 4 gq + r.
+// The metadata words of tokens 4 gq + r of a packed tile (loaded with the
+// tile's score inputs, ahead of the score MFMAs).
 template <int BITS>
-__device__ inline void score_finish(float (&sc)[4], u32x4 (&md)[4], const f32x4 (&acc)[6], const uint8_t* slot,
-                                    float bias, const ScoreMul& km, bool has, int j0, int vlo, int vhi, int gq) {
-  using G = TileGeom<BITS>;
+__device__ inline void load_tile_meta(u32x4 (&md)[4], const uint8_t* slot, int gq) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) md[r] = lds_ld<u32x4>(slot + G::kOffMeta + 16 * (4 * gq + r));
+  for (int r = 0; r < 4; ++r) md[r] = lds_ld<u32x4>(slot + TileGeom<BITS>::kOffMeta + 16 * (4 * gq + r));
+}
+
+template <int BITS>
+__device__ inline void score_finish(float (&sc)[4], const u32x4 (&md)[4], const f32x4 (&acc)[6], float bias,
+                                    const ScoreMul& km, bool has, int j0, int vlo, int vhi, int gq) {
   float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -646,9 +651,13 @@ __device__ inline int p_entry(int kb, int g, int gq, int h) { return (((kb * 4 +
 // bounds p by 2^29, which fp32 sums hold.
 // Lane (n16, gq) reads the scale word of token 4 gq + n16 % 4, group n16 / 4,
 // and the row's 16 lanes take their maximum by rotations within the row.
+// (word: that scale word, loaded with the tile's score inputs)
 template <int BITS>
-__device__ inline float scale_headroom(const uint8_t* slot, int n16, int gq) {
-  uint32_t a = lds_ld<uint32_t>(slot + TileGeom<BITS>::kOffMeta + 16 * (4 * gq + (n16 & 3)) + 4 * (n16 >> 2)) & 0x7FFFu;
+__device__ inline uint32_t headroom_word(const uint8_t* slot, int n16, int gq) {
+  return lds_ld<uint32_t>(slot + TileGeom<BITS>::kOffMeta + 16 * (4 * gq + (n16 & 3)) + 4 * (n16 >> 2));
+}
+__device__ inline float scale_headroom(uint32_t word) {
+  uint32_t a = word & 0x7FFFu;
   a = max(a, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(a), 0x128, 0xF, 0xF, true)));  // row_ror:8
   a = max(a, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(a), 0x124, 0xF, 0xF, true)));  // row_ror:4
   a = max(a, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(a), 0x122, 0xF, 0xF, true)));  // row_ror:2
@@ -1255,18 +1264,20 @@ __device__ void packed_wg(f32x4 (&o)[8], float (&st)[kStatW], float (&m_o)[4], c
     // page ids of this tile and of the tiles issued this round, read with
     // the tile's LDS inputs
     const int id_cur = pid_at(it), id_1 = pid_at(it + 1), id_2 = pid_at(it + 2);
+    // every LDS input of the tile's scores is requested before the MFMAs
     ScoreIn<BITS> si;
     load_score_in<BITS>(si, slot, n16, gq);
+    u32x4 md[4];
+    load_tile_meta<BITS>(md, slot, gq);
+    const uint32_t hw = headroom_word<BITS>(slot, n16, gq);
     has = has && page_of_id(p, uniform(id_cur)) != nullptr;
     f32x4 acc[6];
     score_mfma<BITS>(acc, si, q, ro);
     float sc[4];
-    u32x4 md[4];
     km.rope = ro.mul;
-    score_finish<BITS>(sc, md, acc, slot, ro.bias, km, has, (t_lo + it) * kTile, sr.lo_p, sr.hi_p, gq);
+    score_finish<BITS>(sc, md, acc, ro.bias, km, has, (t_lo + it) * kTile, sr.lo_p, sr.hi_p, gq);
     if (r == 0 && it + 1 < my_end) issue(it + 1, uniform(id_1), 1);
-    const float tmax =
-        row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) + scale_headroom<BITS>(slot, n16, gq));
+    const float tmax = row_allmax(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) + scale_headroom(hw));
     if (gq == 0) smax[n16 * kWaves + wave] = tmax;
     lds_barrier();
 
