@@ -649,9 +649,9 @@ __device__ inline int p_entry(int kb, int g, int gq, int h) { return (((kb * 4 +
 // weights P'_g below never overflow, and the largest of a tile sits near
 // 2^14, far above the subnormal range, at any latent magnitude.  k >= -21
 // bounds p by 2^29, which fp32 sums hold.
-// Lane (n16, gq) reads the scale word of token 4 gq + n16 % 4, group n16 / 4,
-// and the row's 16 lanes take their maximum by rotations within the row.
-// (word: that scale word, loaded with the tile's score inputs)
+// Lane (n16, gq) reads the scale word of token 4 gq + n16 % 4, group n16 / 4
+// (with the tile's score inputs), and the row's 16 lanes take their maximum
+// by rotations within the row.
 template <int BITS>
 __device__ inline uint32_t headroom_word(const uint8_t* slot, int n16, int gq) {
   return lds_ld<uint32_t>(slot + TileGeom<BITS>::kOffMeta + 16 * (4 * gq + (n16 & 3)) + 4 * (n16 >> 2));
@@ -665,12 +665,9 @@ __device__ inline float scale_headroom(uint32_t word) {
   return static_cast<float>(a >> 10) - 21.f;
 }
 
-// Weights of this wave's packed tile: P'_g = fp16(p s_g / sigma) into the P'
-// entries its tokens fall in (tokens 4 gq + 2, 4 gq + 3 land in the output
-// unpack's sigma = 16 slots); adds this lane's sums of p and of p m_g (fp32)
-// to st.  Each weight is one v_fma_mix{lo,hi}_f16 (p s + 0 rounded to fp16),
-// with the scale taken as the fp16 low half of its metadata word and the pair
-// packed in one register.
+// Two fp16 weights in one register: p0 s0 and p1 s1 (+ 0), each one
+// v_fma_mix{lo,hi}_f16 rounded to fp16, with the scale s taken as the fp16 low
+// half of its metadata word w.
 __device__ inline uint32_t weight_pair(float p0, uint32_t w0, float p1, uint32_t w1) {
   uint32_t d;
   asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]\n\t"
@@ -680,6 +677,10 @@ __device__ inline uint32_t weight_pair(float p0, uint32_t w0, float p1, uint32_t
   return d;
 }
 
+// Weights of this wave's packed tile: P'_g = fp16(p s_g / sigma) into the P'
+// entries its tokens fall in (tokens 4 gq + 2, 4 gq + 3 land in the output
+// unpack's sigma = 16 slots); adds this lane's sums of p and of p m_g (fp32)
+// to st.
 __device__ inline void packed_weights(const float (&pr)[4], const u32x4 (&md)[4], uint8_t* pbase,
                                       float (&st)[kStatW], int wave, int n16, int gq) {
   st[0] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
