@@ -182,7 +182,8 @@ def test_transformed_writer_rejects_null_matrix(torch_cuda):
 
 
 def test_decode_edge_inputs(torch_cuda):
-    """Constant groups, all-zero tokens, bf16 subnormals and large outliers."""
+    """Constant groups, all-zero tokens, bf16 subnormals, large outliers and
+    codes on exact rounding ties."""
     torch = torch_cuda
     from bit_kv_cache_writer_amd import mla
     P, L = 64, 192
@@ -192,6 +193,15 @@ def test_decode_edge_inputs(torch_cuda):
     ckv[12, :128] = wl.f32_to_bf16_bits(np.full(128, -2.5, np.float32))
     ckv[13] = wl.f32_to_bf16_bits((np.arange(512) % 7 - 3).astype(np.float32) * 1e-39)
     ckv[14, 5] = wl.f32_to_bf16_bits(np.float32(3000.0))
+    # exact ties: groups whose step is 1 or 2 with values on the half-integers
+    # of the quotient (every code a round-half-to-even case, which the writer
+    # settles with the IEEE division), and a k_R channel of the first page
+    # likewise
+    half = np.concatenate([[0.0, 15.0], np.arange(0.5, 15.0, 1.0)])
+    tie = np.resize(half, 128).astype(np.float32)
+    ckv[15] = wl.f32_to_bf16_bits(np.concatenate([tie, 2.0 * tie, tie - 8.0, -2.0 * tie]))
+    ckv[16] = wl.f32_to_bf16_bits(np.concatenate([tie[::-1], tie, 0.25 * tie, tie + 0.5]))
+    kr[0:64, 9] = wl.f32_to_bf16_bits(np.resize(half, 64).astype(np.float32))
     kr[20:40, 3] = wl.f32_to_bf16_bits(np.float32(-0.0))
     for bits, clip in ((4, 0.0), (2, 0.94)):
         glay, olay = layouts(P, bits, clip, 2, 16)
