@@ -48,6 +48,7 @@ struct WriterParams {
   uint16_t* ring;
   uint16_t* tail;
   int32_t batch, total_new, max_pages, num_pool_pages, pages_per_seq_grid;
+  int32_t token_split;  // plain writer: workgroups per page (1, 2 or 4), tokens dealt between them
   int32_t P, bits, sink_n, local;
   int32_t clip, clip_lo, clip_hi;
   float clip_frac;
@@ -344,8 +345,11 @@ __device__ inline void transform_pass(float (&acc)[kWaves], const uint8_t* arow,
 template <int kMode>
 __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   constexpr bool kTransform = kMode != 0;
-  const int g = kMode == 2 ? static_cast<int>(blockIdx.x & 3u) : 0;
-  const int blk = kMode == 2 ? static_cast<int>(blockIdx.x >> 2) : static_cast<int>(blockIdx.x);
+  // kMode 2: latent group g of the page; kMode 0: token share g of
+  // p.token_split (share 0 also does the page's k_R work)
+  const int split = kMode == 2 ? 4 : (kMode == 0 ? p.token_split : 1);
+  const int g = static_cast<int>(blockIdx.x % static_cast<uint32_t>(split));
+  const int blk = static_cast<int>(blockIdx.x / static_cast<uint32_t>(split));
   const int b = blk / p.pages_per_seq_grid;
   const int pi = blk % p.pages_per_seq_grid;
   if (b >= p.batch) return;
@@ -387,7 +391,9 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   // this wave's first token goes out with them (its row index is clamped
   // into the input: a wave without a token reads a row it does not use)
   TokenRows cur{};
-  if constexpr (!kTransform) cur = load_token(p, r0 + (min(tb + wave, te - 1) - sb), lane);
+  // (kMode 0: this workgroup's tokens are tb + g kWaves + wave + k kWaves split)
+  const int t_first = tb + (kMode == 0 ? g * kWaves : 0) + wave, t_step = kWaves * (kMode == 0 ? split : 1);
+  if constexpr (!kTransform) cur = load_token(p, r0 + (min(t_first, te - 1) - sb), lane);
   const int page_id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pg];
   if (page_id < 0 || page_id >= p.num_pool_pages) {
     __syncthreads();  // no direct load outlives the workgroup
@@ -596,9 +602,9 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
     }
   } else {
     // Latent codes + metadata, BF16 sink / ring copies.
-    for (int t = tb + wave; t < te; t += kWaves) {
+    for (int t = t_first; t < te; t += t_step) {
       const TokenRows x = cur;
-      if (t + kWaves < te) cur = load_token(p, r0 + (t + kWaves - sb), lane);
+      if (t + t_step < te) cur = load_token(p, r0 + (t + t_step - sb), lane);
       write_latent_token(p, x.ckv, page, t - pg * P, lane);
       if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, x.ckv, x.kr, lane);
       if (p.local > 0 && t >= end - p.local)
@@ -763,9 +769,17 @@ int write_impl(const mla_lowbit_layout* layout, const void* a_c, const void* c_k
   // pages a call of n tokens can touch: (n - 1) / P + 2
   p.pages_per_seq_grid = (max_new_per_seq - 1) / g.page_size + 2;
   // with the transform and no clipping, four workgroups per page (one per
-  // latent group); the clip needs all 512 channels of a token in one wave
+  // latent group); the clip needs all 512 channels of a token in one wave.
+  // The plain writer deals a page's tokens to 2 or 4 workgroups when a call
+  // writes many tokens into few pages (chunked prefill of a few sequences),
+  // so that the chip holds more than one workgroup per CU.
   const bool split = a_c && !g.clip;
-  const int64_t blocks = static_cast<int64_t>(batch) * p.pages_per_seq_grid * (split ? 4 : 1);
+  p.token_split = 1;
+  if (!a_c && max_new_per_seq >= 4 * kWaves) {
+    const int64_t pages = static_cast<int64_t>(batch) * ((max_new_per_seq + g.page_size - 1) / g.page_size);
+    p.token_split = pages <= 256 ? 4 : (pages <= 512 ? 2 : 1);
+  }
+  const int64_t blocks = static_cast<int64_t>(batch) * p.pages_per_seq_grid * (split ? 4 : p.token_split);
   if (blocks > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
   if (split)
     hipLaunchKernelGGL(writer_kernel<2>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
