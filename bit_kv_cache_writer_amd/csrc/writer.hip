@@ -4,7 +4,10 @@
 // 0.94-quantile |x| clipping for the 2-bit latent, per-(channel, page) 4-bit
 // k_R with FP16 scale/min).
 //
-// One workgroup (8 waves) per (sequence, cache page touched by the call):
+// One workgroup (8 waves) per (sequence, cache page touched by the call), or
+// two / four per page when a call brings many tokens into few pages (a
+// page's tokens are then dealt to them in runs of 8, and the first one of a
+// page does all of its k_R and tail work below):
 //   * each wave quantizes whole latent tokens: lane l owns channels 8l..8l+7,
 //     so a 128-channel group is 16 lanes and its min/max is a 16-lane
 //     butterfly; codes are packed in registers and stored as one dword
