@@ -53,7 +53,7 @@ struct WriterParams {
   int32_t batch, total_new, max_pages, num_pool_pages, pages_per_seq_grid;
   int32_t token_split;  // plain writer: workgroups per page (1, 2 or 4), tokens dealt between them
   int32_t P, bits, sink_n, local;
-  int32_t clip, clip_lo, clip_hi;
+  int32_t clip_lo, clip_hi;
   float clip_frac;
   int64_t latent_row, latent_meta_off, rope_codes_off, rope_meta_off, page_bytes;
 };
@@ -131,14 +131,14 @@ __device__ inline float rint_div(float d, float s, float rcp_s) {
 __device__ inline uint32_t pack_codes(const float (&v)[8], float m, float s, float rcp_s, int bits, float levels) {
   const float rc = s > 0.0f ? rcp_s : 0.0f;
   float r[8];
-  bool near = false;
+  float dev = 0.0f;  // largest |qa - rint(qa)| of the 8 (a max3 chain)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float qa = (v[i] - m) * rc;
     r[i] = rintf(qa);
-    near |= fabsf(qa - r[i]) >= 0.49999f;
+    dev = fmaxf(dev, fabsf(qa - r[i]));
   }
-  if (__builtin_expect(near, 0)) {
+  if (__builtin_expect(dev >= 0.49999f, 0)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = rint_div(v[i] - m, s, rcp_s);
   }
@@ -199,29 +199,101 @@ __device__ inline float lanes_max_mod8(float v) {
   return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-// Number of the wave's 8 x 64 values a[i] with a[i] <= t (wave-uniform), by
-// ballots: one compare and one popcount per register, no cross-lane round trip.
-__device__ inline int wave_count_le(const uint32_t (&a)[8], uint32_t t) {
-  int c = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c += __popcll(__ballot(a[i] <= t));
-  return c;
+// Min / max over the whole wave: the row reduction of row_minmax16, then the
+// swaps of 16-lane rows and of 32-lane halves.
+__device__ inline int wave_min_i32(int v) {
+  v = min(v, dpp_key<0xB1>(v));
+  v = min(v, dpp_key<0x4E>(v));
+  v = min(v, dpp_key<0x124>(v));
+  v = min(v, dpp_key<0x128>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+  v = min(static_cast<int>(a[0]), static_cast<int>(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+  return min(static_cast<int>(c[0]), static_cast<int>(c[1]));
 }
-__device__ inline uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, 64)));
-  return v;
+__device__ inline int wave_max_i32(int v) {
+  v = max(v, dpp_key<0xB1>(v));
+  v = max(v, dpp_key<0x4E>(v));
+  v = max(v, dpp_key<0x124>(v));
+  v = max(v, dpp_key<0x128>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+  v = max(static_cast<int>(a[0]), static_cast<int>(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+  return max(static_cast<int>(c[0]), static_cast<int>(c[1]));
 }
 
-// k-th smallest (0-based) of the 512 |x| bit patterns held 8 per lane,
-// built bit by bit from the most significant one.
-__device__ inline uint32_t wave_kth_smallest(const uint32_t (&a)[8], int k) {
-  uint32_t prefix = 0;
-  for (int b = 14; b >= 0; --b) {
-    const uint32_t t = prefix | ((1u << b) - 1u);
-    if (wave_count_le(a, t) < k + 1) prefix |= 1u << b;
+// Sorts a lane's 8 keys into descending order with a 19-comparator network
+// of depth 6 (checked on all 256 zero-one inputs).
+__device__ inline void sort8_desc(uint32_t (&s)[8]) {
+  constexpr int kPairs[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6}, {3, 7}, {0, 1}, {2, 3},
+                                 {4, 5}, {6, 7}, {2, 4}, {3, 5}, {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+  for (int c = 0; c < 19; ++c) {
+    const uint32_t a = s[kPairs[c][0]], b = s[kPairs[c][1]];
+    s[kPairs[c][0]] = max(a, b);
+    s[kPairs[c][1]] = min(a, b);
   }
-  return prefix;
+}
+
+// Bisection for the smallest key v in [lo, hi] with fewer than `need`
+// (>= 1) of the wave's 512 keys above it (lo, hi wave-uniform and enclosing
+// that key).  Each probe counts the keys above mid with one ballot per
+// column of the lanes' sorted keys: column j's set of lanes is part of
+// column j - 1's, so an empty column ends the count (below need: hi = mid),
+// and so does the count reaching need (lo = mid + 1).  Per column: one
+// compare into a lane mask, its popcount (SCC: any lane set) and the
+// popcount taken from the remaining need - 1 (SCC: borrow, i.e. the count
+// reached need).  The interval shrinks on every probe, so the loop ends
+// after at most 15 probes.
+#define MLA_GT_COLUMN(J)                              \
+  "v_cmp_gt_u32_e64 %[m], %[s" #J "], %[mid]\n\t"     \
+  "s_bcnt1_i32_b64 %[pc], %[m]\n\t"                  \
+  "s_cbranch_scc0 .Lbelow%=\n\t"                     \
+  "s_sub_u32 %[r], %[r], %[pc]\n\t"                  \
+  "s_cbranch_scc1 .Labove%=\n\t"
+__device__ inline uint32_t wave_bisect_rank(const uint32_t (&s)[8], uint32_t lo, uint32_t hi, int need) {
+  const uint32_t need_m1 = static_cast<uint32_t>(need - 1);
+  uint32_t mid, pc, r;
+  uint64_t m;
+  asm volatile(".Lprobe%=:\n\t"
+               "s_cmp_lt_u32 %[lo], %[hi]\n\t"
+               "s_cbranch_scc0 .Ldone%=\n\t"
+               "s_add_u32 %[mid], %[lo], %[hi]\n\t"
+               "s_lshr_b32 %[mid], %[mid], 1\n\t"
+               "s_mov_b32 %[r], %[nm1]\n\t"
+               MLA_GT_COLUMN(0) MLA_GT_COLUMN(1) MLA_GT_COLUMN(2) MLA_GT_COLUMN(3)
+               MLA_GT_COLUMN(4) MLA_GT_COLUMN(5) MLA_GT_COLUMN(6) MLA_GT_COLUMN(7)
+               ".Lbelow%=:\n\t"
+               "s_mov_b32 %[hi], %[mid]\n\t"
+               "s_branch .Lprobe%=\n"
+               ".Labove%=:\n\t"
+               "s_add_u32 %[lo], %[mid], 1\n\t"
+               "s_branch .Lprobe%=\n"
+               ".Ldone%=:"
+               : [lo] "+s"(lo), [hi] "+s"(hi), [mid] "=&s"(mid), [pc] "=&s"(pc), [r] "=&s"(r), [m] "=&s"(m)
+               : [s0] "v"(s[0]), [s1] "v"(s[1]), [s2] "v"(s[2]), [s3] "v"(s[3]), [s4] "v"(s[4]),
+                 [s5] "v"(s[5]), [s6] "v"(s[6]), [s7] "v"(s[7]), [nm1] "s"(need_m1)
+               : "scc");
+  return lo;
+}
+#undef MLA_GT_COLUMN
+
+// k-th smallest (0-based) of the 512 keys, held 8 per lane in descending
+// order: the smallest v with fewer than 512 - k keys above it, by bisection
+// between two keys that enclose it.  Each lane holds j + 1 keys at or above
+// its column j, so with j = (511 - k) / 64 at least 512 - k keys lie at or
+// above the wave minimum of column j; the wave maximum bounds it above.
+__device__ inline uint32_t wave_kth_smallest(const uint32_t (&s)[8], int k) {
+  const int need = kLatentDim - k;
+  const int col = (need - 1) >> 6;
+  uint32_t sc = s[0];
+  if (col != 0) {
+#pragma unroll
+    for (int j = 1; j < 8; ++j) sc = col == j ? s[j] : sc;
+  }
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave_min_i32(static_cast<int>(sc))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave_max_i32(static_cast<int>(s[0]))));
+  return wave_bisect_rank(s, lo, hi, need);
 }
 
 // Quantizes one latent token (one wave; lane l holds channels 8l..8l+7), or,
@@ -229,6 +301,7 @@ __device__ inline uint32_t wave_kth_smallest(const uint32_t (&a)[8], int k) {
 // reductions stay inside each row, and col (= lane for whole tokens) is the
 // channel octet the lane holds, which places its codes and its group's
 // metadata word.
+template <bool kClip>
 __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8_t* page, int slot, int col) {
   const int lane = col;
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -238,29 +311,37 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
     x[2 * i] = canon_zero(bf16_to_f32(w[i] & 0xFFFFu));
     x[2 * i + 1] = canon_zero(bf16_to_f32(w[i] >> 16));
   }
-  if (p.clip) {
+  if constexpr (kClip) {
+    // |x| as 15-bit bf16 keys, each lane's sorted in descending order
     uint32_t a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = (__float_as_uint(x[i]) >> 16) & 0x7FFFu;
+    sort8_desc(a);
     const uint32_t lo = wave_kth_smallest(a, p.clip_lo);
-    const int c_le = wave_count_le(a, lo);
-    uint32_t above = 0xFFFFFFFFu;
+    // order statistic clip_hi: the smallest key above lo if at least
+    // 512 - clip_hi keys lie above lo, else lo itself.  The columns holding
+    // keys above lo come first (each column's lanes are part of the previous
+    // one's), so the first empty column ends the pass; a lane's smallest key
+    // above lo is the last of its sorted keys that is.
+    uint32_t above = 0x7FFFFFFFu;
+    int n_above = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (a[i] > lo) above = min(above, a[i]);
-    above = wave_min_u32(above);
-    const uint32_t hi = (c_le >= p.clip_hi + 1) ? lo : above;
+    for (int i = 0; i < 8; ++i) {
+      const uint64_t m = __ballot(a[i] > lo);
+      if (m == 0) break;
+      n_above += __popcll(m);
+      above = a[i] > lo ? a[i] : above;
+    }
+    uint32_t hi = lo;
+    if (n_above >= kLatentDim - p.clip_hi)
+      hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave_min_i32(static_cast<int>(above))));
     const float flo = bf16_to_f32(lo), fhi = bf16_to_f32(hi);
     const float d = fhi - flo;
     const float prod = p.clip_frac * d;
     const float c = flo + prod;
+    // clamp to [-c, c] (c >= 0); the sign of a zero result is normalized
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = x[i];
-      v = v < -c ? -c : v;
-      v = v > c ? c : v;
-      x[i] = canon_zero(v);
-    }
+    for (int i = 0; i < 8; ++i) x[i] = canon_zero(__builtin_amdgcn_fmed3f(x[i], -c, c));
   }
   float mn = x[0], mx = x[0];
 #pragma unroll
@@ -344,8 +425,9 @@ __device__ inline void transform_pass(float (&acc)[kWaves], const uint8_t* arow,
 
 // kMode 0: plain writer; 1: with the latent transform, one workgroup per
 // page; 2: with the latent transform, four workgroups per page (latent group
-// g = blockIdx.x % 4; no clipping).
-template <int kMode>
+// g = blockIdx.x % 4).  kClip: the INT2 latent's quantile clip (never with
+// kMode 2); a separate instantiation keeps its code out of the others.
+template <int kMode, bool kClip>
 __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   constexpr bool kTransform = kMode != 0;
   // kMode 2: latent group g of the page; kMode 0: token share g of
@@ -470,7 +552,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       if (wave == 0 && q < n) {
         const int t = t0 + q;
         const uint4 y = *reinterpret_cast<const uint4*>(&s_y[q][8 * l16]);
-        write_latent_token(p, y, page, t - pg * P, 16 * g + l16);
+        write_latent_token<false>(p, y, page, t - pg * P, 16 * g + l16);
         // this group's slice of the BF16 rows (the group-0 workgroup adds k_R)
         auto copy_slice = [&](uint16_t* dst) {
           reinterpret_cast<uint4*>(dst + kGroup * g)[l16] = y;
@@ -596,7 +678,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
         const int t = t0 + wave;
         const uint4 y = s_y[wave][lane];
         const uint4 kr = reinterpret_cast<const uint4*>(p.k_r + (r0 + (t - sb)) * static_cast<int64_t>(kRopeDim))[lane & 7];
-        write_latent_token(p, y, page, t - pg * P, lane);
+        write_latent_token<kClip>(p, y, page, t - pg * P, lane);
         if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, y, kr, lane);
         if (p.local > 0 && t >= end - p.local)
           copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, y, kr, lane);
@@ -608,7 +690,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
     for (int t = t_first; t < te; t += t_step) {
       const TokenRows x = cur;
       if (t + t_step < te) cur = load_token(p, r0 + (t + t_step - sb), lane);
-      write_latent_token(p, x.ckv, page, t - pg * P, lane);
+      write_latent_token<kClip>(p, x.ckv, page, t - pg * P, lane);
       if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, x.ckv, x.kr, lane);
       if (p.local > 0 && t >= end - p.local)
         copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, x.ckv, x.kr, lane);
@@ -760,7 +842,6 @@ int write_impl(const mla_lowbit_layout* layout, const void* a_c, const void* c_k
   p.bits = g.latent_bits;
   p.sink_n = g.sink;
   p.local = g.local;
-  p.clip = g.clip ? 1 : 0;
   p.clip_lo = g.clip_lo;
   p.clip_hi = g.clip_hi;
   p.clip_frac = g.clip_frac;
@@ -785,11 +866,13 @@ int write_impl(const mla_lowbit_layout* layout, const void* a_c, const void* c_k
   const int64_t blocks = static_cast<int64_t>(batch) * p.pages_per_seq_grid * (split ? 4 : p.token_split);
   if (blocks > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
   if (split)
-    hipLaunchKernelGGL(writer_kernel<2>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
-  else if (a_c)
-    hipLaunchKernelGGL(writer_kernel<1>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((writer_kernel<2, false>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  else if (a_c)  // with the transform only the clip keeps one workgroup per page
+    hipLaunchKernelGGL((writer_kernel<1, true>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  else if (g.clip)
+    hipLaunchKernelGGL((writer_kernel<0, true>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(writer_kernel<0>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((writer_kernel<0, false>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
 }
 

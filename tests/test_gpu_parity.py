@@ -221,6 +221,66 @@ def test_decode_edge_inputs(torch_cuda):
                        lse_slack=ref.lse_slack(ql, qr, 0.07))
 
 
+def _clip_rows(seed, n):
+    """Latent rows that stress the clip's order statistics: ties, constant
+    and all-zero rows, a single non-zero value, eight large values in one
+    lane's channels, wide exponent spreads, bf16 subnormals, two-valued and
+    all-negative rows, and plain Gaussian rows between them."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in range(n):
+        k = i % 12
+        x = rng.standard_normal(512)
+        if k == 1:
+            x = rng.integers(-3, 4, 512).astype(np.float64)
+        elif k == 2:
+            x = np.full(512, 1.5)
+        elif k == 3:
+            x = np.zeros(512)
+            x[rng.integers(0, 512)] = 2.0
+        elif k == 4:
+            x = np.zeros(512)
+        elif k == 5:
+            x[:8] *= 1000.0  # lane 0 holds all eight
+        elif k == 6:
+            x = rng.choice([-1.0, 1.0], 512) * 2.0 ** rng.integers(-40, 15, 512)
+        elif k == 7:
+            x = (np.arange(512) % 9 - 4) * 1e-39 + (rng.random(512) < 0.1) * rng.standard_normal(512)
+        elif k == 8:
+            x = np.where(rng.random(512) < 0.5, 0.75, -3.25)
+        elif k == 9:
+            x = -np.abs(x) * 40.0
+        elif k == 10:
+            x = np.linspace(-300.0, 300.0, 512)[rng.permutation(512)]
+        rows.append(x.astype(np.float32))
+    return wl.f32_to_bf16_bits(np.stack(rows))
+
+
+# quantiles whose search starts from columns 0, 1, 4, 5 and 7 of the lanes'
+# sorted keys (the lower rank's column), both ends, and the 4-bit latent
+CLIP_QS = [(2, 0.94), (2, 0.5), (2, 0.999), (2, 1e-4), (2, 1.0), (2, 0.87), (2, 0.3), (4, 0.94)]
+
+
+@pytest.mark.parametrize("bits,q", CLIP_QS, ids=[f"c{b}r4_q{q}" for b, q in CLIP_QS])
+def test_clip_order_statistics(torch_cuda, bits, q):
+    """The clip value of every token (and so its codes and metadata) is
+    bit-exact on rows built to break an order-statistic search."""
+    torch = torch_cuda
+    from bit_kv_cache_writer_amd import mla
+    P, L = 32, 80
+    _, kr = random_tokens(17, L)
+    ckv = _clip_rows(18, L)
+    glay, olay = layouts(P, bits, q, 2, 16)
+    bt, n_pool = perm_block_table(4, 1, 3)
+    gpu = mla.DeviceCache(glay, 1, 3, bt, n_pool)
+    ref = OracleCache(olay, 1, 3, bt, n_pool)
+    ref.append(ckv, kr, [L])
+    say("clip order statistics", bits, q)
+    gpu.append(_to_dev(torch, ckv), _to_dev(torch, kr), [L])
+    torch.cuda.synchronize()
+    compare_cache(gpu, ref)
+
+
 # --------------------------------------------------------------------------
 # the configurations at their full sizes, in the launch configuration the
 # benchmark times; sampled sequences (and, for the many-head ones, a subset
