@@ -73,41 +73,44 @@ __device__ inline uint32_t f32_to_bf16_rne(float x) {
 // nearest, x + 0 = x otherwise (one add; contraction is off in this file).
 __device__ inline float canon_zero(float x) { return x + 0.0f; }
 
-__device__ inline uint16_t f16_bits_rn(float x) {
-  _Float16 h = static_cast<_Float16>(x);  // v_cvt_f16_f32, round to nearest even
-  return __builtin_bit_cast(uint16_t, h);
-}
-
 __device__ inline float f16_to_f32(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-// An infinity (a finite input beyond the fp16 range) saturates to the largest
-// finite fp16 of its sign, so the metadata always stays finite.
-__device__ inline uint16_t f16_saturate(uint16_t h) {
-  return (h & 0x7FFFu) == 0x7C00u ? static_cast<uint16_t>((h & 0x8000u) | 0x7BFFu) : h;
+// fp16 bits of x rounded toward zero, zero-extended (v_cvt_pkrtz_f16_f32 of
+// x and +0: a finite x never becomes an infinity).
+__device__ inline uint32_t f16_bits_rz(float x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, 0.0f));
 }
 
-// Largest fp16 <= x (-65504 for x below it): round to nearest, then step one
-// ulp down if it went up.
+// Largest fp16 <= x (x not -0; -65504 for x below it): toward zero, then, for
+// a negative x that this moved up, one step away from zero (the bit pattern
+// plus one: -0 becomes the smallest negative subnormal, -65504 becomes -inf,
+// which the unsigned min takes back to -65504; no other pattern is above it).
 __device__ inline uint16_t f16_round_down(float x) {
-  uint16_t h = f16_bits_rn(x);
-  if (f16_to_f32(h) > x) {
-    if ((h & 0x7FFFu) == 0) h = 0x8001u;  // zero -> smallest negative subnormal
-    else h = (h & 0x8000u) ? h + 1 : h - 1;
-  }
-  return f16_saturate(h);
+  uint32_t h = f16_bits_rz(x);
+  if (f16_to_f32(static_cast<uint16_t>(h)) > x) ++h;
+  return static_cast<uint16_t>(min(h, 0xFBFFu));
 }
 
-// Smallest fp16 >= x (x >= 0 here; a zero result is +0; 65504 for x above it).
+// Smallest fp16 >= x (x >= 0, not -0; 65504 for x above it): toward zero,
+// then one step up if that moved down (65504 + 1 step is +inf, taken back
+// by the min).
 __device__ inline uint16_t f16_round_up(float x) {
-  uint16_t h = f16_bits_rn(x);
-  if (f16_to_f32(h) < x) {
-    if ((h & 0x7FFFu) == 0) h = 0x0001u;
-    else h = (h & 0x8000u) ? h - 1 : h + 1;
-    if (h == 0x8000u) h = 0;
-  }
-  return f16_saturate(h);
+  uint32_t h = f16_bits_rz(x);
+  if (f16_to_f32(static_cast<uint16_t>(h)) < x) ++h;
+  return static_cast<uint16_t>(min(h, 0x7BFFu));
+}
+
+// span / d, correctly rounded, for d = 3 or 15 (rd = rn(1 / d)) and
+// 0 <= span <= 2^20: the product with rd and one FMA correction of it give
+// the IEEE quotient for every fp32 span in that range (checked against the
+// division one by one).  Spans of in-range inputs stay below 2^18, and above
+// 15 * 65504 the scale saturates whatever the last bit.
+__device__ inline float div_levels(float span, float d, float rd) {
+  const float q0 = span * rd;
+  const float e = __builtin_fmaf(-q0, d, span);
+  return __builtin_fmaf(e, rd, q0);
 }
 
 // rint of the correctly rounded quotient d / s (d >= 0, s > 0, the quotient
@@ -305,11 +308,13 @@ template <bool kClip>
 __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8_t* page, int slot, int col) {
   const int lane = col;
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  // (a -0 among the values changes no code; the group's min and max are
+  // made +0 below)
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[2 * i] = canon_zero(bf16_to_f32(w[i] & 0xFFFFu));
-    x[2 * i + 1] = canon_zero(bf16_to_f32(w[i] >> 16));
+    x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
   if constexpr (kClip) {
     // |x| as 15-bit bf16 keys, each lane's sorted in descending order
@@ -339,9 +344,10 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
     const float d = fhi - flo;
     const float prod = p.clip_frac * d;
     const float c = flo + prod;
-    // clamp to [-c, c] (c >= 0); the sign of a zero result is normalized
+    // clamp to [-c, c] (c >= 0)
+    const float nc = -c;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = canon_zero(__builtin_amdgcn_fmed3f(x[i], -c, c));
+    for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_fmed3f(x[i], nc, c);
   }
   float mn = x[0], mx = x[0];
 #pragma unroll
@@ -350,11 +356,13 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
     mx = fmaxf(mx, x[i]);
   }
   row_minmax16(mn, mx);
+  mn = canon_zero(mn);
+  mx = canon_zero(mx);
   const int levels = (1 << p.bits) - 1;
   const uint16_t mh = f16_round_down(mn);
   const float minf = f16_to_f32(mh);
   const float span = mx - minf;
-  const float s = span / static_cast<float>(levels);
+  const float s = p.bits == 4 ? div_levels(span, 15.0f, 1.0f / 15.0f) : div_levels(span, 3.0f, 1.0f / 3.0f);
   const uint16_t sh = f16_round_up(s);
   const float sf = f16_to_f32(sh);
   const float rs = __builtin_amdgcn_rcpf(sf);
@@ -379,15 +387,22 @@ __device__ inline void copy_row(uint16_t* dst, const uint4 ckv, const uint4 kr, 
   if (lane < 8) reinterpret_cast<uint4*>(dst + kLatentDim)[lane] = kr;
 }
 
-// One token's rows as a wave holds them (see copy_row).
-struct TokenRows {
-  uint4 ckv, kr;
-};
-__device__ inline TokenRows load_token(const WriterParams& p, int64_t row, int lane) {
-  TokenRows r;
-  r.ckv = reinterpret_cast<const uint4*>(p.c_kv + row * kLatentDim)[lane];
-  r.kr = reinterpret_cast<const uint4*>(p.k_r + row * kRopeDim)[lane & 7];
-  return r;
+// One token's latent row as a wave holds it (see copy_row).
+__device__ inline uint4 load_latent(const WriterParams& p, int64_t row, int lane) {
+  return reinterpret_cast<const uint4*>(p.c_kv + row * kLatentDim)[lane];
+}
+
+// The BF16 copies of sequence b's token at position t (input row `row`,
+// latent bf16 row `ckv` as a wave holds it) in the sink and the window ring,
+// for a token that belongs there (end: the sequence length after the call);
+// its k_R row is read only then.
+__device__ inline void retain_token(const WriterParams& p, int b, int t, int end, int64_t row, const uint4 ckv,
+                                    int lane) {
+  const bool to_sink = t < p.sink_n, to_ring = p.local > 0 && t >= end - p.local;
+  if (!to_sink && !to_ring) return;
+  const uint4 kr = reinterpret_cast<const uint4*>(p.k_r + row * kRopeDim)[lane & 7];
+  if (to_sink) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, ckv, kr, lane);
+  if (to_ring) copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, ckv, kr, lane);
 }
 
 // Columns k0 .. k0 + 63 of the latent transform for N tokens: acc[w] of
@@ -428,7 +443,7 @@ __device__ inline void transform_pass(float (&acc)[kWaves], const uint8_t* arow,
 // g = blockIdx.x % 4).  kClip: the INT2 latent's quantile clip (never with
 // kMode 2); a separate instantiation keeps its code out of the others.
 template <int kMode, bool kClip>
-__global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMode == 0 ? 8 : 1))) writer_kernel(WriterParams p) {
   constexpr bool kTransform = kMode != 0;
   // kMode 2: latent group g of the page; kMode 0: token share g of
   // p.token_split (share 0 also does the page's k_R work)
@@ -451,7 +466,9 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   const int last_page = (end - 1) / P;
   if (last_page >= p.max_pages) return;  // positions beyond the block table
   const int tb = max(sb, pg * P), te = min(end, (pg + 1) * P);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (the wave index is the same in every lane: read from lane 0, it is a
+  // scalar, and so are the token indices and loop bounds derived from it)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint16_t* tail = p.tail + static_cast<int64_t>(b) * P * kRopeDim;
 
   // k_R rows of a page that becomes full in this call (tail buffer for tokens
@@ -475,10 +492,10 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
   }
   // this wave's first token goes out with them (its row index is clamped
   // into the input: a wave without a token reads a row it does not use)
-  TokenRows cur{};
+  uint4 cur{};
   // (kMode 0: this workgroup's tokens are tb + g kWaves + wave + k kWaves split)
   const int t_first = tb + (kMode == 0 ? g * kWaves : 0) + wave, t_step = kWaves * (kMode == 0 ? split : 1);
-  if constexpr (!kTransform) cur = load_token(p, r0 + (min(t_first, te - 1) - sb), lane);
+  if constexpr (!kTransform) cur = load_latent(p, r0 + (min(t_first, te - 1) - sb), lane);
   const int page_id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pg];
   if (page_id < 0 || page_id >= p.num_pool_pages) {
     __syncthreads();  // no direct load outlives the workgroup
@@ -677,23 +694,26 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       if (wave < n) {
         const int t = t0 + wave;
         const uint4 y = s_y[wave][lane];
-        const uint4 kr = reinterpret_cast<const uint4*>(p.k_r + (r0 + (t - sb)) * static_cast<int64_t>(kRopeDim))[lane & 7];
         write_latent_token<kClip>(p, y, page, t - pg * P, lane);
-        if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, y, kr, lane);
-        if (p.local > 0 && t >= end - p.local)
-          copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, y, kr, lane);
+        retain_token(p, b, t, end, r0 + (t - sb), y, lane);
       }
       lds_barrier();  // s_x and s_y are refilled for the next tokens
     }
   } else {
-    // Latent codes + metadata, BF16 sink / ring copies.
-    for (int t = t_first; t < te; t += t_step) {
-      const TokenRows x = cur;
-      if (t + t_step < te) cur = load_token(p, r0 + (t + t_step - sb), lane);
-      write_latent_token<kClip>(p, x.ckv, page, t - pg * P, lane);
-      if (t < p.sink_n) copy_row(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems, x.ckv, x.kr, lane);
-      if (p.local > 0 && t >= end - p.local)
-        copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, x.ckv, x.kr, lane);
+    // Latent codes + metadata, BF16 sink / ring copies.  Two tokens per trip,
+    // each loaded while the other is written (two register sets, no copies).
+    const auto token = [&](const uint4 x, int t) {
+      write_latent_token<kClip>(p, x, page, t - pg * P, lane);
+      retain_token(p, b, t, end, r0 + (t - sb), x, lane);
+    };
+    uint4 nxt{};
+    for (int t = t_first; t < te; t += 2 * t_step) {
+      const int t1 = t + t_step;
+      if (t1 < te) nxt = load_latent(p, r0 + (t1 - sb), lane);
+      token(cur, t);
+      if (t1 >= te) break;
+      if (t1 + t_step < te) cur = load_latent(p, r0 + (t1 + t_step - sb), lane);
+      token(nxt, t1);
     }
   }
 
@@ -717,7 +737,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = canon_zero(bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu));
+        const float v = bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu);
         mn[e] = fminf(mn[e], v);
         mx[e] = fmaxf(mx[e], v);
       }
@@ -743,10 +763,12 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
         cmn = fminf(cmn, s_min[w][c]);
         cmx = fmaxf(cmx, s_max[w][c]);
       }
+      cmn = canon_zero(cmn);
+      cmx = canon_zero(cmx);
       const uint16_t mh = f16_round_down(cmn);
       const float minf = f16_to_f32(mh);
       const float span = cmx - minf;
-      const float sc = span / 15.0f;
+      const float sc = div_levels(span, 15.0f, 1.0f / 15.0f);
       const uint16_t sh = f16_round_up(sc);
       s_minf[c] = minf;
       s_sf[c] = f16_to_f32(sh);
@@ -772,7 +794,7 @@ __global__ void __launch_bounds__(kThreads) writer_kernel(WriterParams p) {
       for (int e = 0; e < 8; ++e) {
         uint32_t code = 0;
         if (sf[e] > 0.0f) {
-          float r = rint_div(canon_zero(bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu)) - minf[e],
+          float r = rint_div(bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu) - minf[e],
                              sf[e], rsf[e]);
           r = fminf(fmaxf(r, 0.0f), 15.0f);
           code = static_cast<uint32_t>(r);
