@@ -225,18 +225,43 @@ __device__ inline int wave_max_i32(int v) {
   return max(static_cast<int>(c[0]), static_cast<int>(c[1]));
 }
 
-// Sorts a lane's 8 keys into descending order with a 19-comparator network
-// of depth 6 (checked on all 256 zero-one inputs).
-__device__ inline void sort8_desc(uint32_t (&s)[8]) {
-  constexpr int kPairs[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6}, {3, 7}, {0, 1}, {2, 3},
-                                 {4, 5}, {6, 7}, {2, 4}, {3, 5}, {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
-#pragma unroll
-  for (int c = 0; c < 19; ++c) {
-    const uint32_t a = s[kPairs[c][0]], b = s[kPairs[c][1]];
-    s[kPairs[c][0]] = max(a, b);
-    s[kPairs[c][1]] = min(a, b);
-  }
+// A lane's 8 clip keys, two per dword: 15-bit keys (|x| as bf16 bits), so
+// that each packed 16-bit min / max handles two of them.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline void ce_u16x2(u16x2& a, u16x2& b) {
+  const u16x2 hi = __builtin_elementwise_max(a, b), lo = __builtin_elementwise_min(a, b);
+  a = hi;
+  b = lo;
 }
+
+// Sorts a lane's 8 keys into descending order: column j (0..7) is the low
+// half of u[j] for j < 4, the high half of u[j - 4] otherwise.  The low and
+// the high halves are first sorted each on their own (one 5-comparator
+// network running on both), then merged by one bitonic step (each low key
+// against the high keys in reverse order: the larger four and the smaller
+// four), and both fours are finished by a bitonic half-cleaner, again side by
+// side.  (Checked on all 256 zero-one inputs and on random inputs with ties.)
+__device__ inline void sort8_packed(u16x2 (&u)[4]) {
+  ce_u16x2(u[0], u[1]);
+  ce_u16x2(u[2], u[3]);
+  ce_u16x2(u[0], u[2]);
+  ce_u16x2(u[1], u[3]);
+  ce_u16x2(u[1], u[2]);
+  const u16x2 r3 = u[3].yx, r2 = u[2].yx;
+  const u16x2 m0 = __builtin_elementwise_max(u[0], r3), n0 = __builtin_elementwise_min(u[0], r3);
+  const u16x2 m1 = __builtin_elementwise_max(u[1], r2), n1 = __builtin_elementwise_min(u[1], r2);
+  u[0] = __builtin_shufflevector(m0, n0, 0, 2);
+  u[1] = __builtin_shufflevector(m1, n1, 0, 2);
+  u[2] = __builtin_shufflevector(m1, n1, 1, 3);
+  u[3] = __builtin_shufflevector(m0, n0, 1, 3);
+  ce_u16x2(u[0], u[2]);
+  ce_u16x2(u[1], u[3]);
+  ce_u16x2(u[0], u[1]);
+  ce_u16x2(u[2], u[3]);
+}
+__device__ inline uint32_t key_column(const u16x2 (&u)[4], int j) { return j < 4 ? u[j].x : u[j - 4].y; }
+__device__ inline uint32_t packed_bits(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
 // Bisection for the smallest key v in [lo, hi] with fewer than `need`
 // (>= 1) of the wave's 512 keys above it (lo, hi wave-uniform and enclosing
@@ -244,28 +269,33 @@ __device__ inline void sort8_desc(uint32_t (&s)[8]) {
 // column of the lanes' sorted keys: column j's set of lanes is part of
 // column j - 1's, so an empty column ends the count (below need: hi = mid),
 // and so does the count reaching need (lo = mid + 1).  Per column: one
-// compare into a lane mask, its popcount (SCC: any lane set) and the
-// popcount taken from the remaining need - 1 (SCC: borrow, i.e. the count
-// reached need).  The interval shrinks on every probe, so the loop ends
-// after at most 15 probes.
-#define MLA_GT_COLUMN(J)                              \
-  "v_cmp_gt_u32_e64 %[m], %[s" #J "], %[mid]\n\t"     \
+// compare into a lane mask (a 16-bit compare for a low half; for a high half
+// the dword against mid * 2^16 + 0xFFFF), its popcount (SCC: any lane set)
+// and the popcount taken from the remaining need - 1 (SCC: borrow, i.e. the
+// count reached need).  The interval shrinks on every probe, so the loop
+// ends after at most 15 probes.
+#define MLA_GT_COLUMN(OP, J, T)                       \
+  OP " %[m], %[u" #J "], %[" T "]\n\t"                \
   "s_bcnt1_i32_b64 %[pc], %[m]\n\t"                  \
   "s_cbranch_scc0 .Lbelow%=\n\t"                     \
   "s_sub_u32 %[r], %[r], %[pc]\n\t"                  \
   "s_cbranch_scc1 .Labove%=\n\t"
-__device__ inline uint32_t wave_bisect_rank(const uint32_t (&s)[8], uint32_t lo, uint32_t hi, int need) {
+#define MLA_GT_LOW(J) MLA_GT_COLUMN("v_cmp_gt_u16_e64", J, "mid")
+#define MLA_GT_HIGH(J) MLA_GT_COLUMN("v_cmp_gt_u32_e64", J, "midh")
+__device__ inline uint32_t wave_bisect_rank(const u16x2 (&u)[4], uint32_t lo, uint32_t hi, int need) {
   const uint32_t need_m1 = static_cast<uint32_t>(need - 1);
-  uint32_t mid, pc, r;
+  uint32_t mid, midh, pc, r;
   uint64_t m;
   asm volatile(".Lprobe%=:\n\t"
                "s_cmp_lt_u32 %[lo], %[hi]\n\t"
                "s_cbranch_scc0 .Ldone%=\n\t"
                "s_add_u32 %[mid], %[lo], %[hi]\n\t"
                "s_lshr_b32 %[mid], %[mid], 1\n\t"
+               "s_lshl_b32 %[midh], %[mid], 16\n\t"
+               "s_or_b32 %[midh], %[midh], 0xffff\n\t"
                "s_mov_b32 %[r], %[nm1]\n\t"
-               MLA_GT_COLUMN(0) MLA_GT_COLUMN(1) MLA_GT_COLUMN(2) MLA_GT_COLUMN(3)
-               MLA_GT_COLUMN(4) MLA_GT_COLUMN(5) MLA_GT_COLUMN(6) MLA_GT_COLUMN(7)
+               MLA_GT_LOW(0) MLA_GT_LOW(1) MLA_GT_LOW(2) MLA_GT_LOW(3)
+               MLA_GT_HIGH(0) MLA_GT_HIGH(1) MLA_GT_HIGH(2) MLA_GT_HIGH(3)
                ".Lbelow%=:\n\t"
                "s_mov_b32 %[hi], %[mid]\n\t"
                "s_branch .Lprobe%=\n"
@@ -273,12 +303,15 @@ __device__ inline uint32_t wave_bisect_rank(const uint32_t (&s)[8], uint32_t lo,
                "s_add_u32 %[lo], %[mid], 1\n\t"
                "s_branch .Lprobe%=\n"
                ".Ldone%=:"
-               : [lo] "+s"(lo), [hi] "+s"(hi), [mid] "=&s"(mid), [pc] "=&s"(pc), [r] "=&s"(r), [m] "=&s"(m)
-               : [s0] "v"(s[0]), [s1] "v"(s[1]), [s2] "v"(s[2]), [s3] "v"(s[3]), [s4] "v"(s[4]),
-                 [s5] "v"(s[5]), [s6] "v"(s[6]), [s7] "v"(s[7]), [nm1] "s"(need_m1)
+               : [lo] "+s"(lo), [hi] "+s"(hi), [mid] "=&s"(mid), [midh] "=&s"(midh), [pc] "=&s"(pc), [r] "=&s"(r),
+                 [m] "=&s"(m)
+               : [u0] "v"(packed_bits(u[0])), [u1] "v"(packed_bits(u[1])), [u2] "v"(packed_bits(u[2])),
+                 [u3] "v"(packed_bits(u[3])), [nm1] "s"(need_m1)
                : "scc");
   return lo;
 }
+#undef MLA_GT_HIGH
+#undef MLA_GT_LOW
 #undef MLA_GT_COLUMN
 
 // k-th smallest (0-based) of the 512 keys, held 8 per lane in descending
@@ -286,17 +319,18 @@ __device__ inline uint32_t wave_bisect_rank(const uint32_t (&s)[8], uint32_t lo,
 // between two keys that enclose it.  Each lane holds j + 1 keys at or above
 // its column j, so with j = (511 - k) / 64 at least 512 - k keys lie at or
 // above the wave minimum of column j; the wave maximum bounds it above.
-__device__ inline uint32_t wave_kth_smallest(const uint32_t (&s)[8], int k) {
+__device__ inline uint32_t wave_kth_smallest(const u16x2 (&u)[4], int k) {
   const int need = kLatentDim - k;
   const int col = (need - 1) >> 6;
-  uint32_t sc = s[0];
+  uint32_t sc = u[0].x;
   if (col != 0) {
 #pragma unroll
-    for (int j = 1; j < 8; ++j) sc = col == j ? s[j] : sc;
+    for (int j = 1; j < 8; ++j) sc = col == j ? key_column(u, j) : sc;
   }
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave_min_i32(static_cast<int>(sc))));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave_max_i32(static_cast<int>(s[0]))));
-  return wave_bisect_rank(s, lo, hi, need);
+  const uint32_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave_max_i32(static_cast<int>(u[0].x))));
+  return wave_bisect_rank(u, lo, hi, need);
 }
 
 // Quantizes one latent token (one wave; lane l holds channels 8l..8l+7), or,
@@ -317,12 +351,13 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
     x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
   if constexpr (kClip) {
-    // |x| as 15-bit bf16 keys, each lane's sorted in descending order
-    uint32_t a[8];
+    // |x| as 15-bit bf16 keys (the input words with their sign bits
+    // cleared), each lane's sorted in descending order
+    u16x2 u[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = (__float_as_uint(x[i]) >> 16) & 0x7FFFu;
-    sort8_desc(a);
-    const uint32_t lo = wave_kth_smallest(a, p.clip_lo);
+    for (int i = 0; i < 4; ++i) u[i] = __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu);
+    sort8_packed(u);
+    const uint32_t lo = wave_kth_smallest(u, p.clip_lo);
     // order statistic clip_hi: the smallest key above lo if at least
     // 512 - clip_hi keys lie above lo, else lo itself.  The columns holding
     // keys above lo come first (each column's lanes are part of the previous
@@ -331,11 +366,12 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
     uint32_t above = 0x7FFFFFFFu;
     int n_above = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint64_t m = __ballot(a[i] > lo);
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t key = key_column(u, j);
+      const uint64_t m = __ballot(key > lo);
       if (m == 0) break;
       n_above += __popcll(m);
-      above = a[i] > lo ? a[i] : above;
+      above = key > lo ? key : above;
     }
     uint32_t hi = lo;
     if (n_above >= kLatentDim - p.clip_hi)
