@@ -152,11 +152,6 @@ __device__ inline uint32_t pack_codes(const float (&v)[8], float m, float s, flo
   return packed;
 }
 
-// A DPP lane move within 16-lane rows.
-template <int kCtrl>
-__device__ inline float dpp_move(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
 // Min and max over each 16-lane row by DPP lane moves (VALU, no LDS round
 // trip): swap neighbours, swap pairs, then rotate the row by 4 and by 8.  They
 // run on order-preserving integer keys of the floats (negative values get
@@ -185,21 +180,33 @@ __device__ inline void row_minmax16(float& mn, float& mx) {
   mn = key_f32(a);
   mx = key_f32(b);
 }
-// Min / max over lanes l, l ^ 8, l ^ 16, ... (the 8 lanes of equal l % 8):
-// a DPP row rotation by 8, then the row-swap permutes across 16 and 32 lanes.
-__device__ inline float lanes_min_mod8(float v) {
-  v = fminf(v, dpp_move<0x128>(v));
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fminf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+// Packed signed 16-bit pairs, reduced over the whole wave per half: DPP lane
+// moves within 16-lane rows, then the swaps of rows and of 32-lane halves.
+// (The swapped dwords are taken out as plain 32-bit values before they are
+// reinterpreted: a bit cast straight from an element of the returned pair
+// reads the first element.)
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+template <int kCtrl>
+__device__ inline i16x2 dpp_i16x2(i16x2 v) {
+  return __builtin_bit_cast(i16x2, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
 }
-__device__ inline float lanes_max_mod8(float v) {
-  v = fmaxf(v, dpp_move<0x128>(v));
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+template <bool kMax>
+__device__ inline i16x2 pick(i16x2 a, i16x2 b) {
+  return kMax ? __builtin_elementwise_max(a, b) : __builtin_elementwise_min(a, b);
+}
+template <bool kMax>
+__device__ inline i16x2 wave_reduce_i16x2(i16x2 v) {
+  v = pick<kMax>(v, dpp_i16x2<0xB1>(v));
+  v = pick<kMax>(v, dpp_i16x2<0x4E>(v));
+  v = pick<kMax>(v, dpp_i16x2<0x124>(v));
+  v = pick<kMax>(v, dpp_i16x2<0x128>(v));
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  u = __builtin_bit_cast(uint32_t, pick<kMax>(__builtin_bit_cast(i16x2, a0), __builtin_bit_cast(i16x2, a1)));
+  const auto c = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t c0 = c[0], c1 = c[1];
+  return pick<kMax>(__builtin_bit_cast(i16x2, c0), __builtin_bit_cast(i16x2, c1));
 }
 
 // Min / max over the whole wave: the row reduction of row_minmax16, then the
@@ -511,14 +518,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
   // of earlier calls, input rows for new ones) go straight from global memory
   // into LDS, all at once (16 bytes per lane and load), before the page id is
   // looked up: they do not depend on it.  The barrier before their reduction
-  // waits for them.
+  // waits for them.  Row s's channel octet q sits in 16-byte unit
+  // 8 s + (q ^ (s % 8)), so that a wave reading one octet of 64 rows (a row
+  // per lane) spreads over every bank.
   __shared__ uint4 s_rows[256 * kRopeDim / 8];  // P x 64 bf16
   const bool completes = g == 0 && (pg + 1) * P <= end;  // (the group-0 workgroup does the k_R work)
   if (completes) {
     for (int k = 0; k * kThreads < P * (kRopeDim / 8); ++k) {
       const int i = static_cast<int>(threadIdx.x) + k * kThreads;
       if (k * kThreads + 64 * wave >= P * (kRopeDim / 8)) break;  // whole waves (P * 8 is a multiple of 256)
-      const int slot = i >> 3, q = i & 7;
+      const int slot = i >> 3, q = (i & 7) ^ (slot & 7);
       const int t = pg * P + slot;
       const uint4* src = t < sb ? reinterpret_cast<const uint4*>(tail + static_cast<int64_t>(slot) * kRopeDim) + q
                                 : reinterpret_cast<const uint4*>(p.k_r + (r0 + (t - sb)) * static_cast<int64_t>(kRopeDim)) + q;
@@ -753,91 +762,100 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
     }
   }
 
-  // k_R of a page that becomes full: per channel over its P tokens.  Thread
-  // (part, octet q) takes channels 8q .. 8q + 7 of rows part, part + 32, ...
-  // (16-byte LDS reads); the 8 parts of a wave meet by lane moves, the four
-  // waves in LDS.
-  __shared__ float s_min[kWaves][kRopeDim], s_max[kWaves][kRopeDim];
-  __shared__ float s_minf[kRopeDim], s_sf[kRopeDim];
+  // k_R of a page that becomes full: per channel over its P tokens.  Wave w
+  // takes channels 8w .. 8w + 7 (octet w) of rows lane, lane + 64, ...: the
+  // octet's minimum and maximum are reduced inside the wave as packed 16-bit
+  // order keys of the bf16 values (two channels per dword), lanes 0..7 form
+  // one channel's metadata each, and every lane then codes its rows' octet
+  // (one dword: row s, channels 8w .. 8w + 7 is dword 8 s + w).  No data
+  // crosses waves, so one barrier (the rows in LDS) is all it takes.
   if (completes) {
     __syncthreads();
-    const int q = threadIdx.x & 7, part = threadIdx.x >> 3;
-    float mn[8], mx[8];
+    const int q = wave;
+    const int rows_per_lane = (P + 63) >> 6;
+    // order keys: a bf16 b as a signed 16-bit k = b, or b ^ 0x7FFF for a
+    // negative b (the map is its own inverse; -0 sorts just below +0)
+    const auto keys = [](uint32_t w) {
+      const i16x2 neg = __builtin_bit_cast(i16x2, w) >> i16x2{15, 15};  // -1 in a negative half
+      return w ^ (__builtin_bit_cast(uint32_t, neg) & 0x7FFF7FFFu);
+    };
+    i16x2 kmn[4], kmx[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      mn[e] = 3.0e38f;
-      mx[e] = -3.0e38f;
+    for (int d = 0; d < 4; ++d) {
+      kmn[d] = i16x2{0x7FFF, 0x7FFF};
+      kmx[d] = i16x2{-0x8000, -0x8000};
     }
-    for (int s = part; s < P; s += kThreads / 8) {
-      const uint4 w = s_rows[s * (kRopeDim / 8) + q];
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int k = 0; k < rows_per_lane; ++k) {
+      const int s = lane + 64 * k;
+      if (s < P) {
+        const uint4 w = s_rows[s * 8 + (q ^ (s & 7))];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu);
-        mn[e] = fminf(mn[e], v);
-        mx[e] = fmaxf(mx[e], v);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      mn[e] = lanes_min_mod8(mn[e]);
-      mx[e] = lanes_max_mod8(mx[e]);
-    }
-    if (lane < 8) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s_min[wave][8 * q + e] = mn[e];
-        s_max[wave][8 * q + e] = mx[e];
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x < kRopeDim) {
-      const int c = threadIdx.x;
-      float cmn = s_min[0][c], cmx = s_max[0][c];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) {
-        cmn = fminf(cmn, s_min[w][c]);
-        cmx = fmaxf(cmx, s_max[w][c]);
-      }
-      cmn = canon_zero(cmn);
-      cmx = canon_zero(cmx);
-      const uint16_t mh = f16_round_down(cmn);
-      const float minf = f16_to_f32(mh);
-      const float span = cmx - minf;
-      const float sc = div_levels(span, 15.0f, 1.0f / 15.0f);
-      const uint16_t sh = f16_round_up(sc);
-      s_minf[c] = minf;
-      s_sf[c] = f16_to_f32(sh);
-      uint16_t* meta = reinterpret_cast<uint16_t*>(page + p.rope_meta_off);
-      meta[c] = sh;
-      meta[kRopeDim + c] = mh;
-    }
-    __syncthreads();
-    // codes, packed as they are made: dword i = row i / 8, channels 8 (i % 8) .. + 7
-    float minf[8], sf[8], rsf[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      minf[e] = s_minf[8 * q + e];
-      sf[e] = s_sf[8 * q + e];
-      rsf[e] = __builtin_amdgcn_rcpf(sf[e]);
-    }
-    uint32_t* rc = reinterpret_cast<uint32_t*>(page + p.rope_codes_off);
-    for (int s = part; s < P; s += kThreads / 8) {
-      const uint4 w = s_rows[s * (kRopeDim / 8) + q];
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-      uint32_t packed = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t code = 0;
-        if (sf[e] > 0.0f) {
-          float r = rint_div(bf16_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu) - minf[e],
-                             sf[e], rsf[e]);
-          r = fminf(fmaxf(r, 0.0f), 15.0f);
-          code = static_cast<uint32_t>(r);
+        for (int d = 0; d < 4; ++d) {
+          const i16x2 kk = __builtin_bit_cast(i16x2, keys(ww[d]));
+          kmn[d] = __builtin_elementwise_min(kmn[d], kk);
+          kmx[d] = __builtin_elementwise_max(kmx[d], kk);
         }
-        packed |= code << (4 * e);
       }
-      rc[s * (kRopeDim / 8) + q] = packed;
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      kmn[d] = wave_reduce_i16x2<false>(kmn[d]);
+      kmx[d] = wave_reduce_i16x2<true>(kmx[d]);
+    }
+    // lane e < 8: channel 8q + e
+    const int e = lane & 7;
+    const uint32_t pmn = __builtin_bit_cast(uint32_t, e < 2 ? kmn[0] : e < 4 ? kmn[1] : e < 6 ? kmn[2] : kmn[3]);
+    const uint32_t pmx = __builtin_bit_cast(uint32_t, e < 2 ? kmx[0] : e < 4 ? kmx[1] : e < 6 ? kmx[2] : kmx[3]);
+    const uint32_t bmn = keys((e & 1) ? pmn >> 16 : pmn & 0xFFFFu) & 0xFFFFu;
+    const uint32_t bmx = keys((e & 1) ? pmx >> 16 : pmx & 0xFFFFu) & 0xFFFFu;
+    const float cmn = canon_zero(bf16_to_f32(bmn)), cmx = canon_zero(bf16_to_f32(bmx));
+    const uint16_t mh = f16_round_down(cmn);
+    const float minf = f16_to_f32(mh);
+    const float span = cmx - minf;
+    const uint16_t sh = f16_round_up(div_levels(span, 15.0f, 1.0f / 15.0f));
+    const float sf = f16_to_f32(sh);
+    if (lane < 8) {
+      uint16_t* meta = reinterpret_cast<uint16_t*>(page + p.rope_meta_off);
+      meta[8 * q + lane] = sh;
+      meta[kRopeDim + 8 * q + lane] = mh;
+    }
+    // every lane gets the octet's offsets, steps and reciprocals (0 for a
+    // zero step: its codes are 0)
+    float mo[8], so[8], ro[8];
+    const float rc = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      mo[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, minf), c));
+      so[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sf), c));
+      ro[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rc), c));
+    }
+    uint32_t* const codes = reinterpret_cast<uint32_t*>(page + p.rope_codes_off);
+    for (int k = 0; k < rows_per_lane; ++k) {
+      const int s = lane + 64 * k;
+      if (s < P) {
+        const uint4 w = s_rows[s * 8 + (q ^ (s & 7))];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        float d[8], r[8];
+        float dev = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          d[c] = bf16_to_f32((c & 1) ? ww[c >> 1] >> 16 : ww[c >> 1] & 0xFFFFu) - mo[c];
+          const float qa = d[c] * ro[c];
+          r[c] = rintf(qa);
+          dev = fmaxf(dev, fabsf(qa - r[c]));
+        }
+        if (__builtin_expect(dev >= 0.49999f, 0)) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            if (so[c] > 0.0f) r[c] = rint_div(d[c], so[c], ro[c]);
+        }
+        uint32_t packed = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          packed |= static_cast<uint32_t>(__builtin_amdgcn_fmed3f(r[c], 0.0f, 15.0f)) << (4 * c);
+        codes[s * 8 + q] = packed;
+      }
     }
   }
 
