@@ -272,37 +272,39 @@ __device__ inline uint32_t packed_bits(u16x2 v) { return __builtin_bit_cast(uint
 
 // Bisection for the smallest key v in [lo, hi] with fewer than `need`
 // (>= 1) of the wave's 512 keys above it (lo, hi wave-uniform and enclosing
-// that key).  Each probe counts the keys above mid with one ballot per
-// column of the lanes' sorted keys: column j's set of lanes is part of
-// column j - 1's, so an empty column ends the count (below need: hi = mid),
-// and so does the count reaching need (lo = mid + 1).  Per column: one
-// compare into a lane mask (a 16-bit compare for a low half; for a high half
-// the dword against mid * 2^16 + 0xFFFF), its popcount (SCC: any lane set)
-// and the popcount taken from the remaining need - 1 (SCC: borrow, i.e. the
-// count reached need).  The interval shrinks on every probe, so the loop
-// ends after at most 15 probes.
-#define MLA_GT_COLUMN(OP, J, T)                       \
-  OP " %[m], %[u" #J "], %[" T "]\n\t"                \
+// that key, hi the wave maximum of column 0).  Each probe counts the keys
+// above mid with one ballot per column of the lanes' sorted keys: column j's
+// set of lanes is part of column j - 1's, so an empty column ends the count
+// (below need: hi = mid), and so does the count reaching need (lo = mid + 1).
+// Column 0 is never empty (mid < hi <= its maximum).  Per column: a 16-bit
+// compare into a lane mask (low halves of u, then of uh = u >> 16), its
+// popcount (SCC: any lane set) and the popcount taken from the remaining
+// need - 1 (SCC: borrow, i.e. the count reached need).  The interval shrinks
+// on every probe, so the loop ends after at most 15 probes.
+#define MLA_GT_COLUMN(V)                              \
+  "v_cmp_gt_u16_e64 %[m], %[" V "], %[mid]\n\t"        \
   "s_bcnt1_i32_b64 %[pc], %[m]\n\t"                  \
   "s_cbranch_scc0 .Lbelow%=\n\t"                     \
   "s_sub_u32 %[r], %[r], %[pc]\n\t"                  \
   "s_cbranch_scc1 .Labove%=\n\t"
-#define MLA_GT_LOW(J) MLA_GT_COLUMN("v_cmp_gt_u16_e64", J, "mid")
-#define MLA_GT_HIGH(J) MLA_GT_COLUMN("v_cmp_gt_u32_e64", J, "midh")
 __device__ inline uint32_t wave_bisect_rank(const u16x2 (&u)[4], uint32_t lo, uint32_t hi, int need) {
   const uint32_t need_m1 = static_cast<uint32_t>(need - 1);
-  uint32_t mid, midh, pc, r;
+  uint32_t uh[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) uh[j] = u[j].y;
+  uint32_t mid, pc, r;
   uint64_t m;
   asm volatile(".Lprobe%=:\n\t"
                "s_cmp_lt_u32 %[lo], %[hi]\n\t"
                "s_cbranch_scc0 .Ldone%=\n\t"
                "s_add_u32 %[mid], %[lo], %[hi]\n\t"
                "s_lshr_b32 %[mid], %[mid], 1\n\t"
-               "s_lshl_b32 %[midh], %[mid], 16\n\t"
-               "s_or_b32 %[midh], %[midh], 0xffff\n\t"
-               "s_mov_b32 %[r], %[nm1]\n\t"
-               MLA_GT_LOW(0) MLA_GT_LOW(1) MLA_GT_LOW(2) MLA_GT_LOW(3)
-               MLA_GT_HIGH(0) MLA_GT_HIGH(1) MLA_GT_HIGH(2) MLA_GT_HIGH(3)
+               "v_cmp_gt_u16_e64 %[m], %[u0], %[mid]\n\t"
+               "s_bcnt1_i32_b64 %[pc], %[m]\n\t"
+               "s_sub_u32 %[r], %[nm1], %[pc]\n\t"
+               "s_cbranch_scc1 .Labove%=\n\t"
+               MLA_GT_COLUMN("u1") MLA_GT_COLUMN("u2") MLA_GT_COLUMN("u3")
+               MLA_GT_COLUMN("h0") MLA_GT_COLUMN("h1") MLA_GT_COLUMN("h2") MLA_GT_COLUMN("h3")
                ".Lbelow%=:\n\t"
                "s_mov_b32 %[hi], %[mid]\n\t"
                "s_branch .Lprobe%=\n"
@@ -310,15 +312,13 @@ __device__ inline uint32_t wave_bisect_rank(const u16x2 (&u)[4], uint32_t lo, ui
                "s_add_u32 %[lo], %[mid], 1\n\t"
                "s_branch .Lprobe%=\n"
                ".Ldone%=:"
-               : [lo] "+s"(lo), [hi] "+s"(hi), [mid] "=&s"(mid), [midh] "=&s"(midh), [pc] "=&s"(pc), [r] "=&s"(r),
-                 [m] "=&s"(m)
+               : [lo] "+s"(lo), [hi] "+s"(hi), [mid] "=&s"(mid), [pc] "=&s"(pc), [r] "=&s"(r), [m] "=&s"(m)
                : [u0] "v"(packed_bits(u[0])), [u1] "v"(packed_bits(u[1])), [u2] "v"(packed_bits(u[2])),
-                 [u3] "v"(packed_bits(u[3])), [nm1] "s"(need_m1)
+                 [u3] "v"(packed_bits(u[3])), [h0] "v"(uh[0]), [h1] "v"(uh[1]), [h2] "v"(uh[2]), [h3] "v"(uh[3]),
+                 [nm1] "s"(need_m1)
                : "scc");
   return lo;
 }
-#undef MLA_GT_HIGH
-#undef MLA_GT_LOW
 #undef MLA_GT_COLUMN
 
 // k-th smallest (0-based) of the 512 keys, held 8 per lane in descending
