@@ -125,6 +125,20 @@ __device__ inline float rint_div(float d, float s, float rcp_s) {
   return r;
 }
 
+// Eight 4-bit codes (integer-valued floats in [0, 15]) packed, code i in
+// bits 4i .. 4i + 3: the even codes go to the bytes of one dword and the odd
+// ones to another by v_cvt_pk_u8_f32 (exact for integers), then one shift-or
+// interleaves them.
+__device__ inline uint32_t pack_nibbles(const float (&c)[8]) {
+  uint32_t even = 0, odd = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    even = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * k], k, even);
+    odd = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * k + 1], k, odd);
+  }
+  return even | (odd << 4);
+}
+
 // Codes of 8 values v[i] with offset m and step s: for s > 0 the same codes
 // as min(max(rint_div(v - m, s), 0), levels); s = 0 gives 0 (the reciprocal
 // is replaced by 0, so every quotient is 0).  The fast quotient is checked
@@ -145,10 +159,13 @@ __device__ inline uint32_t pack_codes(const float (&v)[8], float m, float s, flo
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = rint_div(v[i] - m, s, rcp_s);
   }
+  float c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(r[i], 0.0f, levels);
+  if (bits == 4) return pack_nibbles(c);
   uint32_t packed = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    packed |= static_cast<uint32_t>(__builtin_amdgcn_fmed3f(r[i], 0.0f, levels)) << (bits * i);
+  for (int i = 0; i < 8; ++i) packed |= static_cast<uint32_t>(c[i]) << (bits * i);
   return packed;
 }
 
@@ -850,11 +867,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
           for (int c = 0; c < 8; ++c)
             if (so[c] > 0.0f) r[c] = rint_div(d[c], so[c], ro[c]);
         }
-        uint32_t packed = 0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          packed |= static_cast<uint32_t>(__builtin_amdgcn_fmed3f(r[c], 0.0f, 15.0f)) << (4 * c);
-        codes[s * 8 + q] = packed;
+        for (int c = 0; c < 8; ++c) r[c] = __builtin_amdgcn_fmed3f(r[c], 0.0f, 15.0f);
+        codes[s * 8 + q] = pack_nibbles(r);
       }
     }
   }
