@@ -762,20 +762,27 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
       lds_barrier();  // s_x and s_y are refilled for the next tokens
     }
   } else {
-    // Latent codes + metadata, BF16 sink / ring copies.  Two tokens per trip,
-    // each loaded while the other is written (two register sets, no copies).
+    // Latent codes + metadata, BF16 sink / ring copies.  Three tokens per
+    // trip in three register sets, each token's row requested two tokens
+    // before it is written (no register copies).
     const auto token = [&](const uint4 x, int t) {
       write_latent_token<kClip>(p, x, page, t - pg * P, lane);
       retain_token(p, b, t, end, r0 + (t - sb), x, lane);
     };
-    uint4 nxt{};
-    for (int t = t_first; t < te; t += 2 * t_step) {
-      const int t1 = t + t_step;
-      if (t1 < te) nxt = load_latent(p, r0 + (t1 - sb), lane);
+    const auto fetch = [&](uint4& x, int t) {
+      if (t < te) x = load_latent(p, r0 + (t - sb), lane);
+    };
+    uint4 nx1{}, nx2{};
+    fetch(nx1, t_first + t_step);
+    for (int t = t_first; t < te; t += 3 * t_step) {
+      fetch(nx2, t + 2 * t_step);
       token(cur, t);
-      if (t1 >= te) break;
-      if (t1 + t_step < te) cur = load_latent(p, r0 + (t1 + t_step - sb), lane);
-      token(nxt, t1);
+      if (t + t_step >= te) break;
+      fetch(cur, t + 3 * t_step);
+      token(nx1, t + t_step);
+      if (t + 2 * t_step >= te) break;
+      fetch(nx1, t + 4 * t_step);
+      token(nx2, t + 2 * t_step);
     }
   }
 
