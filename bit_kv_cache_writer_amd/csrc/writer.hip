@@ -169,33 +169,38 @@ __device__ inline uint32_t pack_codes(const float (&v)[8], float m, float s, flo
   return packed;
 }
 
-// Min and max over each 16-lane row by DPP lane moves (VALU, no LDS round
-// trip): swap neighbours, swap pairs, then rotate the row by 4 and by 8.  They
-// run on order-preserving integer keys of the floats (negative values get
-// their magnitude bits flipped), so each step is one v_min_i32 / v_max_i32
-// with its lane move fused in.  Exact for every non-NaN value; the key map is
-// its own inverse.
-__device__ inline int f32_key(float f) {
-  const int b = __float_as_int(f);
-  return b ^ ((b >> 31) & 0x7FFFFFFF);
-}
-__device__ inline float key_f32(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+// DPP lane move within 16-lane rows (bound_ctrl set: the fused form).
 template <int kCtrl>
 __device__ inline int dpp_key(int k) {
   return __builtin_amdgcn_mov_dpp(k, kCtrl, 0xF, 0xF, true);
 }
-__device__ inline void row_minmax16(float& mn, float& mx) {
-  int a = f32_key(mn), b = f32_key(mx);
-  a = min(a, dpp_key<0xB1>(a));
-  b = max(b, dpp_key<0xB1>(b));
-  a = min(a, dpp_key<0x4E>(a));
-  b = max(b, dpp_key<0x4E>(b));
-  a = min(a, dpp_key<0x124>(a));
-  b = max(b, dpp_key<0x124>(b));
-  a = min(a, dpp_key<0x128>(a));
-  b = max(b, dpp_key<0x128>(b));
-  mn = key_f32(a);
-  mx = key_f32(b);
+
+// Min and max of a lane's 8 values, then over each 16-lane row by DPP lane
+// moves fused into v_min_f32 / v_max_f32 (swap neighbours, swap pairs, rotate
+// the row by 4 and by 8): 16 VALU instructions.  Written out so that no
+// canonicalizing copies are inserted around the float min / max (the values
+// are never NaN); the s_nop keep two wait states between a VGPR's write and
+// its DPP read.  Which zero a min or max of -0 and +0 returns is left open
+// (the callers normalize it).
+__device__ inline void group_minmax(const float (&x)[8], float& mn, float& mx) {
+#define MLA_DPP_STEP(CTRL)                                                   \
+  "s_nop 0\n\t"                                                             \
+  "v_min_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_max_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+  asm volatile("v_min3_f32 %0, %2, %3, %4\n\t"
+               "v_max3_f32 %1, %2, %3, %4\n\t"
+               "v_min3_f32 %0, %0, %5, %6\n\t"
+               "v_max3_f32 %1, %1, %5, %6\n\t"
+               "v_min3_f32 %0, %0, %7, %8\n\t"
+               "v_max3_f32 %1, %1, %7, %8\n\t"
+               "v_min_f32 %0, %0, %9\n\t"
+               "v_max_f32 %1, %1, %9\n\t"
+               "s_nop 0\n\t"
+               MLA_DPP_STEP("quad_perm:[1,0,3,2]") MLA_DPP_STEP("quad_perm:[2,3,0,1]")
+               MLA_DPP_STEP("row_ror:4") MLA_DPP_STEP("row_ror:8")
+               : "=&v"(mn), "=&v"(mx)
+               : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+#undef MLA_DPP_STEP
 }
 // Packed signed 16-bit pairs, reduced over the whole wave per half: DPP lane
 // moves within 16-lane rows, then the swaps of rows and of 32-lane halves.
@@ -226,8 +231,8 @@ __device__ inline i16x2 wave_reduce_i16x2(i16x2 v) {
   return pick<kMax>(__builtin_bit_cast(i16x2, c0), __builtin_bit_cast(i16x2, c1));
 }
 
-// Min / max over the whole wave: the row reduction of row_minmax16, then the
-// swaps of 16-lane rows and of 32-lane halves.
+// Min / max of integers over the whole wave: the row steps of group_minmax,
+// then the swaps of 16-lane rows and of 32-lane halves.
 __device__ inline int wave_min_i32(int v) {
   v = min(v, dpp_key<0xB1>(v));
   v = min(v, dpp_key<0x4E>(v));
@@ -409,13 +414,8 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_fmed3f(x[i], nc, c);
   }
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    mn = fminf(mn, x[i]);
-    mx = fmaxf(mx, x[i]);
-  }
-  row_minmax16(mn, mx);
+  float mn, mx;
+  group_minmax(x, mn, mx);
   mn = canon_zero(mn);
   mx = canon_zero(mx);
   const int levels = (1 << p.bits) - 1;
