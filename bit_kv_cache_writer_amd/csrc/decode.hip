@@ -1428,7 +1428,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
 // takes CB channels: its 2 CB columns are (channel, heads 8 (col % 2) .. + 7),
 // 16 bytes of the channel-major partial rows each, and its SG split groups
 // take the splits g, g + SG, ... of every column with up to 16 row loads in
-// flight per thread; the split groups' sums meet in LDS at the end.  Grid =
+// flight per thread; the split groups' sums meet in LDS at the end (summed in
+// two stages by all the threads).  Grid =
 // (sequence, head block) x 512 / CB.  A partial holds the split's normalized
 // output O_s / l_s (fp16) and (m_s, l_s); the merge weights split s by
 // 2^(m_s - M) l_s / sum over splits, M = max_s m_s, per head (formed by all
@@ -1439,6 +1440,9 @@ struct Cmb {
   static constexpr int kQ = kThreads / kHeadBlock;  // split groups of the weights
   static constexpr int kBlocks = kLatentDim / CB;   // workgroups per (sequence, head block)
   static constexpr int kMaxS = SG == 1 ? 32 : kMaxSplits;  // splits it is launched for
+  static constexpr int kOut = 2 * CB * 8;                  // outputs of a workgroup (channel, head)
+  static constexpr int kParts = kThreads / kOut;          // threads per output in the final sum
+  static_assert(SG == 1 || (kThreads % kOut == 0 && SG % kParts == 0), "final sum layout");
 };
 
 // Dynamic LDS of combine_kernel<CB, SG> for n splits: s_ml [split][m 16, l 16],
@@ -1533,18 +1537,30 @@ __global__ void __launch_bounds__((Cmb<CB, SG>::kThreads)) combine_kernel(const 
 #pragma unroll 16
   for (int sp = sg + SG * kEarly; sp < n_splits; sp += SG) add(sp, ldg<u32x4>(row + static_cast<int64_t>(sp) * kPartBytes));
   if constexpr (SG > 1) {
+    // the split groups' sums meet in LDS, then in two stages over all the
+    // threads: output o (column o / 8, head h0 + o % 8 of it) is summed over
+    // every C::kParts-th split group by C::kParts threads, whose parts meet
+    // once more
     float* const mine = s_acc + t * 8;
     *reinterpret_cast<f32x4*>(mine) = f32x4{acc[0], acc[1], acc[2], acc[3]};
     *reinterpret_cast<f32x4*>(mine + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
     __syncthreads();
-    if (sg != 0) return;
+    const int o = t % C::kOut, part = t / C::kOut;
+    float sum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float sum = 0.f;
+    for (int g = part; g < SG; g += C::kParts) sum += s_acc[(g * 2 * CB + (o >> 3)) * 8 + (o & 7)];
+    __syncthreads();
+    s_acc[part * C::kOut + o] = sum;
+    __syncthreads();
+    if (t >= C::kOut) return;
+    float tot = 0.f;
 #pragma unroll
-      for (int g = 0; g < SG; ++g) sum += s_acc[(g * 2 * CB + col) * 8 + e];
-      acc[e] = sum;
-    }
+    for (int q = 0; q < C::kParts; ++q) tot += s_acc[q * C::kOut + t];
+    const int oc = CB * cb + (t >> 4), oh = 8 * ((t >> 3) & 1) + (t & 7);
+    const int hg = hb * kHeadBlock + oh;
+    if (hg < heads)
+      out[(static_cast<int64_t>(b) * heads + hg) * kLatentDim + oc] = tot * s_red[2 * C::kQ * kHeadBlock + oh];
+    return;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -1554,10 +1570,8 @@ __global__ void __launch_bounds__((Cmb<CB, SG>::kThreads)) combine_kernel(const 
   }
 }
 
-// Launches the merge in the shape that suits the split count: one wave per 32
-// channels when the splits are few (up to 32), else 8-channel blocks of 16
-// split groups (four times the workgroups, 16 times the loads in flight per
-// column), which a handful of sequences with hundreds of splits needs.
+// Launches the merge kernel in one shape (CB channels per workgroup, SG
+// split groups); launch_merge picks the shape.
 template <int CB, int SG>
 int launch_combine(const DecodeParams& p, int64_t groups, int heads, int n_hb, int n_splits, hipStream_t stream) {
   static const bool attr_ok =
@@ -1571,6 +1585,17 @@ int launch_combine(const DecodeParams& p, int64_t groups, int heads, int n_hb, i
   hipLaunchKernelGGL((combine_kernel<CB, SG>), grid, block, lds, stream, p.parts, p.out, p.lse, heads, n_hb,
                      n_splits);
   return hipGetLastError() == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ERR_HIP;
+}
+
+// The merge shape for n_splits partials of `groups` (sequence, head block)
+// groups: one wave per 32 channels when the splits are few (up to 32); else
+// 8-channel blocks of 16 split groups, or, when so few groups would leave
+// most of the chip idle (under 256 workgroups), 4-channel blocks of 32 split
+// groups (twice the workgroups, every row of a thread in flight at once).
+int launch_merge(const DecodeParams& p, int64_t groups, int heads, int n_hb, int n_splits, hipStream_t stream) {
+  if (n_splits <= 32) return launch_combine<32, 1>(p, groups, heads, n_hb, n_splits, stream);
+  if (groups * (kLatentDim / 8) < 256) return launch_combine<4, 32>(p, groups, heads, n_hb, n_splits, stream);
+  return launch_combine<8, 16>(p, groups, heads, n_hb, n_splits, stream);
 }
 
 #include "decode_bf16.h"
@@ -1629,8 +1654,7 @@ int bf16_decode_impl(const void* q_lat, const void* q_rope, int32_t batch, int32
     cp.parts = p.parts;
     cp.out = out;
     cp.lse = lse;
-    return plan.n_splits <= 32 ? launch_combine<32, 1>(cp, groups, heads, plan.n_hb, plan.n_splits, stream)
-                               : launch_combine<8, 16>(cp, groups, heads, plan.n_hb, plan.n_splits, stream);
+    return launch_merge(cp, groups, heads, plan.n_hb, plan.n_splits, stream);
   }
   return MLA_LOWBIT_OK;
 }
@@ -1766,10 +1790,7 @@ int decode_impl(const mla_lowbit_layout* layout, const void* q_lat, const void* 
                        stream, p);
   if (hipGetLastError() != hipSuccess) return MLA_LOWBIT_ERR_HIP;
   if (plan.n_splits > 1) {
-    if (plan.n_splits <= 32)
-      rc = launch_combine<32, 1>(p, groups, heads, plan.n_hb, plan.n_splits, stream);
-    else
-      rc = launch_combine<8, 16>(p, groups, heads, plan.n_hb, plan.n_splits, stream);
+    rc = launch_merge(p, groups, heads, plan.n_hb, plan.n_splits, stream);
     if (rc) return rc;
   }
   return MLA_LOWBIT_OK;
