@@ -8,10 +8,13 @@
 // two / four per page when a call brings many tokens into few pages (a
 // page's tokens are then dealt to them in runs of 8, and the first one of a
 // page does all of its k_R and tail work below):
-//   * each wave quantizes whole latent tokens: lane l owns channels 8l..8l+7,
-//     so a 128-channel group is 16 lanes and its min/max is a 16-lane
-//     butterfly; codes are packed in registers and stored as one dword
-//     (4-bit) or one half-word (2-bit) per lane;
+//   * each wave quantizes whole latent tokens, three per loop trip, each
+//     row requested two tokens ahead: lane l owns channels 8l..8l+7, so a
+//     128-channel group is 16 lanes and its min/max DPP steps within a row;
+//     codes are packed in registers and stored as one dword (4-bit) or one
+//     half-word (2-bit) per lane; the INT2 clip takes its order statistics
+//     by bisection over each lane's sorted keys, counting with one ballot
+//     per column;
 //   * if the page becomes full in this call the workgroup quantizes its k_R
 //     per channel over the P tokens (tail buffer for tokens written by earlier
 //     calls, input rows for the new ones);
