@@ -558,8 +558,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
   // this wave's first token goes out with them (its row index is clamped
   // into the input: a wave without a token reads a row it does not use)
   uint4 cur{};
-  // (kMode 0: this workgroup's tokens are tb + g kWaves + wave + k kWaves split)
-  const int t_first = tb + (kMode == 0 ? g * kWaves : 0) + wave, t_step = kWaves * (kMode == 0 ? split : 1);
+  // kMode 0 with the tokens of a page dealt to `split` workgroups: on a page
+  // that this call completes, the first workgroup only does the page's k_R
+  // work and the others take its tokens (its share would otherwise run after
+  // theirs); token runs of kWaves go round the token workgroups in turn.
+  const bool finalize_only = kMode == 0 && split > 1 && (pg + 1) * P <= end;  // same in every workgroup of the page
+  const int tok_wgs = finalize_only ? split - 1 : split, tok_g = finalize_only ? g - 1 : g;
+  const int t_first = kMode != 0 ? tb + wave : (tok_g < 0 ? te : tb + tok_g * kWaves + wave);
+  const int t_step = kWaves * (kMode == 0 ? tok_wgs : 1);
   if constexpr (!kTransform) cur = load_latent(p, r0 + (min(t_first, te - 1) - sb), lane);
   const int page_id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pg];
   if (page_id < 0 || page_id >= p.num_pool_pages) {
