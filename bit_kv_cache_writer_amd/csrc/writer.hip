@@ -14,7 +14,7 @@
 //     128-channel group is 16 lanes and its min/max DPP steps within a row;
 //     codes are packed in registers and stored as one dword (4-bit) or one
 //     half-word (2-bit) per lane; the INT2 clip takes its order statistics
-//     by bisection over each lane's sorted keys, counting with one ballot
+//     by a binary search over each lane's sorted keys, counting with one ballot
 //     per column;
 //   * if the page becomes full in this call the workgroup quantizes its k_R
 //     per channel over the P tokens (tail buffer for tokens written by earlier
@@ -296,21 +296,25 @@ __device__ inline void sort8_packed(u16x2 (&u)[4]) {
 __device__ inline uint32_t key_column(const u16x2 (&u)[4], int j) { return j < 4 ? u[j].x : u[j - 4].y; }
 __device__ inline uint32_t packed_bits(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// Bisection for the smallest key v in [lo, hi] with fewer than `need`
-// (>= 1) of the wave's 512 keys above it (lo, hi wave-uniform and enclosing
-// that key, hi the wave maximum of column 0).  Each probe counts the keys
-// above mid with one ballot per column of the lanes' sorted keys: column j's
-// set of lanes is part of column j - 1's, so an empty column ends the count
-// (below need: hi = mid), and so does the count reaching need (lo = mid + 1).
-// Column 0 is never empty (mid < hi <= its maximum).  Per column: a 16-bit
-// compare into a lane mask (low halves of u, then of uh = u >> 16), its
-// popcount (SCC: any lane set) and the popcount taken from the remaining
-// need - 1 (SCC: borrow, i.e. the count reached need).  The interval shrinks
-// on every probe, so the loop ends after at most 15 probes.
+// The smallest key v in [lo, hi] with fewer than `need` (>= 1) of the
+// wave's 512 keys above it (lo, hi wave-uniform and enclosing that key, with
+// at least `need` keys at or above lo), by binary lifting: base, starting at
+// lo - 1, is the largest key known to have at least `need` keys above it;
+// steps of 2^(k-1), ..., 1 with 2^k >= hi - lo + 1 probe base + step and move
+// base there when the probe has at least `need` keys above it, and the answer
+// is base + 1.  Probes stay below 2 hi - lo <= 0xFFFE, inside the 16-bit
+// compares.  Each probe counts the keys above it with one ballot per column
+// of the lanes' sorted keys: column j's set of lanes is part of column
+// j - 1's, so an empty column ends the count (fewer than need), and so does
+// the count reaching need.  Per column: a 16-bit compare into a lane mask
+// (low halves of u, then of uh = u >> 16), its popcount (SCC: any lane set)
+// and the popcount taken from the remaining need - 1 (SCC: borrow, i.e. the
+// count reached need).  The step's shift sets SCC while a step is left, so
+// the loop needs no compare of its own.
 #define MLA_GT_COLUMN(V)                              \
-  "v_cmp_gt_u16_e64 %[m], %[" V "], %[mid]\n\t"        \
+  "v_cmp_gt_u16_e64 %[m], %[" V "], %[t]\n\t"          \
   "s_bcnt1_i32_b64 %[pc], %[m]\n\t"                  \
-  "s_cbranch_scc0 .Lbelow%=\n\t"                     \
+  "s_cbranch_scc0 .Lnext%=\n\t"                      \
   "s_sub_u32 %[r], %[r], %[pc]\n\t"                  \
   "s_cbranch_scc1 .Labove%=\n\t"
 __device__ inline uint32_t wave_bisect_rank(const u16x2 (&u)[4], uint32_t lo, uint32_t hi, int need) {
@@ -318,38 +322,42 @@ __device__ inline uint32_t wave_bisect_rank(const u16x2 (&u)[4], uint32_t lo, ui
   uint32_t uh[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) uh[j] = u[j].y;
-  uint32_t mid, pc, r;
-  uint64_t m;
-  asm volatile(".Lprobe%=:\n\t"
-               "s_cmp_lt_u32 %[lo], %[hi]\n\t"
-               "s_cbranch_scc0 .Ldone%=\n\t"
-               "s_add_u32 %[mid], %[lo], %[hi]\n\t"
-               "s_lshr_b32 %[mid], %[mid], 1\n\t"
-               "v_cmp_gt_u16_e64 %[m], %[u0], %[mid]\n\t"
-               "s_bcnt1_i32_b64 %[pc], %[m]\n\t"
-               "s_sub_u32 %[r], %[nm1], %[pc]\n\t"
-               "s_cbranch_scc1 .Labove%=\n\t"
-               MLA_GT_COLUMN("u1") MLA_GT_COLUMN("u2") MLA_GT_COLUMN("u3")
-               MLA_GT_COLUMN("h0") MLA_GT_COLUMN("h1") MLA_GT_COLUMN("h2") MLA_GT_COLUMN("h3")
-               ".Lbelow%=:\n\t"
-               "s_mov_b32 %[hi], %[mid]\n\t"
-               "s_branch .Lprobe%=\n"
-               ".Labove%=:\n\t"
-               "s_add_u32 %[lo], %[mid], 1\n\t"
-               "s_branch .Lprobe%=\n"
-               ".Ldone%=:"
-               : [lo] "+s"(lo), [hi] "+s"(hi), [mid] "=&s"(mid), [pc] "=&s"(pc), [r] "=&s"(r), [m] "=&s"(m)
-               : [u0] "v"(packed_bits(u[0])), [u1] "v"(packed_bits(u[1])), [u2] "v"(packed_bits(u[2])),
-                 [u3] "v"(packed_bits(u[3])), [h0] "v"(uh[0]), [h1] "v"(uh[1]), [h2] "v"(uh[2]), [h3] "v"(uh[3]),
-                 [nm1] "s"(need_m1)
-               : "scc");
-  return lo;
+  // 2^(k-1) for the smallest k with 2^k >= hi - lo + 1 (0: lo is the answer)
+  uint32_t step = hi > lo ? 1u << (31 - __builtin_clz(hi - lo)) : 0u;
+  uint32_t base = lo - 1u;
+  if (step != 0) {
+    uint32_t t, pc, r;
+    uint64_t m;
+    asm volatile(".Lprobe%=:\n\t"
+                 "s_add_u32 %[t], %[base], %[step]\n\t"
+                 "v_cmp_gt_u16_e64 %[m], %[u0], %[t]\n\t"
+                 "s_bcnt1_i32_b64 %[pc], %[m]\n\t"
+                 "s_sub_u32 %[r], %[nm1], %[pc]\n\t"
+                 "s_cbranch_scc1 .Labove%=\n\t"
+                 MLA_GT_COLUMN("u1") MLA_GT_COLUMN("u2") MLA_GT_COLUMN("u3")
+                 MLA_GT_COLUMN("h0") MLA_GT_COLUMN("h1") MLA_GT_COLUMN("h2") MLA_GT_COLUMN("h3")
+                 ".Lnext%=:\n\t"
+                 "s_lshr_b32 %[step], %[step], 1\n\t"
+                 "s_cbranch_scc1 .Lprobe%=\n\t"
+                 "s_branch .Ldone%=\n"
+                 ".Labove%=:\n\t"
+                 "s_mov_b32 %[base], %[t]\n\t"
+                 "s_lshr_b32 %[step], %[step], 1\n\t"
+                 "s_cbranch_scc1 .Lprobe%=\n"
+                 ".Ldone%=:"
+                 : [base] "+s"(base), [step] "+s"(step), [t] "=&s"(t), [pc] "=&s"(pc), [r] "=&s"(r), [m] "=&s"(m)
+                 : [u0] "v"(packed_bits(u[0])), [u1] "v"(packed_bits(u[1])), [u2] "v"(packed_bits(u[2])),
+                   [u3] "v"(packed_bits(u[3])), [h0] "v"(uh[0]), [h1] "v"(uh[1]), [h2] "v"(uh[2]), [h3] "v"(uh[3]),
+                   [nm1] "s"(need_m1)
+                 : "scc");
+  }
+  return base + 1u;
 }
 #undef MLA_GT_COLUMN
 
 // k-th smallest (0-based) of the 512 keys, held 8 per lane in descending
-// order: the smallest v with fewer than 512 - k keys above it, by bisection
-// between two keys that enclose it.  Each lane holds j + 1 keys at or above
+// order: the smallest v with fewer than 512 - k keys above it, by a binary
+// search between two keys that enclose it.  Each lane holds j + 1 keys at or above
 // its column j, so with j = (511 - k) / 64 at least 512 - k keys lie at or
 // above the wave minimum of column j; the wave maximum bounds it above.
 __device__ inline uint32_t wave_kth_smallest(const u16x2 (&u)[4], int k) {
