@@ -216,23 +216,29 @@ template <int kCtrl>
 __device__ inline i16x2 dpp_i16x2(i16x2 v) {
   return __builtin_bit_cast(i16x2, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
 }
-template <bool kMax>
-__device__ inline i16x2 pick(i16x2 a, i16x2 b) {
-  return kMax ? __builtin_elementwise_max(a, b) : __builtin_elementwise_min(a, b);
+// Minimum over a lane and its DPP partner of one of two packed-key dwords:
+// the lane keeps `hi` when `up` is set, else `lo`, and sends the other to the
+// partner, whose `up` is the opposite (one step of a reduce-scatter).
+template <int kCtrl>
+__device__ inline uint32_t scatter_min(bool up, uint32_t lo, uint32_t hi) {
+  const uint32_t keep = up ? hi : lo, send = up ? lo : hi;
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(i16x2, keep),
+                                                                dpp_i16x2<kCtrl>(__builtin_bit_cast(i16x2, send))));
 }
-template <bool kMax>
-__device__ inline i16x2 wave_reduce_i16x2(i16x2 v) {
-  v = pick<kMax>(v, dpp_i16x2<0xB1>(v));
-  v = pick<kMax>(v, dpp_i16x2<0x4E>(v));
-  v = pick<kMax>(v, dpp_i16x2<0x124>(v));
-  v = pick<kMax>(v, dpp_i16x2<0x128>(v));
-  uint32_t u = __builtin_bit_cast(uint32_t, v);
+// Packed 16-bit minimum over the lanes l, l ^ 8, l ^ 16, ... (the lanes that
+// agree in their three low bits): the 8-lane step inside a row, then the
+// swaps of 16-lane rows and of 32-lane halves.
+__device__ inline uint32_t min_over_octets(uint32_t u) {
+  u = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(i16x2, u),
+                                                             dpp_i16x2<0x128>(__builtin_bit_cast(i16x2, u))));
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   const uint32_t a0 = a[0], a1 = a[1];
-  u = __builtin_bit_cast(uint32_t, pick<kMax>(__builtin_bit_cast(i16x2, a0), __builtin_bit_cast(i16x2, a1)));
+  u = __builtin_bit_cast(uint32_t,
+                         __builtin_elementwise_min(__builtin_bit_cast(i16x2, a0), __builtin_bit_cast(i16x2, a1)));
   const auto c = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   const uint32_t c0 = c[0], c1 = c[1];
-  return pick<kMax>(__builtin_bit_cast(i16x2, c0), __builtin_bit_cast(i16x2, c1));
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_min(__builtin_bit_cast(i16x2, c0), __builtin_bit_cast(i16x2, c1)));
 }
 
 // Min / max of integers over the whole wave: the row steps of group_minmax,
@@ -840,17 +846,35 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
         }
       }
     }
+    // The eight dwords (minimum keys of the channel pairs 0..3, then the
+    // maximum keys complemented, so that all eight reduce by minimum) are
+    // reduced by a reduce-scatter: the partners l ^ 1, l ^ 2 (quad permutes)
+    // and l ^ 7 (half-row mirror) each halve the lane's dwords by a lane bit
+    // in which the partners differ and agree in the others (a = b0 ^ b2,
+    // b = b1 ^ b2, c = b2), so that lane l ends with dword 4a + 2b + c over
+    // its 8 lanes; the lanes agreeing in their low three bits then finish it.
+    uint32_t dw[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      kmn[d] = wave_reduce_i16x2<false>(kmn[d]);
-      kmx[d] = wave_reduce_i16x2<true>(kmx[d]);
+      dw[d] = __builtin_bit_cast(uint32_t, kmn[d]);
+      dw[4 + d] = ~__builtin_bit_cast(uint32_t, kmx[d]);
     }
-    // lane e < 8: channel 8q + e
-    const int e = lane & 7;
-    const uint32_t pmn = __builtin_bit_cast(uint32_t, e < 2 ? kmn[0] : e < 4 ? kmn[1] : e < 6 ? kmn[2] : kmn[3]);
-    const uint32_t pmx = __builtin_bit_cast(uint32_t, e < 2 ? kmx[0] : e < 4 ? kmx[1] : e < 6 ? kmx[2] : kmx[3]);
-    const uint32_t bmn = keys((e & 1) ? pmn >> 16 : pmn & 0xFFFFu) & 0xFFFFu;
-    const uint32_t bmx = keys((e & 1) ? pmx >> 16 : pmx & 0xFFFFu) & 0xFFFFu;
+    const bool ua = ((lane ^ (lane >> 2)) & 1) != 0, ub = (((lane >> 1) ^ (lane >> 2)) & 1) != 0,
+               uc = ((lane >> 2) & 1) != 0;
+    uint32_t e4[4], e2[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e4[i] = scatter_min<0xB1>(ua, dw[i], dw[i + 4]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) e2[j] = scatter_min<0x4E>(ub, e4[j], e4[j + 2]);
+    const uint32_t g = min_over_octets(scatter_min<0x141>(uc, e2[0], e2[1]));
+    // Lanes l and l ^ 1 hold the minimum and the (complemented) maximum of the
+    // channel pair k = 2b + c; lane l < 8 takes channel 2k + (l & 1) of the
+    // octet, so lanes 0..7 hold channels 0, 1, 4, 5, 6, 7, 2, 3.
+    const uint32_t other = __builtin_bit_cast(uint32_t, dpp_i16x2<0xB1>(__builtin_bit_cast(i16x2, g)));
+    const uint32_t pmn = ua ? other : g, pmx = ~(ua ? g : other);
+    const int e = 4 * static_cast<int>(ub) + 2 * static_cast<int>(uc) + (lane & 1);
+    const uint32_t bmn = keys((lane & 1) ? pmn >> 16 : pmn & 0xFFFFu) & 0xFFFFu;
+    const uint32_t bmx = keys((lane & 1) ? pmx >> 16 : pmx & 0xFFFFu) & 0xFFFFu;
     const float cmn = canon_zero(bf16_to_f32(bmn)), cmx = canon_zero(bf16_to_f32(bmx));
     const uint16_t mh = f16_round_down(cmn);
     const float minf = f16_to_f32(mh);
@@ -859,8 +883,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
     const float sf = f16_to_f32(sh);
     if (lane < 8) {
       uint16_t* meta = reinterpret_cast<uint16_t*>(page + p.rope_meta_off);
-      meta[8 * q + lane] = sh;
-      meta[kRopeDim + 8 * q + lane] = mh;
+      meta[8 * q + e] = sh;
+      meta[kRopeDim + 8 * q + e] = mh;
     }
     // every lane gets the octet's offsets, steps and reciprocals (0 for a
     // zero step: its codes are 0)
@@ -868,9 +892,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
     const float rc = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      mo[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, minf), c));
-      so[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sf), c));
-      ro[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rc), c));
+      const int src = 4 * ((c >> 1) & 1) + 2 * ((c >> 2) ^ ((c >> 1) & 1)) + (c & 1);  // the lane of channel c
+      mo[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, minf), src));
+      so[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sf), src));
+      ro[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rc), src));
     }
     uint32_t* const codes = reinterpret_cast<uint32_t*>(page + p.rope_codes_off);
     for (int k = 0; k < rows_per_lane; ++k) {
