@@ -81,30 +81,34 @@ __device__ inline float f16_to_f32(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-// fp16 bits of x rounded toward zero, zero-extended (v_cvt_pkrtz_f16_f32 of
-// x and +0: a finite x never becomes an infinity).
-__device__ inline uint32_t f16_bits_rz(float x) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, 0.0f));
-}
+// Directed fp16 rounding by the conversion itself: the wave's MODE register
+// (its four round-mode bits: fp32 and fp16/fp64, 0 nearest-even, 1 toward
+// +inf, 2 toward -inf) is set for one v_cvt_f16_f32 and put back to
+// nearest-even, all inside one asm block so that no other instruction runs
+// under the directed mode; two wait states follow each mode change.  The
+// unsigned min takes an infinity (a value beyond 65504 in that direction)
+// back to the largest finite fp16.  x is not -0 (the callers normalize it).
+#define MLA_CVT_F16_DIRECTED(MODE)                                   \
+  "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), " MODE "\n\t"     \
+  "s_nop 1\n\t"                                                    \
+  "v_cvt_f16_f32_e32 %0, %1\n\t"                                   \
+  "s_nop 1\n\t"                                                    \
+  "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 0"
 
-// Largest fp16 <= x (x not -0; -65504 for x below it): toward zero, then, for
-// a negative x that this moved up, one step away from zero (the bit pattern
-// plus one: -0 becomes the smallest negative subnormal, -65504 becomes -inf,
-// which the unsigned min takes back to -65504; no other pattern is above it).
+// Largest fp16 <= x (-65504 for x below it).
 __device__ inline uint16_t f16_round_down(float x) {
-  uint32_t h = f16_bits_rz(x);
-  if (f16_to_f32(static_cast<uint16_t>(h)) > x) ++h;
-  return static_cast<uint16_t>(min(h, 0xFBFFu));
+  uint32_t h;
+  asm volatile(MLA_CVT_F16_DIRECTED("10") : "=v"(h) : "v"(x));
+  return static_cast<uint16_t>(min(h & 0xFFFFu, 0xFBFFu));
 }
 
-// Smallest fp16 >= x (x >= 0, not -0; 65504 for x above it): toward zero,
-// then one step up if that moved down (65504 + 1 step is +inf, taken back
-// by the min).
+// Smallest fp16 >= x (x >= 0; 65504 for x above it).
 __device__ inline uint16_t f16_round_up(float x) {
-  uint32_t h = f16_bits_rz(x);
-  if (f16_to_f32(static_cast<uint16_t>(h)) < x) ++h;
-  return static_cast<uint16_t>(min(h, 0x7BFFu));
+  uint32_t h;
+  asm volatile(MLA_CVT_F16_DIRECTED("5") : "=v"(h) : "v"(x));
+  return static_cast<uint16_t>(min(h & 0xFFFFu, 0x7BFFu));
 }
+#undef MLA_CVT_F16_DIRECTED
 
 // span / d, correctly rounded, for d = 3 or 15 (rd = rn(1 / d)) and
 // 0 <= span <= 2^20: the product with rd and one FMA correction of it give
@@ -149,7 +153,13 @@ __device__ inline uint32_t pack_nibbles(const float (&c)[8]) {
 // for nearness to a half-integer once for the 8 values (|qa - rint(qa)| at
 // least 0.5 - 1e-5 is the same set as rint_div's test), and only a row with
 // such a value takes the IEEE division.  Codes are packed `bits` apiece.
-__device__ inline uint32_t pack_codes(const float (&v)[8], float m, float s, float rcp_s, int bits, float levels) {
+// The clamp to [0, levels] is never active for finite values in the stated
+// range, so none is applied: m is at most the group's minimum (rounded
+// down), so v - m >= 0; and s is at least fl(span / levels) (rounded up to
+// fp16), span = fl(max - m) bounds every fl(v - m), so each quotient, fast
+// (a reciprocal within 1 ulp) or divided, is at most levels (1 + 2^-22)
+// and rounds to at most levels.
+__device__ inline uint32_t pack_codes(const float (&v)[8], float m, float s, float rcp_s, int bits) {
   const float rc = s > 0.0f ? rcp_s : 0.0f;
   float r[8];
   float dev = 0.0f;  // largest |qa - rint(qa)| of the 8 (a max3 chain)
@@ -163,13 +173,10 @@ __device__ inline uint32_t pack_codes(const float (&v)[8], float m, float s, flo
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = rint_div(v[i] - m, s, rcp_s);
   }
-  float c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(r[i], 0.0f, levels);
-  if (bits == 4) return pack_nibbles(c);
+  if (bits == 4) return pack_nibbles(r);
   uint32_t packed = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) packed |= static_cast<uint32_t>(c[i]) << (bits * i);
+  for (int i = 0; i < 8; ++i) packed |= static_cast<uint32_t>(r[i]) << (bits * i);
   return packed;
 }
 
@@ -436,7 +443,6 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
   group_minmax(x, mn, mx);
   mn = canon_zero(mn);
   mx = canon_zero(mx);
-  const int levels = (1 << p.bits) - 1;
   const uint16_t mh = f16_round_down(mn);
   const float minf = f16_to_f32(mh);
   const float span = mx - minf;
@@ -444,7 +450,7 @@ __device__ void write_latent_token(const WriterParams& p, const uint4 raw, uint8
   const uint16_t sh = f16_round_up(s);
   const float sf = f16_to_f32(sh);
   const float rs = __builtin_amdgcn_rcpf(sf);
-  const uint32_t packed = pack_codes(x, minf, sf, rs, p.bits, static_cast<float>(levels));
+  const uint32_t packed = pack_codes(x, minf, sf, rs, p.bits);
   uint8_t* row = page + static_cast<int64_t>(slot) * p.latent_row;
   if (p.bits == 4) {
     reinterpret_cast<uint32_t*>(row)[lane] = packed;
@@ -917,9 +923,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
           for (int c = 0; c < 8; ++c)
             if (so[c] > 0.0f) r[c] = rint_div(d[c], so[c], ro[c]);
         }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) r[c] = __builtin_amdgcn_fmed3f(r[c], 0.0f, 15.0f);
-        codes[s * 8 + q] = pack_nibbles(r);
+        codes[s * 8 + q] = pack_nibbles(r);  // (in [0, 15] without a clamp, as in pack_codes)
       }
     }
   }
