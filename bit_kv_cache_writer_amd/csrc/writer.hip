@@ -9,13 +9,18 @@
 // page's tokens are then dealt to them in runs of 8, and the first one of a
 // page does all of its k_R and tail work below, and no tokens when the page
 // completes):
-//   * each wave quantizes whole latent tokens, three per loop trip, each
-//     row requested two tokens ahead: lane l owns channels 8l..8l+7, so a
-//     128-channel group is 16 lanes and its min/max DPP steps within a row;
-//     codes are packed in registers and stored as one dword (4-bit) or one
-//     half-word (2-bit) per lane; the INT2 clip takes its order statistics
-//     by a binary search over each lane's sorted keys, counting with one ballot
-//     per column;
+//   * without the clip each wave quantizes two whole latent tokens at a
+//     time, one per half-wave, two pairs per loop trip, each pair's rows
+//     requested one pair ahead: lane l owns channels 16c..16c+15 (c = l mod
+//     32) of its half's token, so a 128-channel group is 8 lanes and its
+//     min/max take three DPP steps, and the group's metadata arithmetic is
+//     shared by the two tokens; codes are packed in registers and stored as
+//     two dwords (4-bit) or one dword (2-bit) per lane;
+//   * with the INT2 clip each wave quantizes one whole token at a time (three
+//     per loop trip, rows requested two tokens ahead), lane l owning channels
+//     8l..8l+7: a group is 16 lanes, and the clip takes its order statistics
+//     by a binary search over each lane's sorted keys, counting with one
+//     ballot per column;
 //   * if the page becomes full in this call the workgroup quantizes its k_R
 //     per channel over the P tokens (tail buffer for tokens written by earlier
 //     calls, input rows for the new ones);
@@ -211,6 +216,38 @@ __device__ inline void group_minmax(const float (&x)[8], float& mn, float& mx) {
                MLA_DPP_STEP("row_ror:4") MLA_DPP_STEP("row_ror:8")
                : "=&v"(mn), "=&v"(mx)
                : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+#undef MLA_DPP_STEP
+}
+// The same for 16 values a lane and 8-lane groups (two tokens per wave, 16
+// channels a lane): swap neighbours, swap pairs, mirror the half-row; 22 VALU
+// instructions for two tokens.
+__device__ inline void group_minmax16(const float (&x)[16], float& mn, float& mx) {
+#define MLA_DPP_STEP(CTRL)                                                   \
+  "s_nop 0\n\t"                                                             \
+  "v_min_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_max_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+  asm volatile("v_min3_f32 %0, %2, %3, %4\n\t"
+               "v_max3_f32 %1, %2, %3, %4\n\t"
+               "v_min3_f32 %0, %0, %5, %6\n\t"
+               "v_max3_f32 %1, %1, %5, %6\n\t"
+               "v_min3_f32 %0, %0, %7, %8\n\t"
+               "v_max3_f32 %1, %1, %7, %8\n\t"
+               "v_min3_f32 %0, %0, %9, %10\n\t"
+               "v_max3_f32 %1, %1, %9, %10\n\t"
+               "v_min3_f32 %0, %0, %11, %12\n\t"
+               "v_max3_f32 %1, %1, %11, %12\n\t"
+               "v_min3_f32 %0, %0, %13, %14\n\t"
+               "v_max3_f32 %1, %1, %13, %14\n\t"
+               "v_min3_f32 %0, %0, %15, %16\n\t"
+               "v_max3_f32 %1, %1, %15, %16\n\t"
+               "v_min_f32 %0, %0, %17\n\t"
+               "v_max_f32 %1, %1, %17\n\t"
+               "s_nop 0\n\t"
+               MLA_DPP_STEP("quad_perm:[1,0,3,2]") MLA_DPP_STEP("quad_perm:[2,3,0,1]")
+               MLA_DPP_STEP("row_half_mirror")
+               : "=&v"(mn), "=&v"(mx)
+               : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+                 "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
 #undef MLA_DPP_STEP
 }
 // Packed signed 16-bit pairs, reduced over the whole wave per half: DPP lane
@@ -489,6 +526,68 @@ __device__ inline void retain_token(const WriterParams& p, int b, int t, int end
   if (to_ring) copy_row(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems, ckv, kr, lane);
 }
 
+// Quantizes two latent tokens with one wave (no clip): lanes 0..31 hold
+// one token and lanes 32..63 the other, lane l channels 16 c .. 16 c + 15
+// (c = l mod 32), so a 128-channel group is 8 lanes and the group's min / max
+// and metadata are worked out once per lane for both tokens.  x holds the
+// lane's 32 bytes of its token's row; the codes go to row slot `slot` of the
+// page (two dwords a lane at 4 bits, one at 2), and nothing is stored where
+// `store` is false (a half-wave without a token).  The stores address the
+// first token's code row and metadata (`rows`, `metas`, the same in every
+// lane) plus per-lane byte offsets that also step to the second token.
+__device__ void write_latent_pair(const WriterParams& p, const uint4 (&raw)[2], uint8_t* rows, uint8_t* metas,
+                                  uint32_t code_off, uint32_t meta_off, int col, bool store) {
+  const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+  float mn, mx;
+  group_minmax16(x, mn, mx);
+  mn = canon_zero(mn);
+  mx = canon_zero(mx);
+  const uint16_t mh = f16_round_down(mn);
+  const float minf = f16_to_f32(mh);
+  const float span = mx - minf;
+  const float s = p.bits == 4 ? div_levels(span, 15.0f, 1.0f / 15.0f) : div_levels(span, 3.0f, 1.0f / 3.0f);
+  const uint16_t sh = f16_round_up(s);
+  const float sf = f16_to_f32(sh);
+  const float rs = __builtin_amdgcn_rcpf(sf);
+  float a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = x[i];
+    b[i] = x[8 + i];
+  }
+  const uint32_t ca = pack_codes(a, minf, sf, rs, p.bits), cb = pack_codes(b, minf, sf, rs, p.bits);
+  if (!store) return;
+  if (p.bits == 4) {
+    *reinterpret_cast<uint2*>(rows + code_off) = make_uint2(ca, cb);
+  } else {
+    *reinterpret_cast<uint32_t*>(rows + code_off) = ca | (cb << 16);
+  }
+  if ((col & 7) == 0)
+    *reinterpret_cast<uint32_t*>(metas + meta_off) = static_cast<uint32_t>(sh) | (static_cast<uint32_t>(mh) << 16);
+}
+
+// retain_token for a half-wave holding its token's row 32 bytes a lane
+// (lane c = l mod 32 holds c_KV bytes 32 c .. 32 c + 31, k_R by c < 8).
+__device__ inline void retain_half(const WriterParams& p, int b, int t, int end, int64_t row, const uint4 (&x)[2],
+                                   int col) {
+  const bool to_sink = t < p.sink_n, to_ring = p.local > 0 && t >= end - p.local;
+  if (!to_sink && !to_ring) return;
+  const uint4 kr = reinterpret_cast<const uint4*>(p.k_r + row * kRopeDim)[col & 7];
+  const auto put = [&](uint16_t* dst) {
+    reinterpret_cast<uint4*>(dst)[2 * col] = x[0];
+    reinterpret_cast<uint4*>(dst)[2 * col + 1] = x[1];
+    if (col < 8) reinterpret_cast<uint4*>(dst + kLatentDim)[col] = kr;
+  };
+  if (to_sink) put(p.sink + (static_cast<int64_t>(b) * p.sink_n + t) * kRowElems);
+  if (to_ring) put(p.ring + (static_cast<int64_t>(b) * p.local + t % p.local) * kRowElems);
+}
+
 // Columns k0 .. k0 + 63 of the latent transform for N tokens: acc[w] of
 // token w continues its fp32 fma chain over A_c row `arow` (64 staged bf16
 // values) times the token's inputs xs[w][k0 ..] (fp32, broadcast from LDS),
@@ -525,9 +624,11 @@ __device__ inline void transform_pass(float (&acc)[kWaves], const uint8_t* arow,
 // kMode 0: plain writer; 1: with the latent transform, one workgroup per
 // page; 2: with the latent transform, four workgroups per page (latent group
 // g = blockIdx.x % 4).  kClip: the INT2 latent's quantile clip (never with
-// kMode 2); a separate instantiation keeps its code out of the others.
+// kMode 2); a separate instantiation keeps its code out of the others.  The
+// plain writer is held to 80 VGPRs (6 waves per SIMD, 3 workgroups per CU:
+// its two-token path needs 79), the clip writer to 64 (8 waves per SIMD).
 template <int kMode, bool kClip>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMode == 0 ? 8 : 1))) writer_kernel(WriterParams p) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMode == 0 ? (kClip ? 8 : 6) : 1))) writer_kernel(WriterParams p) {
   constexpr bool kTransform = kMode != 0;
   // kMode 2: latent group g of the page; kMode 0: token share g of
   // p.token_split (share 0 also does the page's k_R work)
@@ -587,7 +688,35 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
   const int tok_wgs = finalize_only ? split - 1 : split, tok_g = finalize_only ? g - 1 : g;
   const int t_first = kMode != 0 ? tb + wave : (tok_g < 0 ? te : tb + tok_g * kWaves + wave);
   const int t_step = kWaves * (kMode == 0 ? tok_wgs : 1);
-  if constexpr (!kTransform) cur = load_latent(p, r0 + (min(t_first, te - 1) - sb), lane);
+  // (the plain writer without the clip takes two tokens a wave: half-wave
+  // h = lane / 32 has token t_first + h t_step of each pair)
+  constexpr bool kPairs = kMode == 0 && !kClip;
+  const int half = lane >> 5, col2 = lane & 31;
+  uint4 pa[2] = {};
+  // byte offsets of the lane's part of its half-wave's token from the pair's
+  // first token: input row, code row, metadata (same in every pair)
+  const uint32_t step_h = static_cast<uint32_t>(half * t_step);
+  const uint32_t in_off = step_h * (kLatentDim * 2) + 32u * static_cast<uint32_t>(col2);
+  const uint32_t code_off = step_h * static_cast<uint32_t>(p.latent_row) + (p.bits == 4 ? 8u : 4u) * col2;
+  const uint32_t meta_off = step_h * (kGroups * 4) + 4u * static_cast<uint32_t>(col2 >> 3);
+  const auto load_pair = [&](uint4(&x)[2], int t) {  // t: the pair's first token
+    const uint8_t* src =
+        reinterpret_cast<const uint8_t*>(p.c_kv + static_cast<int64_t>(r0 + (t - sb)) * kLatentDim) + in_off;
+    x[0] = reinterpret_cast<const uint4*>(src)[0];
+    x[1] = reinterpret_cast<const uint4*>(src)[1];
+  };
+  if constexpr (kPairs) {
+    // (a half-wave past the page's last token reads that token's row instead)
+    if (t_first + half * t_step < te) {
+      load_pair(pa, t_first);
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(p.c_kv + static_cast<int64_t>(r0 + (te - 1 - sb)) * kLatentDim) + 2 * col2;
+      pa[0] = src[0];
+      pa[1] = src[1];
+    }
+  } else if constexpr (!kTransform) {
+    cur = load_latent(p, r0 + (min(t_first, te - 1) - sb), lane);
+  }
   const int page_id = p.block_table[static_cast<int64_t>(b) * p.max_pages + pg];
   if (page_id < 0 || page_id >= p.num_pool_pages) {
     __syncthreads();  // no direct load outlives the workgroup
@@ -790,6 +919,29 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
         retain_token(p, b, t, end, r0 + (t - sb), y, lane);
       }
       lds_barrier();  // s_x and s_y are refilled for the next tokens
+    }
+  } else if constexpr (kPairs) {
+    // Two tokens a wave (one a half-wave), two pairs per trip in two register
+    // sets: each pair's rows are requested before the previous pair is
+    // written (no register copies).
+    const auto pair = [&](const uint4(&x)[2], int t) {
+      const int my = t + half * t_step;
+      const bool ok = my < te;
+      uint8_t* const rows = page + static_cast<int64_t>(t - pg * P) * p.latent_row;
+      uint8_t* const metas = page + p.latent_meta_off + static_cast<int64_t>(t - pg * P) * (kGroups * 4);
+      if (ok) retain_half(p, b, my, end, r0 + (my - sb), x, col2);  // (first: the raw row is then dead)
+      write_latent_pair(p, x, rows, metas, code_off, meta_off, col2, ok);
+    };
+    const auto fetch2 = [&](uint4(&x)[2], int t) {
+      if (t + half * t_step < te) load_pair(x, t);
+    };
+    uint4 pb[2] = {};
+    for (int t = t_first; t < te; t += 4 * t_step) {
+      fetch2(pb, t + 2 * t_step);
+      pair(pa, t);
+      if (t + 2 * t_step >= te) break;
+      fetch2(pa, t + 4 * t_step);
+      pair(pb, t + 2 * t_step);
     }
   } else {
     // Latent codes + metadata, BF16 sink / ring copies.  Three tokens per
