@@ -77,6 +77,10 @@ CASES = [
     # the layout's largest protection: sink 64 and a 4096-token window, one
     # sequence past both and one inside them
     ("c2r4_p64_maxwin", 64, 2, 0.94, 64, 4096, [4500, 3000], 16),
+    # 2-bit latents without the clip (two tokens a wave): odd token counts per
+    # page and wave, sink and ring copies from either half-wave
+    ("c2r4_p64_noclip_ragged", 64, 2, 0.0, 4, 32, [1, 2, 63, 64, 65, 191, 700], 16),
+    ("c4r4_p32_odd_h20", 32, 4, 0.0, 3, 5, [33, 15, 97], 20),
 ]
 
 
@@ -111,6 +115,8 @@ def test_chunked_appends_equal_bulk(torch_cuda):
     gpu2, ref2 = _build(torch, "chunked_c4r4", 32, 4, 0.0, 4, 8, lengths, seed=92,
                         chunks=[[1, 1, 1]] * 7 + [[L - 7 for L in lengths]])
     compare_cache(gpu2, ref2)
+    gpu3, ref3 = _build(torch, "chunked_c2r4_noclip", 64, 2, 0.0, 4, 32, lengths, seed=93, chunks=sched)
+    compare_cache(gpu3, ref3)
 
 
 TRANSFORM_CASES = [
