@@ -5,7 +5,7 @@
 // k_R with FP16 scale/min).
 //
 // One workgroup (8 waves) per (sequence, cache page touched by the call), or
-// two / five per page when a call brings many tokens into few pages (a
+// three / five per page when a call brings many tokens into few pages (a
 // page's tokens are then dealt to them in runs of 8, and the first one of a
 // page does all of its k_R and tail work below, and no tokens when the page
 // completes):
@@ -60,7 +60,7 @@ struct WriterParams {
   uint16_t* ring;
   uint16_t* tail;
   int32_t batch, total_new, max_pages, num_pool_pages, pages_per_seq_grid;
-  int32_t token_split;  // plain writer: workgroups per page (1, 2 or 5), tokens dealt between them
+  int32_t token_split;  // plain writer: workgroups per page (1, 3 or 5), tokens dealt between them
   int32_t P, bits, sink_n, local;
   int32_t clip_lo, clip_hi;
   float clip_frac;
@@ -1151,7 +1151,7 @@ int write_impl(const mla_lowbit_layout* layout, const void* a_c, const void* c_k
   p.pages_per_seq_grid = (max_new_per_seq - 1) / g.page_size + 2;
   // with the transform and no clipping, four workgroups per page (one per
   // latent group); the clip needs all 512 channels of a token in one wave.
-  // The plain writer deals a page's tokens to 2 or 5 workgroups when a call
+  // The plain writer deals a page's tokens to 3 or 5 workgroups when a call
   // writes many tokens into few pages (chunked prefill of a few sequences),
   // so that the chip holds more than one workgroup per CU; on a page the call
   // completes the first of them only does the page's k_R work.
@@ -1159,7 +1159,7 @@ int write_impl(const mla_lowbit_layout* layout, const void* a_c, const void* c_k
   p.token_split = 1;
   if (!a_c && max_new_per_seq >= 4 * kWaves) {
     const int64_t pages = static_cast<int64_t>(batch) * ((max_new_per_seq + g.page_size - 1) / g.page_size);
-    p.token_split = pages <= 256 ? 5 : (pages <= 512 ? 2 : 1);
+    p.token_split = pages <= 256 ? 5 : (pages <= 1024 ? 3 : 1);
   }
   const int64_t blocks = static_cast<int64_t>(batch) * p.pages_per_seq_grid * (split ? 4 : p.token_split);
   if (blocks > 0x7FFFFFFF) return MLA_LOWBIT_ERR_UNSUPPORTED;
