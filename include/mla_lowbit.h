@@ -113,9 +113,11 @@ int mla_lowbit_layout_query(const mla_lowbit_layout* layout, mla_lowbit_sizes* s
  *     (FP16 scale/min per channel and page) and packed.
  * Codes, metadata and the BF16 copies equal, bit for bit, those of appending
  * the same tokens one at a time.  `seqlens_before` is not modified.
- * Inputs must be finite bf16.  The FP16 minimum is rounded toward -inf and
- * the scale toward +inf, each saturating at +-65504; mla_lowbit_decode
- * further requires |x| <= 65280 (the largest bf16 below the fp16 limit).
+ * Inputs must be finite bf16 with |x| <= 65280 (the largest bf16 below the
+ * fp16 limit), as mla_lowbit_decode also requires.  The FP16 minimum is
+ * rounded toward -inf and the scale toward +inf; within that range every
+ * code falls in [0, levels] without a clamp, and the codes are not clamped
+ * (values beyond it give codes that differ from a clamped quantizer's).
  *
  *   c_kv           bf16 [total_new][512], 16-B aligned
  *   k_r            bf16 [total_new][64],  16-B aligned
